@@ -1,0 +1,181 @@
+"""Benchmark of the MoE layer share on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config tp_share]
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: route -> permute -> gate/up grouped GEMM with the
+SiLU*up epilogue -> down grouped GEMM -> top-k weighted combine (moe_layer).
+W untimed steps, then exactly K timed steps bracketed by device
+synchronizations.  Per-kernel durations come from HIP events recorded on the
+launch stream around each step of the same path called entry point by entry
+point.  Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_BF16_TFLOPS = 2516.6   # dense bf16 / fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0       # HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", default="tp_share")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle baseline sample (0 disables it)")
+    p.add_argument("--traffic", default=None,
+                   help="json file with rocprof FETCH/WRITE-derived HBM bytes per launch")
+    return p.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(collectives and sharding are out of scope); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_expert_grouped_amd as moe
+    from moe_expert_grouped_amd import synthetic as syn
+
+    torch.cuda.set_device(0)
+    cfg = syn.CONFIGS[a.config]
+    d = syn.make_config(a.config)
+    T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
+    dev16 = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    x, wg, wu, wd = dev16(d["x"]), dev16(d["wg"]), dev16(d["wu"]), dev16(d["wd"])
+    given = "logits" not in d
+    logits = None if given else torch.from_numpy(d["logits"]).cuda()
+    tidx = torch.from_numpy(d["topk_idx"]).cuda() if given else None
+    tw = torch.from_numpy(d["topk_w"]).cuda() if given else None
+    ws = moe.layer_workspace(T, H, E, k, I)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        moe.layer(x, wg, wu, wd, k, logits=logits, topk_idx=tidx, topk_w=tw, workspace=ws, out=out)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / a.steps
+
+    # ---- per-kernel durations: HIP events on the launch stream, same path step by step
+    stream = torch.cuda.current_stream()
+    names = ["route", "permute", "gate_up", "down", "combine"]
+    ev = {n: [] for n in names}
+    R = T * k
+    if given:
+        idx_t, w_t = tidx, tw
+    with torch.cuda.stream(stream):
+        for it in range(a.warmup + a.steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            e[0].record(stream)
+            if not given:
+                idx_t, w_t = moe.route(logits, k)
+            e[1].record(stream)
+            P = moe.permute(idx_t, E)
+            e[2].record(stream)
+            h = moe.grouped_gemm(x, wg, P.block_expert, P.num_padded_rows, N=I, K=H, cap=P.cap,
+                                 a_src_row=P.row_to_pair, a_src_div=k, B2=wu, epilogue="silu_mul")
+            e[3].record(stream)
+            y = moe.grouped_gemm(h, wd, P.block_expert, P.num_padded_rows, N=H, K=I, cap=P.cap)
+            e[4].record(stream)
+            moe.combine(y, P.pair_to_row, w_t, out=out)
+            e[5].record(stream)
+            if it >= a.warmup:
+                ev["_events"] = ev.get("_events", []) + [e]
+    torch.cuda.synchronize()
+    dur = {n: float(np.mean([es[i].elapsed_time(es[i + 1]) for es in ev["_events"]])) for i, n in enumerate(names)}
+    m_pad = int(P.num_padded_rows.item())
+    counts = P.counts.cpu().numpy()
+    e_act = int((counts > 0).sum())
+
+    # ---- algorithmic work
+    gemm_flops = 6.0 * R * H * I
+    gu_bytes = 4.0 * e_act * H * I + 2.0 * T * H + 2.0 * R * I      # weights, x, h
+    dn_bytes = 2.0 * e_act * I * H + 2.0 * R * I + 2.0 * R * H      # weights, h, y
+    layer_s = ms * 1e-3
+    gemm_s = (dur["gate_up"] + dur["down"]) * 1e-3
+    gu_s = dur["gate_up"] * 1e-3
+    achieved_gbs = gu_bytes / gu_s / 1e9
+
+    traffic = None
+    if a.traffic and os.path.exists(a.traffic):
+        traffic = json.load(open(a.traffic)).get("gate_up_bytes")
+
+    rec = {
+        "metric": "MoE layer us + grouped-GEMM TFLOP/s (% bf16 MFMA peak), T=2048 H=4096 E=64",
+        "value": round(gemm_flops / layer_s / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s MoE layer share" % a.config, "T": T, "H": H, "E": E, "top_k": k,
+                   "I": I, "routing": cfg.get("routing"), "m_pad": m_pad, "active_experts": e_act},
+        "layer_us": round(ms * 1e3, 2),
+        "gemm_tflops": round(gemm_flops / gemm_s / 1e12, 2),
+        "gemm_mfma_peak_frac": round(gemm_flops / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernel_us": {n: round(v * 1e3, 2) for n, v in dur.items()},
+        "roofline": {
+            "kernel": "grouped_gemm gate/up (SiLU*up epilogue)",
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+        },
+    }
+    if a.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(d, a.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(d, target_s):
+    """The oracle, untuned, on a bounded sample of tokens of the same workload."""
+    import oracle
+    T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
+    if "logits" in d:
+        idx, w = oracle.route(d["logits"], k)
+    else:
+        idx, w = d["topk_idx"], d["topk_w"]
+    n = 8
+    rng = np.random.default_rng(0)
+    while True:
+        toks = np.sort(rng.choice(T, min(n, T), replace=False)).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.moe_tokens(d["x"], idx, w, d["wg"], d["wu"], d["wd"], tokens=toks)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= T:
+            break
+        n = int(min(T, max(2 * n, n * target_s / max(dt, 1e-3) * 1.1)))
+    flops = 6.0 * len(toks) * k * H * I
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "%d of %d tokens (all %d routed slots each), fp64 per-token loops" % (len(toks), T, k)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+/*
+ * moe.h -- C ABI of the grouped-GEMM Mixture-of-Experts library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * One GPU's share of an MoE layer, computed as a grouped GEMM: token rows are
+ * bucketed by their routed expert and each bucket is multiplied by that
+ * expert's own weights.  The path is
+ *
+ *   moe_route -> moe_permute -> grouped_gemm (gate/up, SiLU*up epilogue)
+ *             -> grouped_gemm (down) -> moe_combine          (= moe_layer)
+ *
+ * Sources of the operations (the pages this library follows):
+ *   [P1] "Comm-compute fusion (3): ThunderKittens multi-GPU programming and a
+ *        fusable GEMM template" -- section 4: the grouped GEMM template (rows
+ *        grouped by expert, each group times its own weights; 128-row blocks
+ *        as task and expert alignment unit; a prologue hook before a row
+ *        block is loaded and an epilogue hook after a tile lands).
+ *   [P2] "Comm-compute fusion (1): why write communication into the GEMM
+ *        kernel" -- section 1: the serial MoE layer, expert GEMM (gate/up)
+ *        -> SiLU -> GEMM (down); section 4, four-dataflow table: MoE layer0
+ *        = prologue + reorder by route, layer1 = epilogue + top-k weighted
+ *        reduction.
+ *   [P4] "TIRx and high-performance GEMM (part 2)" -- the dense fp16
+ *        D = A * B^T GEMM with fp32 accumulation (steps 7-9, performance
+ *        table), which is the one-group degenerate case of grouped_gemm.
+ * Routing (top-k + softmax over the k chosen logits), tie-breaks, row order
+ * and padding contents are not fixed by the pages; the readings taken are
+ * stated at each function.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer, owned by the caller.  The
+ *     library never allocates, frees or synchronizes; scratch space comes
+ *     from a caller-provided workspace.
+ *   - bf16 / fp16 tensors are passed as raw 16-bit storage; every tensor is
+ *     dense row-major.  Pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Each call validates its arguments on the host, enqueues its kernels on
+ *     `stream` and returns at once.  Argument errors are reported before any
+ *     HIP call is made; a failed launch returns MOE_ERR_DEVICE.  Faults inside
+ *     kernels surface at the caller's next synchronization.
+ *   - Calls are reentrant; the only global state is a per-device cache of
+ *     the compute-unit count, filled on first use.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define MOE_OK 0
+#define MOE_ERR_INVALID 1     /* null pointer, non-positive size, k > E, misaligned pointer */
+#define MOE_ERR_UNSUPPORTED 2 /* a size or combination the kernels do not handle */
+#define MOE_ERR_WORKSPACE 3   /* workspace or row capacity too small */
+#define MOE_ERR_DEVICE 4      /* no usable device, or a launch failed */
+
+/* Element types of GEMM operands. */
+#define MOE_BF16 0
+#define MOE_FP16 1
+
+/* Layout of the per-group B operand of grouped_gemm. */
+#define MOE_B_KN 0 /* B[g] is [K][N], N contiguous (expert weights [E,H,I] / [E,I,H]) */
+#define MOE_B_NK 1 /* B[g] is [N][K], K contiguous (the dense D = A * B^T case)      */
+
+/* Epilogues of grouped_gemm. */
+#define MOE_EPI_STORE 0    /* D[r][n] = round(acc)                              */
+#define MOE_EPI_SILU_MUL 1 /* D[r][n] = round(SiLU(A.B)[r][n] * (A.B2)[r][n])  */
+
+#define MOE_ROW_BLOCK 128 /* rows per task and per-expert alignment unit [P1 s.4] */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *moe_status_string(int status);
+
+/* Library version string. */
+const char *moe_version(void);
+
+/* Upper bound on the padded row count M_pad of any routing of T tokens to
+ * top-k of E experts: each non-empty expert adds at most 127 padding rows,
+ * rounded up to whole 128-row blocks:  ceil128(T*k + min(E, T*k) * 127).
+ * Returns -1 for invalid sizes. */
+int moe_padded_capacity(int T, int k, int E);
+
+/* ------------------------------------------------------------------------
+ * moe_route -- top-k routing of router logits.                    [P2 s.4]
+ * For each token t: the k experts with the largest logits[t][:], slot 0 the
+ * largest, equal logits ordered by the lower expert id; topk_w[t][j] is the
+ * softmax over the k selected logits (fp32: exp(l_j - l_0) / sum_j').
+ *   logits   [T][E] fp32 (finite)
+ *   topk_idx [T][k] int32 out
+ *   topk_w   [T][k] fp32 out
+ * Requires 1 <= k <= E, k <= 16, E <= 1024.
+ * ---------------------------------------------------------------------- */
+int moe_route(const float *logits, int T, int E, int k, int32_t *topk_idx,
+              float *topk_w, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_permute -- reorder (token, slot) pairs into expert-contiguous,
+ * 128-row-aligned blocks.                              [P1 s.4; P2 s.4, s.5]
+ * Pair p = t*k + j routed to expert e = topk_idx[p].  Outputs:
+ *   expert_counts  [E]    rows routed to each expert
+ *   expert_offsets [E+1]  exclusive prefix sum of counts rounded up to
+ *                         multiples of 128 (an empty expert takes 0 rows);
+ *                         offsets[E] = M_pad
+ *   pair_to_row    [T*k]  row of pair p; within an expert rows follow
+ *                         ascending p (a stable counting sort)
+ *   row_to_pair    [cap]  inverse map; -1 for padding rows and rows >= M_pad
+ *   block_expert   [cap/128] expert of each 128-row block; -1 beyond M_pad
+ *   num_padded_rows [1]   M_pad (device int32, read by grouped_gemm)
+ *   x_perm         [cap][H] bf16, optional (x and x_perm both non-NULL):
+ *                  x_perm[row] = x[row_to_pair[row] / k]; zeros for padding.
+ * cap must be a multiple of 128 and >= moe_padded_capacity(T, k, E).
+ * Expert ids outside [0, E) are undefined behaviour.
+ * Workspace: moe_permute_workspace_size(T, k, E) bytes, 256-byte aligned.
+ * ---------------------------------------------------------------------- */
+size_t moe_permute_workspace_size(int T, int k, int E);
+int moe_permute(const int32_t *topk_idx, int T, int k, int E, const void *x,
+                int H, int32_t *expert_counts, int32_t *expert_offsets,
+                int32_t *pair_to_row, int32_t *row_to_pair,
+                int32_t *block_expert, int32_t *num_padded_rows, void *x_perm,
+                int cap, void *workspace, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * grouped_gemm -- D[r] = A[a(r)] . B[g(r)] over 128-row blocks.   [P1 s.4]
+ * Row r (0 <= r < M_pad, M_pad = *num_rows read on the device and clamped to
+ * cap) belongs to group g(r) = block_group[r / 128] (a negative entry skips
+ * the block).  Its A row is
+ *     a(r) = r                          if a_src_row == NULL
+ *     a(r) = a_src_row[r] / a_src_div   otherwise (the gate/up GEMM passes
+ *                                       row_to_pair and k: the row gather
+ *                                       of the reorder-by-route prologue)
+ * Rows with a_src_row[r] < 0 are padding: their outputs are unspecified.
+ *   dtype      MOE_BF16 or MOE_FP16 (A, B, B2 and D all of this type)
+ *   A          [*][K]   (rows addressed by a(r))
+ *   B, B2      [G][K][N] (MOE_B_KN) or [G][N][K] (MOE_B_NK); B2 only for
+ *              MOE_EPI_SILU_MUL (the up weights; B holds the gate weights)
+ *   D          [cap][N]
+ * Accumulation is fp32 (MFMA); the epilogue rounds to nearest even.
+ * Requires N % 64 == 0, K % 64 == 0, cap % 128 == 0.
+ * ---------------------------------------------------------------------- */
+int grouped_gemm(int dtype, int N, int K, int cap, const void *A,
+                 const int32_t *a_src_row, int a_src_div, const void *B,
+                 const void *B2, int b_layout, const int32_t *block_group,
+                 const int32_t *num_rows, int epilogue, void *D, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_combine -- top-k weighted reduction back to token order.    [P2 s.4]
+ *   out[t][n] = round_bf16( sum_{j<k} topk_w[t][j] * y[pair_to_row[t*k+j]][n] )
+ * accumulated in fp32 in slot order.
+ *   y [*][H] bf16 (expert outputs in permuted row order), out [T][H] bf16.
+ * Requires H % 8 == 0.
+ * ---------------------------------------------------------------------- */
+int moe_combine(const void *y, int H, const int32_t *pair_to_row,
+                const float *topk_w, int T, int k, void *out, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_layer -- the whole share:                               [P2 s.1, s.4]
+ *   out[t] = sum_j w[t][j] * ( SiLU(x[t] . Wg[e]) * (x[t] . Wu[e]) ) . Wd[e],
+ *   e = topk_idx[t][j].
+ * If logits != NULL the routing is computed by moe_route; otherwise
+ * topk_idx_in / topk_w_in give it.
+ *   x [T][H] bf16; w_gate, w_up [E][H][I] bf16; w_down [E][I][H] bf16;
+ *   out [T][H] bf16.
+ * Intermediates: h = SiLU(gate)*up stored as bf16 [M_pad][I], expert outputs
+ * y stored as bf16 [M_pad][H]; both live in the workspace.
+ * Requires H % 64 == 0, I % 64 == 0, plus the limits of the steps.
+ * Workspace: moe_layer_workspace_size(T, H, E, k, I) bytes, 256-byte aligned.
+ * ---------------------------------------------------------------------- */
+size_t moe_layer_workspace_size(int T, int H, int E, int k, int I);
+
+/* Byte offsets of the intermediates inside the moe_layer workspace, for
+ * inspection by callers and tests.  off[] receives, in order:
+ *   0 topk_idx [T*k] int32      1 topk_w [T*k] fp32
+ *   2 expert_counts [E] int32   3 expert_offsets [E+1] int32
+ *   4 pair_to_row [T*k] int32   5 row_to_pair [cap] int32
+ *   6 block_expert [cap/128]    7 num_padded_rows [1] int32
+ *   8 h [cap][I] bf16           9 y [cap][H] bf16
+ *  10 permute scratch          11 total size
+ * Returns MOE_OK or MOE_ERR_INVALID. */
+int moe_layer_workspace_layout(int T, int H, int E, int k, int I,
+                               size_t off[12]);
+
+int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
+              const float *topk_w_in, const void *w_gate, const void *w_up,
+              const void *w_down, int T, int H, int E, int k, int I, void *out,
+              void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

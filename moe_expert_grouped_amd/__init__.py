@@ -1,0 +1,272 @@
+"""Grouped-GEMM Mixture-of-Experts layer for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C ABI declared in ``include/moe.h``: every
+function here only checks and marshals arguments (torch tensors on the GPU,
+the current HIP stream) and calls the library; every step of the path runs in
+the HIP kernels of ``libmoe_gfx950.so``.  There is no CPU fallback: if the
+library is not built, or no GPU is present, calls raise.
+
+    idx, w = route(logits, k)
+    perm   = permute(idx, E)                       # counts, offsets, row maps
+    h      = grouped_gemm(x, wg, perm.block_expert, perm.num_padded_rows, N=I, K=H,
+                          cap=perm.cap, a_src_row=perm.row_to_pair, a_src_div=k,
+                          B2=wu, epilogue="silu_mul")
+    y      = grouped_gemm(h, wd, perm.block_expert, perm.num_padded_rows, N=H, K=I, cap=perm.cap)
+    out    = combine(y, perm.pair_to_row, w)
+    out    = layer(x, wg, wu, wd, k, logits=logits)   # all of the above in one call
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_gfx950.so")
+ROW_BLOCK = 128
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
+_DTYPES = {torch.bfloat16: 0, torch.float16: 1}
+_LAYOUTS = {"kn": 0, "nk": 1}
+_EPIS = {"store": 0, "silu_mul": 1}
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__("%s failed: %s (status %d)" % (fn, msg, status))
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(
+                "libmoe_gfx950.so is not built (%s); run `python -m moe_expert_grouped_amd.build` "
+                "or __graft_entry__.build()" % path)
+        lib = ctypes.CDLL(path)
+        P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        sig = {
+            "moe_status_string": ([I], ctypes.c_char_p),
+            "moe_version": ([], ctypes.c_char_p),
+            "moe_padded_capacity": ([I, I, I], I),
+            "moe_route": ([P, I, I, I, P, P, P], I),
+            "moe_permute_workspace_size": ([I, I, I], Z),
+            "moe_permute": ([P, I, I, I, P, I, P, P, P, P, P, P, P, I, P, Z, P], I),
+            "grouped_gemm": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P], I),
+            "moe_combine": ([P, I, P, P, I, I, P, P], I),
+            "moe_layer_workspace_size": ([I, I, I, I, I], Z),
+            "moe_layer_workspace_layout": ([I, I, I, I, I, ctypes.POINTER(Z)], I),
+            "moe_layer": ([P, P, P, P, P, P, P, I, I, I, I, I, P, P, Z, P], I),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = lib
+    return _lib
+
+
+def _check(fn, status):
+    if status != MOE_OK:
+        raise MoeError(fn, status, load_library().moe_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype=None, dims=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if dims is not None and t.dim() != dims:
+        raise ValueError("%s must have %d dims" % (name, dims))
+
+
+def padded_capacity(T: int, k: int, E: int) -> int:
+    return int(load_library().moe_padded_capacity(T, k, E))
+
+
+# ---------------------------------------------------------------- route
+
+def route(logits: torch.Tensor, k: int):
+    """Top-k experts per token (slot 0 the largest logit, ties to the lower id)
+    and the softmax over the k chosen logits.  Returns (idx int32, w fp32)."""
+    _need(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check("moe_route", load_library().moe_route(_ptr(logits), T, E, k, _ptr(idx), _ptr(w), _stream()))
+    return idx, w
+
+
+# ---------------------------------------------------------------- permute
+
+@dataclass
+class Permutation:
+    counts: torch.Tensor          # [E]
+    offsets: torch.Tensor         # [E+1]
+    pair_to_row: torch.Tensor     # [T*k]
+    row_to_pair: torch.Tensor     # [cap]
+    block_expert: torch.Tensor    # [cap/128]
+    num_padded_rows: torch.Tensor # [1] (device)
+    x_perm: torch.Tensor | None   # [cap, H] or None
+    cap: int
+
+
+def permute(topk_idx: torch.Tensor, E: int, x: torch.Tensor | None = None, cap: int | None = None,
+            workspace: torch.Tensor | None = None) -> Permutation:
+    """Stable expert-major permutation of the (token, slot) pairs into
+    128-row-aligned blocks; optionally gathers x into x_perm."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    lib = load_library()
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    if cap is None:
+        cap = padded_capacity(T, k, E)
+    i32 = dict(dtype=torch.int32, device=dev)
+    counts = torch.empty(E, **i32)
+    offsets = torch.empty(E + 1, **i32)
+    p2r = torch.empty(T * k, **i32)
+    r2p = torch.empty(max(cap, 0), **i32)
+    be = torch.empty(max(cap, 0) // ROW_BLOCK, **i32)
+    mpad = torch.empty(1, **i32)
+    H = 0
+    x_perm = None
+    if x is not None:
+        _need(x, "x", torch.bfloat16, 2)
+        H = x.shape[1]
+        x_perm = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    need = lib.moe_permute_workspace_size(T, k, E)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check("moe_permute", lib.moe_permute(
+        _ptr(topk_idx), T, k, E, _ptr(x), H, _ptr(counts), _ptr(offsets), _ptr(p2r), _ptr(r2p),
+        _ptr(be), _ptr(mpad), _ptr(x_perm), cap, _ptr(workspace), workspace.numel(), _stream()))
+    return Permutation(counts, offsets, p2r, r2p, be, mpad, x_perm, cap)
+
+
+# ---------------------------------------------------------------- grouped GEMM
+
+def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
+                 num_rows: torch.Tensor, *, N: int, K: int, cap: int,
+                 a_src_row: torch.Tensor | None = None, a_src_div: int = 1,
+                 B2: torch.Tensor | None = None, b_layout: str = "kn", epilogue: str = "store",
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """D[r] = A[a(r)] . B[block_group[r // 128]] for r < min(num_rows, cap),
+    or SiLU(A.B) * (A.B2) with epilogue="silu_mul".  Returns D [cap, N]."""
+    _need(A, "A", (torch.bfloat16, torch.float16))
+    _need(B, "B", A.dtype)
+    _need(block_group, "block_group", torch.int32)
+    _need(num_rows, "num_rows", torch.int32)
+    if B2 is not None:
+        _need(B2, "B2", A.dtype)
+    if a_src_row is not None:
+        _need(a_src_row, "a_src_row", torch.int32)
+    if out is None:
+        out = torch.empty((cap, N), dtype=A.dtype, device=A.device)
+    else:
+        _need(out, "out", A.dtype)
+    _check("grouped_gemm", load_library().grouped_gemm(
+        _DTYPES[A.dtype], N, K, cap, _ptr(A), _ptr(a_src_row), a_src_div, _ptr(B), _ptr(B2),
+        _LAYOUTS[b_layout], _ptr(block_group), _ptr(num_rows), _EPIS[epilogue], _ptr(out),
+        _stream()))
+    return out
+
+
+# ---------------------------------------------------------------- combine
+
+def combine(y: torch.Tensor, pair_to_row: torch.Tensor, topk_w: torch.Tensor,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """out[t] = sum_j topk_w[t, j] * y[pair_to_row[t*k + j]] (fp32 sum, bf16 out)."""
+    _need(y, "y", torch.bfloat16, 2)
+    _need(pair_to_row, "pair_to_row", torch.int32)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    T, k = topk_w.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _check("moe_combine", load_library().moe_combine(
+        _ptr(y), H, _ptr(pair_to_row), _ptr(topk_w), T, k, _ptr(out), _stream()))
+    return out
+
+
+# ---------------------------------------------------------------- whole layer
+
+LAYOUT_NAMES = ["topk_idx", "topk_w", "expert_counts", "expert_offsets", "pair_to_row",
+                "row_to_pair", "block_expert", "num_padded_rows", "h", "y", "permute_scratch"]
+
+
+def layer_workspace_layout(T, H, E, k, I):
+    arr = (ctypes.c_size_t * 12)()
+    _check("moe_layer_workspace_layout", load_library().moe_layer_workspace_layout(T, H, E, k, I, arr))
+    return {name: int(arr[i]) for i, name in enumerate(LAYOUT_NAMES)} | {"total": int(arr[11])}
+
+
+def layer_workspace(T, H, E, k, I, device="cuda") -> torch.Tensor:
+    n = load_library().moe_layer_workspace_size(T, H, E, k, I)
+    if n == 0:
+        raise ValueError("invalid layer sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def layer(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, k: int,
+          logits: torch.Tensor | None = None, topk_idx: torch.Tensor | None = None,
+          topk_w: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+          out: torch.Tensor | None = None) -> torch.Tensor:
+    """The MoE layer share: route (or the given routing) -> permute -> gate/up
+    grouped GEMM with SiLU*up -> down grouped GEMM -> top-k weighted combine."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_gate, "w_gate", torch.bfloat16, 3)
+    _need(w_up, "w_up", torch.bfloat16, 3)
+    _need(w_down, "w_down", torch.bfloat16, 3)
+    T, H = x.shape
+    E, _, I = w_gate.shape
+    if logits is not None:
+        _need(logits, "logits", torch.float32, 2)
+    else:
+        _need(topk_idx, "topk_idx", torch.int32, 2)
+        _need(topk_w, "topk_w", torch.float32, 2)
+    if workspace is None:
+        workspace = layer_workspace(T, H, E, k, I, x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _check("moe_layer", load_library().moe_layer(
+        _ptr(x), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), T, H, E, k, I, _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def workspace_view(workspace: torch.Tensor, T, H, E, k, I, name: str) -> torch.Tensor:
+    """A typed view of one intermediate inside a moe_layer workspace."""
+    lay = layer_workspace_layout(T, H, E, k, I)
+    cap = padded_capacity(T, k, E)
+    shapes = {
+        "topk_idx": ((T, k), torch.int32), "topk_w": ((T, k), torch.float32),
+        "expert_counts": ((E,), torch.int32), "expert_offsets": ((E + 1,), torch.int32),
+        "pair_to_row": ((T * k,), torch.int32), "row_to_pair": ((cap,), torch.int32),
+        "block_expert": ((cap // ROW_BLOCK,), torch.int32), "num_padded_rows": ((1,), torch.int32),
+        "h": ((cap, I), torch.bfloat16), "y": ((cap, H), torch.bfloat16),
+    }
+    shape, dt = shapes[name]
+    n = 1
+    for s in shape:
+        n *= s
+    nbytes = n * torch.empty((), dtype=dt).element_size()
+    start = lay[name]
+    return workspace[start:start + nbytes].view(dt).view(shape)

@@ -1,0 +1,239 @@
+// api.hip -- the C ABI (include/moe.h): argument validation, workspace
+// carving and kernel launches.  Validation happens before any HIP call, so
+// every error path can be exercised without a GPU.
+#include <mutex>
+
+#include "../../include/moe.h"
+#include "common.h"
+
+namespace moe {
+hipError_t launch_route(const float *, int, int, int, int32_t *, float *, hipStream_t);
+size_t permute_workspace_bytes(long R, int E);
+hipError_t launch_permute(const int32_t *, int, int, int, const uint16_t *, int, int32_t *,
+                          int32_t *, int32_t *, int32_t *, int32_t *, int32_t *, uint16_t *, int,
+                          void *, hipStream_t);
+hipError_t launch_grouped_gemm(int, int, int, int, const uint16_t *, const int32_t *, int,
+                               const uint16_t *, const uint16_t *, int, const int32_t *,
+                               const int32_t *, int, uint16_t *, int, hipStream_t);
+hipError_t launch_combine(const uint16_t *, int, const int32_t *, const float *, int, int,
+                          uint16_t *, hipStream_t);
+} // namespace moe
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+int g_cus[kMaxDevices]; // 0 = not queried yet
+
+// Compute-unit count of the current device; 0 if there is no usable device.
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_cus[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    g_cus[dev] = prop.multiProcessorCount;
+  }
+  return g_cus[dev];
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+int check_route(const float *logits, int T, int E, int k, const int32_t *idx, const float *w) {
+  if (!logits || !idx || !w) return MOE_ERR_INVALID;
+  if (T <= 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID;
+  if (E > 1024 || k > 16) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+long padded_cap(long T, long k, long E) {
+  const long R = T * k;
+  const long cap = R + (E < R ? E : R) * (MOE_ROW_BLOCK - 1);
+  return (cap + MOE_ROW_BLOCK - 1) / MOE_ROW_BLOCK * MOE_ROW_BLOCK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *moe_status_string(int s) {
+  switch (s) {
+  case MOE_OK: return "ok";
+  case MOE_ERR_INVALID: return "invalid argument";
+  case MOE_ERR_UNSUPPORTED: return "unsupported size or combination";
+  case MOE_ERR_WORKSPACE: return "workspace or capacity too small";
+  case MOE_ERR_DEVICE: return "device error";
+  default: return "unknown status";
+  }
+}
+
+const char *moe_version(void) { return "moe-grouped-gfx950 0.1"; }
+
+int moe_padded_capacity(int T, int k, int E) {
+  if (T <= 0 || k <= 0 || E <= 0) return -1;
+  const long cap = padded_cap(T, k, E);
+  return cap > 0x7fffffffL ? -1 : (int)cap;
+}
+
+int moe_route(const float *logits, int T, int E, int k, int32_t *topk_idx, float *topk_w,
+              void *stream) {
+  int st = check_route(logits, T, E, k, topk_idx, topk_w);
+  if (st != MOE_OK) return st;
+  if (device_cus() == 0) return MOE_ERR_DEVICE;
+  return launch_status(
+      moe::launch_route(logits, T, E, k, topk_idx, topk_w, (hipStream_t)stream));
+}
+
+size_t moe_permute_workspace_size(int T, int k, int E) {
+  if (T <= 0 || k <= 0 || E <= 0) return 0;
+  return align256(moe::permute_workspace_bytes((long)T * k, E));
+}
+
+int moe_permute(const int32_t *topk_idx, int T, int k, int E, const void *x, int H,
+                int32_t *counts, int32_t *offsets, int32_t *pair_to_row, int32_t *row_to_pair,
+                int32_t *block_expert, int32_t *num_padded_rows, void *x_perm, int cap,
+                void *workspace, size_t ws_bytes, void *stream) {
+  if (!topk_idx || !counts || !offsets || !pair_to_row || !row_to_pair || !block_expert ||
+      !num_padded_rows || !workspace)
+    return MOE_ERR_INVALID;
+  if (T <= 0 || k <= 0 || E <= 0 || cap <= 0) return MOE_ERR_INVALID;
+  if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID;
+  if (x && (H <= 0 || !aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID;
+  if (E > 1024) return MOE_ERR_UNSUPPORTED;
+  if (x && H % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((long)T * k > 0x7fffffffL) return MOE_ERR_UNSUPPORTED;
+  if (cap % MOE_ROW_BLOCK != 0) return MOE_ERR_INVALID;
+  if (cap < padded_cap(T, k, E)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < moe_permute_workspace_size(T, k, E)) return MOE_ERR_WORKSPACE;
+  if (device_cus() == 0) return MOE_ERR_DEVICE;
+  return launch_status(moe::launch_permute(
+      topk_idx, T, k, E, (const uint16_t *)x, H, counts, offsets, pair_to_row, row_to_pair,
+      block_expert, num_padded_rows, (uint16_t *)x_perm, cap, workspace, (hipStream_t)stream));
+}
+
+int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t *a_src_row,
+                 int a_src_div, const void *B, const void *B2, int b_layout,
+                 const int32_t *block_group, const int32_t *num_rows, int epilogue, void *D,
+                 void *stream) {
+  if (!A || !B || !block_group || !num_rows || !D) return MOE_ERR_INVALID;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(D) || (B2 && !aligned16(B2)))
+    return MOE_ERR_INVALID;
+  if (N <= 0 || K <= 0 || cap <= 0) return MOE_ERR_INVALID;
+  if (dtype != MOE_BF16 && dtype != MOE_FP16) return MOE_ERR_UNSUPPORTED;
+  if (b_layout != MOE_B_KN && b_layout != MOE_B_NK) return MOE_ERR_UNSUPPORTED;
+  if (epilogue != MOE_EPI_STORE && epilogue != MOE_EPI_SILU_MUL) return MOE_ERR_UNSUPPORTED;
+  if (epilogue == MOE_EPI_SILU_MUL && !B2) return MOE_ERR_INVALID;
+  if (a_src_row && a_src_div <= 0) return MOE_ERR_INVALID;
+  if (N % 64 != 0 || K % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (cap % MOE_ROW_BLOCK != 0) return MOE_ERR_INVALID;
+  const int cus = device_cus();
+  if (cus == 0) return MOE_ERR_DEVICE;
+  return launch_status(moe::launch_grouped_gemm(
+      dtype, N, K, cap, (const uint16_t *)A, a_src_row, a_src_div, (const uint16_t *)B,
+      (const uint16_t *)B2, b_layout, block_group, num_rows, epilogue, (uint16_t *)D, cus,
+      (hipStream_t)stream));
+}
+
+int moe_combine(const void *y, int H, const int32_t *pair_to_row, const float *topk_w, int T,
+                int k, void *out, void *stream) {
+  if (!y || !pair_to_row || !topk_w || !out) return MOE_ERR_INVALID;
+  if (H <= 0 || T <= 0 || k <= 0) return MOE_ERR_INVALID;
+  if (!aligned16(y) || !aligned16(out)) return MOE_ERR_INVALID;
+  if (H % 8 != 0 || k > 16) return MOE_ERR_UNSUPPORTED;
+  if (device_cus() == 0) return MOE_ERR_DEVICE;
+  return launch_status(moe::launch_combine((const uint16_t *)y, H, pair_to_row, topk_w, T, k,
+                                           (uint16_t *)out, (hipStream_t)stream));
+}
+
+int moe_layer_workspace_layout(int T, int H, int E, int k, int I, size_t off[12]) {
+  if (!off || T <= 0 || H <= 0 || E <= 0 || k <= 0 || I <= 0 || k > E) return MOE_ERR_INVALID;
+  const long R = (long)T * k;
+  const long cap = padded_cap(T, k, E);
+  size_t o = 0;
+  auto take = [&](int i, size_t bytes) {
+    off[i] = o;
+    o += align256(bytes);
+  };
+  take(0, R * 4);
+  take(1, R * 4);
+  take(2, (size_t)E * 4);
+  take(3, (size_t)(E + 1) * 4);
+  take(4, R * 4);
+  take(5, cap * 4);
+  take(6, (cap / MOE_ROW_BLOCK) * 4);
+  take(7, 4);
+  take(8, (size_t)cap * I * 2);
+  take(9, (size_t)cap * H * 2);
+  take(10, moe::permute_workspace_bytes(R, E));
+  off[11] = o;
+  return MOE_OK;
+}
+
+size_t moe_layer_workspace_size(int T, int H, int E, int k, int I) {
+  size_t off[12];
+  if (moe_layer_workspace_layout(T, H, E, k, I, off) != MOE_OK) return 0;
+  return off[11];
+}
+
+int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
+              const float *topk_w_in, const void *w_gate, const void *w_up, const void *w_down,
+              int T, int H, int E, int k, int I, void *out, void *workspace, size_t ws_bytes,
+              void *stream) {
+  if (!x || !w_gate || !w_up || !w_down || !out || !workspace) return MOE_ERR_INVALID;
+  if (!logits && (!topk_idx_in || !topk_w_in)) return MOE_ERR_INVALID;
+  if (T <= 0 || H <= 0 || E <= 0 || k <= 0 || I <= 0 || k > E) return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(out) || !aligned16(workspace))
+    return MOE_ERR_INVALID;
+  if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (E > 1024 || k > 16) return MOE_ERR_UNSUPPORTED;
+  if ((long)T * k > 0x7fffffffL / 2) return MOE_ERR_UNSUPPORTED;
+  size_t off[12];
+  moe_layer_workspace_layout(T, H, E, k, I, off);
+  if (ws_bytes < off[11]) return MOE_ERR_WORKSPACE;
+  const int cus = device_cus();
+  if (cus == 0) return MOE_ERR_DEVICE;
+
+  hipStream_t s = (hipStream_t)stream;
+  unsigned char *ws = (unsigned char *)workspace;
+  int32_t *idx = (int32_t *)(ws + off[0]);
+  float *w = (float *)(ws + off[1]);
+  int32_t *counts = (int32_t *)(ws + off[2]);
+  int32_t *offsets = (int32_t *)(ws + off[3]);
+  int32_t *p2r = (int32_t *)(ws + off[4]);
+  int32_t *r2p = (int32_t *)(ws + off[5]);
+  int32_t *bexp = (int32_t *)(ws + off[6]);
+  int32_t *mpad = (int32_t *)(ws + off[7]);
+  uint16_t *h = (uint16_t *)(ws + off[8]);
+  uint16_t *y = (uint16_t *)(ws + off[9]);
+  void *pws = ws + off[10];
+  const int cap = (int)padded_cap(T, k, E);
+
+  const int32_t *ridx = topk_idx_in;
+  const float *rw = topk_w_in;
+  hipError_t e;
+  if (logits) {
+    e = moe::launch_route(logits, T, E, k, idx, w, s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    ridx = idx;
+    rw = w;
+  }
+  e = moe::launch_permute(ridx, T, k, E, nullptr, 0, counts, offsets, p2r, r2p, bexp, mpad,
+                          nullptr, cap, pws, s);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  e = moe::launch_grouped_gemm(MOE_BF16, I, H, cap, (const uint16_t *)x, r2p, k,
+                               (const uint16_t *)w_gate, (const uint16_t *)w_up, MOE_B_KN, bexp,
+                               mpad, MOE_EPI_SILU_MUL, h, cus, s);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  e = moe::launch_grouped_gemm(MOE_BF16, H, I, cap, h, nullptr, 1, (const uint16_t *)w_down,
+                               nullptr, MOE_B_KN, bexp, mpad, MOE_EPI_STORE, y, cus, s);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  e = moe::launch_combine(y, H, p2r, rw, T, k, (uint16_t *)out, s);
+  return launch_status(e);
+}
+
+} // extern "C"

@@ -1,0 +1,149 @@
+"""The C ABI on the host: the library loads, exports every entry point that
+include/moe.h declares, and rejects bad arguments before touching a device.
+No compute call is made (there may be no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_expert_grouped_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail("libmoe_gfx950.so not built: run __graft_entry__.build()")
+    return moe.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 11, names
+    for n in ["moe_route", "moe_permute", "grouped_gemm", "moe_combine", "moe_layer"]:
+        assert n in names
+    for n in names:
+        assert hasattr(lib, n), "missing export " + n
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.moe_status_string(s)
+    assert lib.moe_status_string(99) == b"unknown status"
+    assert lib.moe_version().startswith(b"moe-grouped")
+
+
+def test_padded_capacity(lib):
+    # ceil128(R + min(E, R) * 127)
+    for T, k, E in [(256, 2, 8), (2048, 4, 64), (2048, 1, 16), (128, 1, 16), (16384, 8, 64), (1, 1, 1), (3, 2, 1000)]:
+        R = T * k
+        cap = R + min(E, R) * 127
+        cap = (cap + 127) // 128 * 128
+        assert lib.moe_padded_capacity(T, k, E) == cap
+    assert lib.moe_padded_capacity(0, 1, 1) == -1
+    assert lib.moe_padded_capacity(1, 0, 1) == -1
+
+
+def test_layer_workspace_layout(lib):
+    T, H, E, k, I = 2048, 4096, 64, 4, 512
+    lay = moe.layer_workspace_layout(T, H, E, k, I)
+    offs = [lay[n] for n in moe.LAYOUT_NAMES]
+    assert offs == sorted(offs)
+    assert all(o % 256 == 0 for o in offs)
+    cap = moe.padded_capacity(T, k, E)
+    assert lay["y"] - lay["h"] >= cap * I * 2
+    assert lay["total"] - lay["y"] >= cap * H * 2
+    assert lib.moe_layer_workspace_size(T, H, E, k, I) == lay["total"]
+    assert lib.moe_layer_workspace_size(T, H, E, 65, I) == 0  # k > E
+
+
+FAKE = ctypes.c_void_p(4096)       # aligned non-null; never dereferenced
+MISALIGNED = ctypes.c_void_p(4098)
+NULL = None
+
+
+def test_route_validation(lib):
+    assert lib.moe_route(NULL, 4, 8, 2, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID
+    assert lib.moe_route(FAKE, 4, 8, 9, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID     # k > E
+    assert lib.moe_route(FAKE, 0, 8, 2, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID
+    assert lib.moe_route(FAKE, 4, 2048, 2, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(FAKE, 4, 64, 17, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_permute_validation(lib):
+    ws = lib.moe_permute_workspace_size(100, 2, 8)
+    assert ws > 0
+    cap = lib.moe_padded_capacity(100, 2, 8)
+    args = lambda **kw: dict(dict(idx=FAKE, T=100, k=2, E=8, x=NULL, H=0, cap=cap, ws=FAKE, wsb=ws), **kw)
+
+    def call(a):
+        return lib.moe_permute(a["idx"], a["T"], a["k"], a["E"], a["x"], a["H"], FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, FAKE if a["x"] else NULL, a["cap"], a["ws"], a["wsb"], NULL)
+    assert call(args(idx=NULL)) == moe.MOE_ERR_INVALID
+    assert call(args(cap=cap - 128)) == moe.MOE_ERR_WORKSPACE
+    assert call(args(cap=cap + 1)) == moe.MOE_ERR_INVALID
+    assert call(args(wsb=ws - 1)) == moe.MOE_ERR_WORKSPACE
+    assert call(args(E=2000)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(args(x=FAKE, H=12)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(args(x=MISALIGNED, H=16)) == moe.MOE_ERR_INVALID
+
+
+def test_grouped_gemm_validation(lib):
+    def call(dtype=0, N=128, K=128, cap=256, A=FAKE, src=NULL, div=1, B=FAKE, B2=NULL, lay=0,
+             bg=FAKE, nr=FAKE, epi=0, D=FAKE):
+        return lib.grouped_gemm(dtype, N, K, cap, A, src, div, B, B2, lay, bg, nr, epi, D, NULL)
+    assert call(A=NULL) == moe.MOE_ERR_INVALID
+    assert call(A=MISALIGNED) == moe.MOE_ERR_INVALID
+    assert call(N=96) == moe.MOE_ERR_UNSUPPORTED
+    assert call(K=100) == moe.MOE_ERR_UNSUPPORTED
+    assert call(cap=200) == moe.MOE_ERR_INVALID
+    assert call(dtype=5) == moe.MOE_ERR_UNSUPPORTED
+    assert call(lay=3) == moe.MOE_ERR_UNSUPPORTED
+    assert call(epi=1) == moe.MOE_ERR_INVALID          # SiLU*up needs B2
+    assert call(epi=7) == moe.MOE_ERR_UNSUPPORTED
+    assert call(src=FAKE, div=0) == moe.MOE_ERR_INVALID
+
+
+def test_combine_and_layer_validation(lib):
+    assert lib.moe_combine(NULL, 64, FAKE, FAKE, 4, 2, FAKE, NULL) == moe.MOE_ERR_INVALID
+    assert lib.moe_combine(FAKE, 12, FAKE, FAKE, 4, 2, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine(FAKE, 64, FAKE, FAKE, 4, 17, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
+    T, H, E, k, I = 64, 128, 8, 2, 64
+    ws = lib.moe_layer_workspace_size(T, H, E, k, I)
+
+    def call(x=FAKE, logits=FAKE, idx=NULL, w=NULL, H=H, I=I, k=k, wsb=ws):
+        return lib.moe_layer(x, logits, idx, w, FAKE, FAKE, FAKE, T, H, E, k, I, FAKE, FAKE, wsb, NULL)
+    assert call(x=NULL) == moe.MOE_ERR_INVALID
+    assert call(logits=NULL) == moe.MOE_ERR_INVALID            # neither logits nor routing
+    assert call(H=96) == moe.MOE_ERR_UNSUPPORTED
+    assert call(I=80) == moe.MOE_ERR_UNSUPPORTED
+    assert call(k=9) == moe.MOE_ERR_INVALID
+    assert call(wsb=ws - 1) == moe.MOE_ERR_WORKSPACE
+
+
+def test_valid_call_without_device_reports_device_error(lib):
+    # only meaningful where no GPU is visible; on a GPU machine the call would launch
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert lib.moe_route(FAKE, 4, 8, 2, FAKE, FAKE, NULL) == moe.MOE_ERR_DEVICE
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    saved = moe._lib
+    try:
+        moe._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            moe.load_library(str(tmp_path / "missing.so"))
+    finally:
+        moe._lib = saved

@@ -1,0 +1,133 @@
+"""GPU parity of the grouped GEMM with the oracle.
+
+Integer-exact cases (entries in {-1, 0, 1}) must match bit for bit: every
+partial sum is a small integer, exact in fp32 in any order, so any row,
+column, group or k-slice mapping mistake shows.  Random cases are held to
+the bf16 tolerances."""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_grouped_amd as moe
+import oracle
+from moe_expert_grouped_amd import synthetic as syn
+from _util import assert_close, dev16, host16, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _groups(nblk, G, seed, neg_tail=0):
+    g = np.random.default_rng(seed)
+    bg = np.sort(g.integers(0, G, size=nblk)).astype(np.int32)
+    if neg_tail:
+        bg[-neg_tail:] = -1
+    return bg
+
+
+def _run(A_bits, B_bits, bg, *, N, K, cap, m_rows, dtype, layout="kn", src=None, div=1, B2_bits=None,
+         epi="store"):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    out = torch.full((cap, N), float("nan"), dtype=tdt, device="cuda")
+    D = moe.grouped_gemm(dev16(A_bits, tdt), dev16(B_bits, tdt), torch.from_numpy(bg).cuda(),
+                         torch.tensor([m_rows], dtype=torch.int32, device="cuda"), N=N, K=K, cap=cap,
+                         a_src_row=None if src is None else torch.from_numpy(src).cuda(), a_src_div=div,
+                         B2=None if B2_bits is None else dev16(B2_bits, tdt), b_layout=layout,
+                         epilogue=epi, out=out)
+    torch.cuda.synchronize()
+    return D
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("N,K", [(256, 320), (192, 128), (128, 64), (64, 512)])
+def test_integer_exact(dtype, layout, N, K):
+    G, nblk = 3, 5
+    cap = (nblk + 1) * 128
+    m_rows = nblk * 128
+    bg = _groups(cap // 128, G, N + K, neg_tail=1)
+    A = syn.ternary_bits((cap, K), 1, dtype)
+    B = syn.ternary_bits((G, K, N) if layout == "kn" else (G, N, K), 2, dtype)
+    say("gemm integer", dtype, layout, N, K)
+    D = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype=dtype, layout=layout)
+    ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, is_fp16=(dtype == "fp16"), b_layout=layout,
+                              rows=np.arange(m_rows, dtype=np.int32))
+    got = to_f64(D)
+    assert np.array_equal(got[:m_rows], ref)
+    assert np.all(np.isnan(got[m_rows:]))  # rows beyond num_rows untouched
+
+
+def test_integer_exact_gather_and_negative_group():
+    # A rows gathered through a permutation with padding; one block without a group
+    K, N, G = 256, 128, 4
+    T = 300
+    A = syn.ternary_bits((T, K), 3)
+    B = syn.ternary_bits((G, K, N), 4)
+    cap = 6 * 128
+    bg = np.array([0, 3, -1, 3, 1, 2], np.int32)
+    g = np.random.default_rng(1)
+    src = g.integers(0, T * 2, size=cap).astype(np.int32)
+    src[g.random(cap) < 0.2] = -1
+    say("gemm gather")
+    D = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=cap, dtype="bf16", src=src, div=2)
+    ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, a_src_row=src, a_src_div=2)
+    got = to_f64(D)
+    real = (src >= 0) & (np.repeat(bg, 128) >= 0)
+    assert np.array_equal(got[real], ref[real])
+    assert np.all(np.isnan(got[256:384]))  # the block without a group is not written
+
+
+def test_integer_exact_silu_mul_gate_only_rows():
+    # up weights all one-hot so up = one A entry; gate ternary: checks gate/up pairing per column
+    K, N, G = 192, 128, 2
+    A = syn.ternary_bits((256, K), 5)
+    Bg = syn.ternary_bits((G, K, N), 6)
+    Bu = syn.ternary_bits((G, K, N), 7)
+    bg = np.array([1, 0], np.int32)
+    say("gemm silu integer")
+    D = _run(A, Bg, bg, N=N, K=K, cap=256, m_rows=256, dtype="bf16", B2_bits=Bu, epi="silu_mul")
+    ref = oracle.grouped_gemm(A, Bg, bg, N=N, K=K, B2_bits=Bu, epilogue="silu_mul")
+    assert_close(to_f64(D), ref, "silu integer", max_frac=8e-3, rel_fro=4e-3)
+
+
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("epi", ["store", "silu_mul"])
+def test_random_vs_oracle(layout, epi):
+    G, K, N = 5, 448, 320
+    cap = 9 * 128
+    bg = _groups(9, G, 3)
+    g = np.random.default_rng(7)
+    A = syn.bf16_bits(g.standard_normal((700, K)).astype(np.float32))
+    shape = (G, K, N) if layout == "kn" else (G, N, K)
+    B = syn.bf16_bits((g.standard_normal(shape) / np.sqrt(K)).astype(np.float32))
+    B2 = syn.bf16_bits((g.standard_normal(shape) / np.sqrt(K)).astype(np.float32)) if epi == "silu_mul" else None
+    src = g.integers(-1, 700, size=cap).astype(np.int32)
+    say("gemm random", layout, epi)
+    D = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=cap, dtype="bf16", layout=layout, src=src, div=1,
+             B2_bits=B2, epi=epi)
+    ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, b_layout=layout, a_src_row=src, B2_bits=B2, epilogue=epi)
+    real = src >= 0
+    assert_close(to_f64(D)[real], ref[real], "random %s %s" % (layout, epi))
+
+
+def test_dense_fp16_degenerate_case_sampled():
+    # D = A . B^T, 4096^3 fp16, one group: sampled rows against the oracle,
+    # and every element against the library GEMM (hipBLASLt via torch)
+    d = syn.make_config("dense")
+    M = N = K = 4096
+    say("dense 4096 fp16")
+    A = dev16(d["A"], torch.float16)
+    B = dev16(d["B"], torch.float16)
+    D = moe.grouped_gemm(A, B, torch.zeros(32, dtype=torch.int32, device="cuda"),
+                         torch.tensor([M], dtype=torch.int32, device="cuda"), N=N, K=K, cap=M,
+                         b_layout="nk")
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(0).choice(M, 24, replace=False).astype(np.int32)
+    rows = np.concatenate([rows, [0, 127, 128, 4095]]).astype(np.int32)
+    ref = oracle.grouped_gemm(d["A"], d["B"].reshape(1, N, K), np.zeros(32, np.int32), N=N, K=K,
+                              is_fp16=True, b_layout="nk", rows=rows)
+    got = to_f64(D)[rows]
+    # fp16 output of values up to ~100: half-ulp 0.03; fp32 accumulation of 4096 terms
+    assert np.max(np.abs(got - ref)) <= 0.07
+    assert_close(got, ref, "dense sampled")
+    lib = (A.float() @ B.float().T)
+    assert_close(to_f64(D), lib.double().cpu().numpy(), "dense vs library")

@@ -1,0 +1,129 @@
+"""GPU parity of the whole MoE layer share (moe_layer and the step-by-step
+path) with the oracle, on every workload shape: bit-exact routing and
+permutation inside the layer's workspace, outputs within the bf16
+tolerances (max |err| <= 2e-2 max |ref|, relative Frobenius <= 5e-3).
+Small shapes compare every output; full shapes compare all index arrays and
+a seeded sample of tokens (tokens are independent)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_grouped_amd as moe
+import oracle
+from moe_expert_grouped_amd import synthetic as syn
+from _util import assert_close, dev16, host16, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs_dev(d):
+    return dict(x=dev16(d["x"]), wg=dev16(d["wg"]), wu=dev16(d["wu"]), wd=dev16(d["wd"]))
+
+
+def _routing(d):
+    if "logits" in d:
+        return oracle.route(d["logits"], d["k"])
+    return d["topk_idx"], d["topk_w"]
+
+
+def _run_layer(d, D):
+    T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
+    ws = moe.layer_workspace(T, H, E, k, I)
+    if "logits" in d:
+        out = moe.layer(D["x"], D["wg"], D["wu"], D["wd"], k, logits=torch.from_numpy(d["logits"]).cuda(),
+                        workspace=ws)
+    else:
+        out = moe.layer(D["x"], D["wg"], D["wu"], D["wd"], k, topk_idx=torch.from_numpy(d["topk_idx"]).cuda(),
+                        topk_w=torch.from_numpy(d["topk_w"]).cuda(), workspace=ws)
+    torch.cuda.synchronize()
+    return out, ws
+
+
+def _check_layer(d, tokens=None, what=""):
+    T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
+    say("layer", what, dict(T=T, H=H, E=E, k=k, I=I))
+    D = _inputs_dev(d)
+    out, ws = _run_layer(d, D)
+    idx, w = _routing(d)
+    # routing and permutation inside the layer: bit-exact
+    view = lambda n: moe.workspace_view(ws, T, H, E, k, I, n).cpu().numpy()
+    if "logits" in d:
+        assert np.array_equal(view("topk_idx"), idx), what
+        assert np.max(np.abs(view("topk_w") - w) / w) <= 1e-6
+    P = oracle.permute(idx, E)
+    for n_ws, n_or in [("expert_counts", "counts"), ("expert_offsets", "offsets"),
+                       ("pair_to_row", "pair_to_row"), ("row_to_pair", "row_to_pair"),
+                       ("block_expert", "block_expert")]:
+        assert np.array_equal(view(n_ws), P[n_or]), "%s %s" % (what, n_ws)
+    assert int(view("num_padded_rows")[0]) == P["m_pad"]
+    # values: the layer's definition, token by token
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int32)
+    ref = oracle.moe_tokens(d["x"], idx, w, d["wg"], d["wu"], d["wd"], tokens=tokens)
+    got = to_f64(out)[tokens]
+    r = assert_close(got, ref, what)
+    say("layer", what, "max|err|/max|ref| %.2e  relFro %.2e" % r)
+    return out, ws, D
+
+
+def test_layer_tiny_every_token():
+    _check_layer(syn.make_config("tiny"), what="tiny")
+
+
+def test_layer_tiny_steps_match_layer():
+    # the five entry points called one by one give the same bits as moe_layer
+    d = syn.make_config("tiny")
+    T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
+    D = _inputs_dev(d)
+    say("layer steps tiny")
+    out, ws = _run_layer(d, D)
+    idx, w = moe.route(torch.from_numpy(d["logits"]).cuda(), k)
+    P = moe.permute(idx, E)
+    h = moe.grouped_gemm(D["x"], D["wg"], P.block_expert, P.num_padded_rows, N=I, K=H, cap=P.cap,
+                         a_src_row=P.row_to_pair, a_src_div=k, B2=D["wu"], epilogue="silu_mul")
+    y = moe.grouped_gemm(h, D["wd"], P.block_expert, P.num_padded_rows, N=H, K=I, cap=P.cap)
+    out2 = moe.combine(y, P.pair_to_row, w)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    # intermediate h against the oracle's gate/up GEMM (real rows)
+    Po = oracle.permute(idx.cpu().numpy(), E)
+    href = oracle.grouped_gemm(d["x"], d["wg"], Po["block_expert"], N=I, K=H, a_src_row=Po["row_to_pair"],
+                               a_src_div=k, B2_bits=d["wu"], epilogue="silu_mul", M=Po["m_pad"])
+    real = Po["row_to_pair"][:Po["m_pad"]] >= 0
+    assert_close(to_f64(h)[:Po["m_pad"]][real], href[real], "h")
+    # combine against the oracle's combine of the GPU's own y (only the reduction differs)
+    cref = oracle.combine(host16(y), Po["pair_to_row"], w.cpu().numpy())
+    assert_close(to_f64(out2), cref, "combine", max_frac=8e-3, rel_fro=3e-3)
+
+
+def test_layer_deterministic_and_linear():
+    d = syn.make_config("tiny")
+    D = _inputs_dev(d)
+    say("layer determinism")
+    o1, _ = _run_layer(d, D)
+    o2, _ = _run_layer(d, D)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    # scaling the down weights by 2 scales every output by 2, bit for bit
+    D2 = dict(D)
+    D2["wd"] = (D["wd"].float() * 2).to(torch.bfloat16)
+    o3, _ = _run_layer(d, D2)
+    assert torch.equal((o1.float() * 2).to(torch.bfloat16).view(torch.int16), o3.view(torch.int16))
+
+
+def test_layer_small_shapes():
+    # ragged experts, several tiles, K slices below the ring depth, E = 1
+    for (T, H, E, k, I, seed) in [(300, 128, 6, 2, 192, 1), (97, 256, 16, 4, 64, 2), (130, 64, 1, 1, 128, 3),
+                                  (40, 512, 3, 3, 256, 4)]:
+        d = syn.make_moe(T, H, E, k, I, seed=seed)
+        _check_layer(d, what="small T%d H%d E%d k%d I%d" % (T, H, E, k, I))
+
+
+def _sample(T, n, seed=0):
+    s = np.random.default_rng(seed).choice(T, n, replace=False)
+    return np.sort(np.concatenate([s, [0, T - 1]])).astype(np.int32)
+
+
+@pytest.mark.parametrize("name,n", [("tp_share", 96), ("ep_skew", 96), ("ep_skew_small", 128), ("prefill", 40)])
+def test_layer_full_size(name, n):
+    d = syn.make_config(name)
+    _check_layer(d, tokens=_sample(d["T"], min(n, d["T"] - 2)), what=name)
