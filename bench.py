@@ -34,9 +34,21 @@ def parse():
     p.add_argument("--config", default="tp_share")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample (0 disables it)")
-    p.add_argument("--traffic", default=None,
-                   help="json file with rocprof FETCH/WRITE-derived HBM bytes per launch")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="instead of the layer, run a plain device copy of MIB MiB a few times "
+                        "(reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
 
 
 def main():
@@ -50,7 +62,13 @@ def main():
     from moe_expert_grouped_amd import synthetic as syn
 
     torch.cuda.set_device(0)
+    if a.calibrate_copy:
+        calibrate_copy(a.calibrate_copy)
+        return
     cfg = syn.CONFIGS[a.config]
+    if cfg["kind"] == "dense":
+        bench_dense(a)
+        return
     d = syn.make_config(a.config)
     T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
     dev16 = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
@@ -78,30 +96,28 @@ def main():
     # ---- per-kernel durations: HIP events on the launch stream, same path step by step
     stream = torch.cuda.current_stream()
     names = ["route", "permute", "gate_up", "down", "combine"]
-    ev = {n: [] for n in names}
+    timed = []
     R = T * k
-    if given:
-        idx_t, w_t = tidx, tw
-    with torch.cuda.stream(stream):
-        for it in range(a.warmup + a.steps):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-            e[0].record(stream)
-            if not given:
-                idx_t, w_t = moe.route(logits, k)
-            e[1].record(stream)
-            P = moe.permute(idx_t, E)
-            e[2].record(stream)
-            h = moe.grouped_gemm(x, wg, P.block_expert, P.num_padded_rows, N=I, K=H, cap=P.cap,
-                                 a_src_row=P.row_to_pair, a_src_div=k, B2=wu, epilogue="silu_mul")
-            e[3].record(stream)
-            y = moe.grouped_gemm(h, wd, P.block_expert, P.num_padded_rows, N=H, K=I, cap=P.cap)
-            e[4].record(stream)
-            moe.combine(y, P.pair_to_row, w_t, out=out)
-            e[5].record(stream)
-            if it >= a.warmup:
-                ev["_events"] = ev.get("_events", []) + [e]
+    idx_t, w_t = (tidx, tw) if given else (None, None)
+    for it in range(a.warmup + a.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        e[0].record(stream)
+        if not given:
+            idx_t, w_t = moe.route(logits, k)
+        e[1].record(stream)
+        P = moe.permute(idx_t, E)
+        e[2].record(stream)
+        h = moe.grouped_gemm(x, wg, P.block_expert, P.num_padded_rows, N=I, K=H, cap=P.cap,
+                             a_src_row=P.row_to_pair, a_src_div=k, B2=wu, epilogue="silu_mul")
+        e[3].record(stream)
+        y = moe.grouped_gemm(h, wd, P.block_expert, P.num_padded_rows, N=H, K=I, cap=P.cap)
+        e[4].record(stream)
+        moe.combine(y, P.pair_to_row, w_t, out=out)
+        e[5].record(stream)
+        if it >= a.warmup:
+            timed.append(e)
     torch.cuda.synchronize()
-    dur = {n: float(np.mean([es[i].elapsed_time(es[i + 1]) for es in ev["_events"]])) for i, n in enumerate(names)}
+    dur = {n: float(np.mean([es[i].elapsed_time(es[i + 1]) for es in timed])) for i, n in enumerate(names)}
     m_pad = int(P.num_padded_rows.item())
     counts = P.counts.cpu().numpy()
     e_act = int((counts > 0).sum())
@@ -115,9 +131,7 @@ def main():
     gu_s = dur["gate_up"] * 1e-3
     achieved_gbs = gu_bytes / gu_s / 1e9
 
-    traffic = None
-    if a.traffic and os.path.exists(a.traffic):
-        traffic = json.load(open(a.traffic)).get("gate_up_bytes")
+    traffic = recorded_traffic("grouped_gemm_gate_up_%s" % a.config)
 
     rec = {
         "metric": "MoE layer us + grouped-GEMM TFLOP/s (% bf16 MFMA peak), T=2048 H=4096 E=64",
@@ -151,6 +165,77 @@ def main():
     if a.cpu_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(d, a.cpu_seconds)
     print(json.dumps(rec), flush=True)
+
+
+def bench_dense(a):
+    """The degenerate one-group case: D = A . B^T, fp16 4096^3 (B stored [N][K])."""
+    import torch
+    import moe_expert_grouped_amd as moe
+    from moe_expert_grouped_amd import synthetic as syn
+    d = syn.make_config("dense")
+    M, N, K = d["M"], d["N"], d["K"]
+    dev16 = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.float16).cuda()
+    A, B = dev16(d["A"]), dev16(d["B"])
+    bg = torch.zeros(M // 128, dtype=torch.int32, device="cuda")
+    nr = torch.tensor([M], dtype=torch.int32, device="cuda")
+    D = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    ws = moe.gemm_workspace()
+
+    def step():
+        moe.grouped_gemm(A, B, bg, nr, N=N, K=K, cap=M, b_layout="nk", out=D, workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    kern_ms = e0.elapsed_time(e1) / a.steps
+    flops = 2.0 * M * N * K
+    tf = flops / (kern_ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "dense fp16 GEMM D = A.B^T (one-group grouped_gemm)", "value": round(tf, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": "dense fp16 GEMM M=N=K=4096, D = A.B^T, fp32 accumulate"},
+        "kernel_us": round(kern_ms * 1e3, 2),
+        "roofline": {"kernel": "grouped_gemm (one group, B [N][K], fp16)", "bound": "mfma",
+                     "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }), flush=True)
+
+
+GEMM_SRC = os.path.join(ROOT, "moe_expert_grouped_amd", "csrc", "grouped_gemm.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def recorded_traffic(name):
+    """HBM bytes per launch of a kernel from its committed rocprof counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the plain-copy calibration),
+    or None when there is none or the kernel source changed since."""
+    import hashlib
+    path = os.path.join(PROFILES, name + ".md")
+    if not os.path.exists(path):
+        return None
+    want = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith(("traffic_bytes_per_launch", "kernel_source_sha256")):
+            k, v = line.strip().split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != want:
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(d, target_s):

@@ -140,11 +140,19 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, const void *x,
  *   D          [cap][N]
  * Accumulation is fp32 (MFMA); the epilogue rounds to nearest even.
  * Requires N % 64 == 0, K % 64 == 0, cap % 128 == 0.
+ * workspace (optional, may be NULL): scratch of at least
+ * grouped_gemm_workspace_size() bytes, 256-byte aligned, contents need not be
+ * initialized.  With it, the tasks of a last, partly filled round are split
+ * along K over all workgroups (fp32 partial tiles, summed in K order, so the
+ * result is deterministic); without it, every task runs whole.  Results are
+ * the same up to the fp32 summation order of the split tasks.
  * ---------------------------------------------------------------------- */
+size_t grouped_gemm_workspace_size(void);
 int grouped_gemm(int dtype, int N, int K, int cap, const void *A,
                  const int32_t *a_src_row, int a_src_div, const void *B,
                  const void *B2, int b_layout, const int32_t *block_group,
-                 const int32_t *num_rows, int epilogue, void *D, void *stream);
+                 const int32_t *num_rows, int epilogue, void *D,
+                 void *workspace, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * moe_combine -- top-k weighted reduction back to token order.    [P2 s.4]
@@ -178,10 +186,11 @@ size_t moe_layer_workspace_size(int T, int H, int E, int k, int I);
  *   4 pair_to_row [T*k] int32   5 row_to_pair [cap] int32
  *   6 block_expert [cap/128]    7 num_padded_rows [1] int32
  *   8 h [cap][I] bf16           9 y [cap][H] bf16
- *  10 permute scratch          11 total size
+ *  10 permute scratch          11 grouped-GEMM scratch
+ *  12 total size
  * Returns MOE_OK or MOE_ERR_INVALID. */
 int moe_layer_workspace_layout(int T, int H, int E, int k, int I,
-                               size_t off[12]);
+                               size_t off[13]);
 
 int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
               const float *topk_w_in, const void *w_gate, const void *w_up,

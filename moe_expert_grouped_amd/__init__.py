@@ -58,7 +58,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "moe_route": ([P, I, I, I, P, P, P], I),
             "moe_permute_workspace_size": ([I, I, I], Z),
             "moe_permute": ([P, I, I, I, P, I, P, P, P, P, P, P, P, I, P, Z, P], I),
-            "grouped_gemm": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P], I),
+            "grouped_gemm_workspace_size": ([], Z),
+            "grouped_gemm": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P, Z, P], I),
             "moe_combine": ([P, I, P, P, I, I, P, P], I),
             "moe_layer_workspace_size": ([I, I, I, I, I], Z),
             "moe_layer_workspace_layout": ([I, I, I, I, I, ctypes.POINTER(Z)], I),
@@ -167,9 +168,12 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
                  num_rows: torch.Tensor, *, N: int, K: int, cap: int,
                  a_src_row: torch.Tensor | None = None, a_src_div: int = 1,
                  B2: torch.Tensor | None = None, b_layout: str = "kn", epilogue: str = "store",
-                 out: torch.Tensor | None = None) -> torch.Tensor:
+                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 split_tail: bool = True) -> torch.Tensor:
     """D[r] = A[a(r)] . B[block_group[r // 128]] for r < min(num_rows, cap),
-    or SiLU(A.B) * (A.B2) with epilogue="silu_mul".  Returns D [cap, N]."""
+    or SiLU(A.B) * (A.B2) with epilogue="silu_mul".  Returns D [cap, N].
+    With split_tail, a scratch workspace lets the last partly filled round of
+    tasks be split along K (allocated here if not given)."""
     _need(A, "A", (torch.bfloat16, torch.float16))
     _need(B, "B", A.dtype)
     _need(block_group, "block_group", torch.int32)
@@ -182,11 +186,30 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
         out = torch.empty((cap, N), dtype=A.dtype, device=A.device)
     else:
         _need(out, "out", A.dtype)
-    _check("grouped_gemm", load_library().grouped_gemm(
+    lib = load_library()
+    if split_tail and workspace is None:
+        workspace = gemm_workspace(A.device)
+    if not split_tail:
+        workspace = None
+    _check("grouped_gemm", lib.grouped_gemm(
         _DTYPES[A.dtype], N, K, cap, _ptr(A), _ptr(a_src_row), a_src_div, _ptr(B), _ptr(B2),
         _LAYOUTS[b_layout], _ptr(block_group), _ptr(num_rows), _EPIS[epilogue], _ptr(out),
-        _stream()))
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream()))
     return out
+
+
+_gemm_ws = {}
+
+
+def gemm_workspace(device="cuda") -> torch.Tensor:
+    """A cached scratch buffer of grouped_gemm_workspace_size() bytes per device."""
+    dev = torch.device(device)
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    ws = _gemm_ws.get(key)
+    if ws is None:
+        ws = torch.empty(load_library().grouped_gemm_workspace_size(), dtype=torch.uint8, device=dev)
+        _gemm_ws[key] = ws
+    return ws
 
 
 # ---------------------------------------------------------------- combine
@@ -209,13 +232,14 @@ def combine(y: torch.Tensor, pair_to_row: torch.Tensor, topk_w: torch.Tensor,
 # ---------------------------------------------------------------- whole layer
 
 LAYOUT_NAMES = ["topk_idx", "topk_w", "expert_counts", "expert_offsets", "pair_to_row",
-                "row_to_pair", "block_expert", "num_padded_rows", "h", "y", "permute_scratch"]
+                "row_to_pair", "block_expert", "num_padded_rows", "h", "y", "permute_scratch",
+                "gemm_scratch"]
 
 
 def layer_workspace_layout(T, H, E, k, I):
-    arr = (ctypes.c_size_t * 12)()
+    arr = (ctypes.c_size_t * 13)()
     _check("moe_layer_workspace_layout", load_library().moe_layer_workspace_layout(T, H, E, k, I, arr))
-    return {name: int(arr[i]) for i, name in enumerate(LAYOUT_NAMES)} | {"total": int(arr[11])}
+    return {name: int(arr[i]) for i, name in enumerate(LAYOUT_NAMES)} | {"total": int(arr[12])}
 
 
 def layer_workspace(T, H, E, k, I, device="cuda") -> torch.Tensor:

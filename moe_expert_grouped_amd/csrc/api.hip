@@ -14,7 +14,9 @@ hipError_t launch_permute(const int32_t *, int, int, int, const uint16_t *, int,
                           void *, hipStream_t);
 hipError_t launch_grouped_gemm(int, int, int, int, const uint16_t *, const int32_t *, int,
                                const uint16_t *, const uint16_t *, int, const int32_t *,
-                               const int32_t *, int, uint16_t *, int, hipStream_t);
+                               const int32_t *, int, uint16_t *, void *, size_t, int,
+                               hipStream_t);
+size_t gg_workspace_bytes(int grid);
 hipError_t launch_combine(const uint16_t *, int, const int32_t *, const float *, int, int,
                           uint16_t *, hipStream_t);
 } // namespace moe
@@ -22,6 +24,7 @@ hipError_t launch_combine(const uint16_t *, int, const int32_t *, const float *,
 namespace {
 
 constexpr int kMaxDevices = 64;
+constexpr int kDefaultCus = 256; // sizing when no device is visible (MI355X)
 std::mutex g_mu;
 int g_cus[kMaxDevices]; // 0 = not queried yet
 
@@ -115,10 +118,15 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, const void *x, int
       block_expert, num_padded_rows, (uint16_t *)x_perm, cap, workspace, (hipStream_t)stream));
 }
 
+size_t grouped_gemm_workspace_size(void) {
+  const int cus = device_cus();
+  return align256(moe::gg_workspace_bytes(cus > 0 ? cus : kDefaultCus));
+}
+
 int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t *a_src_row,
                  int a_src_div, const void *B, const void *B2, int b_layout,
                  const int32_t *block_group, const int32_t *num_rows, int epilogue, void *D,
-                 void *stream) {
+                 void *workspace, size_t ws_bytes, void *stream) {
   if (!A || !B || !block_group || !num_rows || !D) return MOE_ERR_INVALID;
   if (!aligned16(A) || !aligned16(B) || !aligned16(D) || (B2 && !aligned16(B2)))
     return MOE_ERR_INVALID;
@@ -130,12 +138,13 @@ int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t 
   if (a_src_row && a_src_div <= 0) return MOE_ERR_INVALID;
   if (N % 64 != 0 || K % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (cap % MOE_ROW_BLOCK != 0) return MOE_ERR_INVALID;
+  if (workspace && !aligned16(workspace)) return MOE_ERR_INVALID;
   const int cus = device_cus();
   if (cus == 0) return MOE_ERR_DEVICE;
   return launch_status(moe::launch_grouped_gemm(
       dtype, N, K, cap, (const uint16_t *)A, a_src_row, a_src_div, (const uint16_t *)B,
-      (const uint16_t *)B2, b_layout, block_group, num_rows, epilogue, (uint16_t *)D, cus,
-      (hipStream_t)stream));
+      (const uint16_t *)B2, b_layout, block_group, num_rows, epilogue, (uint16_t *)D,
+      workspace, workspace ? ws_bytes : 0, cus, (hipStream_t)stream));
 }
 
 int moe_combine(const void *y, int H, const int32_t *pair_to_row, const float *topk_w, int T,
@@ -149,7 +158,7 @@ int moe_combine(const void *y, int H, const int32_t *pair_to_row, const float *t
                                            (uint16_t *)out, (hipStream_t)stream));
 }
 
-int moe_layer_workspace_layout(int T, int H, int E, int k, int I, size_t off[12]) {
+int moe_layer_workspace_layout(int T, int H, int E, int k, int I, size_t off[13]) {
   if (!off || T <= 0 || H <= 0 || E <= 0 || k <= 0 || I <= 0 || k > E) return MOE_ERR_INVALID;
   const long R = (long)T * k;
   const long cap = padded_cap(T, k, E);
@@ -169,14 +178,15 @@ int moe_layer_workspace_layout(int T, int H, int E, int k, int I, size_t off[12]
   take(8, (size_t)cap * I * 2);
   take(9, (size_t)cap * H * 2);
   take(10, moe::permute_workspace_bytes(R, E));
-  off[11] = o;
+  take(11, grouped_gemm_workspace_size());
+  off[12] = o;
   return MOE_OK;
 }
 
 size_t moe_layer_workspace_size(int T, int H, int E, int k, int I) {
-  size_t off[12];
+  size_t off[13];
   if (moe_layer_workspace_layout(T, H, E, k, I, off) != MOE_OK) return 0;
-  return off[11];
+  return off[12];
 }
 
 int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
@@ -192,9 +202,9 @@ int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
   if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (E > 1024 || k > 16) return MOE_ERR_UNSUPPORTED;
   if ((long)T * k > 0x7fffffffL / 2) return MOE_ERR_UNSUPPORTED;
-  size_t off[12];
+  size_t off[13];
   moe_layer_workspace_layout(T, H, E, k, I, off);
-  if (ws_bytes < off[11]) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < off[12]) return MOE_ERR_WORKSPACE;
   const int cus = device_cus();
   if (cus == 0) return MOE_ERR_DEVICE;
 
@@ -211,6 +221,8 @@ int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
   uint16_t *h = (uint16_t *)(ws + off[8]);
   uint16_t *y = (uint16_t *)(ws + off[9]);
   void *pws = ws + off[10];
+  void *gws = ws + off[11];
+  const size_t gws_bytes = off[12] - off[11];
   const int cap = (int)padded_cap(T, k, E);
 
   const int32_t *ridx = topk_idx_in;
@@ -227,10 +239,11 @@ int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   e = moe::launch_grouped_gemm(MOE_BF16, I, H, cap, (const uint16_t *)x, r2p, k,
                                (const uint16_t *)w_gate, (const uint16_t *)w_up, MOE_B_KN, bexp,
-                               mpad, MOE_EPI_SILU_MUL, h, cus, s);
+                               mpad, MOE_EPI_SILU_MUL, h, gws, gws_bytes, cus, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   e = moe::launch_grouped_gemm(MOE_BF16, H, I, cap, h, nullptr, 1, (const uint16_t *)w_down,
-                               nullptr, MOE_B_KN, bexp, mpad, MOE_EPI_STORE, y, cus, s);
+                               nullptr, MOE_B_KN, bexp, mpad, MOE_EPI_STORE, y, gws, gws_bytes,
+                               cus, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   e = moe::launch_combine(y, H, p2r, rw, T, k, (uint16_t *)out, s);
   return launch_status(e);

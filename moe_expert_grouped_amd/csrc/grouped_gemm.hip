@@ -33,6 +33,9 @@
 //     column -- exactly the MFMA B-operand layout;
 //   * v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulators in registers; each
 //     wavefront owns a 64 x (BN/2) quarter of the 128 x BN tile.
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "common.h"
 
 namespace moe {
@@ -51,6 +54,8 @@ struct GGArgs {
   const int32_t *num_rows;
   uint16_t *D;
   int N, K, cap;
+  int group_rows;  // row blocks per super-block of the task order (>= 1)
+  float *partials; // partial tiles of a split tail (NULL: no split)
 };
 
 // 16-byte-granule XOR swizzle of a tile stored with 128-byte rows (A tiles,
@@ -62,7 +67,7 @@ __device__ __forceinline__ int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); 
 // with ds_read_b64_tr_b16: one 16-lane group reads 4 consecutive k rows x 32
 // bytes, two groups read neighbouring 32-byte column pairs.
 template <int BN> __device__ __forceinline__ int swz_kn(int k) {
-  if constexpr (BN == 128)
+  if constexpr (BN >= 128)
     return 2 * (k & 3) + 8 * (k & 1);
   else
     return 2 * (k & 3);
@@ -106,6 +111,126 @@ __device__ __forceinline__ f32x16 mfma32(const i16x4 a0, const i16x4 a1, const i
                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Work schedule, shared by the GEMM kernel and the fixup kernel.
+//
+// Tasks (row block, column block) are cut into nx contiguous ranges, one per
+// XCD (workgroup w runs on XCD w % nx); the S workgroups of an XCD take its
+// tasks round-robin.  When the last round would be mostly empty (the XCD
+// has rem = ntx mod S leftover tasks, rem <= 3/4 S) and a partial-tile buffer
+// is given, those rem tasks are not handed out whole: their rem * KT
+// k-slices are split evenly over the S workgroups (a stream-K tail).  A
+// workgroup then owns at most two tail segments; a segment that covers a
+// whole task is finished in place, the others store fp32 partial tiles that
+// the fixup kernel sums in k order.
+struct Sched {
+  int nx, xcd, slot, S, KT, ncol, nblk;
+  int tx0, full, rem; // first task of this XCD, tasks handed out whole, tail tasks
+  long U;             // tail k-slices
+
+  __device__ void init(const GGArgs &a, int bn, int grid, int block) {
+    KT = a.K / kBK;
+    const int mrows = max(0, min(a.num_rows[0], a.cap));
+    nblk = mrows / kBM;
+    ncol = a.N / bn;
+    const int ntask = nblk * ncol;
+    nx = (grid % 8 == 0) ? 8 : 1;
+    xcd = block % nx;
+    slot = block / nx;
+    S = grid / nx;
+    tx0 = (int)(((long)ntask * xcd) / nx);
+    const int ntx = (int)(((long)ntask * (xcd + 1)) / nx) - tx0;
+    full = ntx / S * S;
+    rem = ntx - full;
+    if (!a.partials || rem == 0 || rem * 4 > S * 3) {
+      full = ntx;
+      rem = 0;
+    }
+    U = (long)rem * KT;
+  }
+  __device__ int bound(int s) const { return (int)(U * s / S); }
+  // tasks this workgroup receives whole
+  __device__ int n_full() const { return full > slot ? (full - slot + S - 1) / S : 0; }
+  // tail segments of slot s: [bound(s), bound(s+1)) in tail k-slices
+  __device__ int n_tail(int s) const {
+    const int r0 = bound(s), r1 = bound(s + 1);
+    return r1 > r0 ? (r1 - 1) / KT - r0 / KT + 1 : 0;
+  }
+  // item i of this workgroup: task, k-slice range [ka, kb), tail task index or -1
+  __device__ void item(int i, int &task, int &ka, int &kb, int &tt) const {
+    const int nf = n_full();
+    if (i < nf) {
+      task = tx0 + slot + i * S;
+      ka = 0;
+      kb = KT;
+      tt = -1;
+    } else {
+      const int r0 = bound(slot), r1 = bound(slot + 1);
+      tt = r0 / KT + (i - nf);
+      task = tx0 + full + tt;
+      ka = max(r0, tt * KT) - tt * KT;
+      kb = min(r1, (tt + 1) * KT) - tt * KT;
+    }
+  }
+};
+
+// Partial tile of one tail segment: ACC floats per thread, stored as
+// [ACC/4][256 threads][4] so each store and load is one coalesced 16-byte
+// access per lane.  Buffer (xcd, slot, j) holds the j-th tail segment
+// (j < 2) of that workgroup.
+__device__ __forceinline__ float *partial_tile(float *base, const Sched &sc, int s, int j,
+                                               int acc_per_thread) {
+  return base + ((size_t)(sc.xcd * sc.S + s) * 2 + j) * (size_t)acc_per_thread * kThreads;
+}
+
+// Epilogue of one 128 x BN output tile: every 32x32 accumulator tile goes
+// through a per-wavefront LDS tile so that each lane writes 16-byte row
+// pieces (the MFMA layout gives each lane one column of 4-row groups).
+template <int BN, int NB, bool FP16, int MI, int NI>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint16_t *Dt, int N,
+                                           MOE_LDS uint16_t *stg, int lane, int wm, int wn) {
+  constexpr int WN = BN / 2;
+  constexpr int EPI_LD = 40;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        float v = acc[0][i][j][r];
+        if constexpr (NB == 2) {
+          const float u = acc[1][i][j][r];
+          v = v / (1.0f + __expf(-v)) * u;
+        }
+        stg[row * EPI_LD + (lane & 31)] = FP16 ? f32_to_f16(v) : f32_to_bf16(v);
+      }
+      const int row = lane >> 1;
+      const int col = (lane & 1) * 16;
+      const u32x4 q0 = *(const MOE_LDS u32x4 *)(stg + row * EPI_LD + col);
+      const u32x4 q1 = *(const MOE_LDS u32x4 *)(stg + row * EPI_LD + col + 8);
+      uint16_t *dst = Dt + (size_t)(wm * 64 + i * 32 + row) * N + wn * WN + j * 32 + col;
+      *reinterpret_cast<u32x4 *>(dst) = q0;
+      *reinterpret_cast<u32x4 *>(dst + 8) = q1;
+    }
+}
+
+// Task order inside the whole-task phase: super-blocks of `group_rows` row
+// blocks; inside one, the column block varies slowest, so the row blocks of
+// a super-block (mostly one expert) read each weight tile at about the same
+// time and share it in L2, while a row block's A tile is reused by its
+// column tasks.
+__device__ __forceinline__ void task_coords(int task, int GR, int ncol, int nblk, int bn, int &b,
+                                            int &n0) {
+  const int span = GR * ncol;
+  const int sb = task / span;
+  const int r = task - sb * span;
+  const int rows = min(GR, nblk - sb * GR);
+  const int n = r / rows;
+  b = sb * GR + (r - n * rows);
+  n0 = n * bn;
+}
+
 // BN: output columns per task (per B matrix); NB: 1 (STORE) or 2 (gate+up);
 // KN: B stored [K][N] (else [N][K]); NSTAGE: LDS ring depth.
 template <int BN, int NB, bool KN, bool FP16, int NSTAGE>
@@ -119,42 +244,39 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   constexpr int A_INSTR = 4;       // DMA instructions per wavefront per A slice
   constexpr int B_INSTR = BN / 32; // per wavefront per B matrix per slice
   constexpr int LOADS = A_INSTR + NB * B_INSTR; // DMA ops per wavefront per slice
-  constexpr int IDX_SLOTS = 8;     // per-wavefront ring of task index tables
+  constexpr int IDX_SLOTS = 4;     // per-wavefront ring of task index tables
   constexpr int IDX_WORDS = 64;    // words per table: 32 source rows, then the group
+  constexpr int ACC = NB * MI * NI * 16; // accumulator floats per thread
   static_assert(LOADS * (NSTAGE - 2) < 64, "vmcnt range");
-  static_assert(NSTAGE >= 2 && NSTAGE < IDX_SLOTS, "ring depth");
+  static_assert(NSTAGE >= 2 && NSTAGE <= IDX_SLOTS, "ring depth");
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE_BYTES];
   __shared__ __attribute__((aligned(256))) int32_t idx_lds[4][IDX_SLOTS][IDX_WORDS];
+  __shared__ __attribute__((aligned(16))) uint16_t epi_lds[4][32 * 40];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1;
   const int wn = wave & 1;
-
   const int N = args.N, K = args.K;
-  const int KT = K / kBK;
-  const int mrows = max(0, min(args.num_rows[0], args.cap));
-  const int nblk = mrows / kBM;
-  const int ncol = N / BN;
-  const int ntask = nblk * ncol;
 
-  // XCD-aware split: contiguous task ranges per XCD, round-robin slots inside
-  const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
-  const int xcd = blockIdx.x % nx;
-  const int slot = blockIdx.x / nx;
-  const int S = gridDim.x / nx;
-  const int t_end = (int)(((long)ntask * (xcd + 1)) / nx);
-  const int t_first = (int)(((long)ntask * xcd) / nx) + slot;
+  Sched sc;
+  sc.init(args, BN, gridDim.x, blockIdx.x);
+  const int KT = sc.KT, ncol = sc.ncol, nblk = sc.nblk;
+  const int n_items = sc.n_full() + sc.n_tail(sc.slot);
+  auto coords = [&](int task, int &b, int &n0) {
+    task_coords(task, args.group_rows, ncol, nblk, BN, b, n0);
+  };
 
   const uint32_t smem_addr = lds_addr_of(smem);
   MOE_LDS int32_t(*my_idx)[IDX_WORDS] = (MOE_LDS int32_t(*)[IDX_WORDS])idx_lds[wave];
 
-  // DMA the index table of task `task` (the 32 source rows this wavefront
-  // loads and the block's group) into ring slot `seq`.
+  // DMA the index table of `task` (the 32 source rows this wavefront loads
+  // and the block's group) into ring slot `seq`.
   auto fetch_index = [&](int task, int seq) {
-    const int b = task / ncol;
+    int b, n0;
+    coords(task, b, n0);
     const uint32_t dst = (uint32_t)(uintptr_t)&my_idx[seq % IDX_SLOTS][0];
     if (args.a_src_row) {
       if (lane < 32)
@@ -167,17 +289,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   };
 
   // ---------------- issue (producer) state ----------------
-  int it_task = t_first;
-  int it_seq = 0; // sequence number of it_task among this workgroup's tasks
-  int it_kt = 0;
+  int it_i = 0;   // item being issued
+  int it_k = 0;   // next k-slice of it
+  int it_kb = 0;  // end of its k-slice range
+  int it_len = 0; // its length
   const unsigned char *a_src[A_INSTR];
   const unsigned char *b_src[NB][B_INSTR];
 
-  // Point the per-lane DMA sources at task `task`, whose index table sits in
+  // Point the per-lane DMA sources at `task`, whose index table sits in
   // ring slot `seq` and has landed.
   auto setup_issue = [&](int task, int seq) {
-    const int b = task / ncol;
-    const int n0 = (task - b * ncol) * BN;
+    int b, n0;
+    coords(task, b, n0);
     const MOE_LDS int32_t *tab = my_idx[seq % IDX_SLOTS];
     const int g = tab[32];
 #pragma unroll
@@ -215,58 +338,72 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
     }
   };
 
+  auto begin_issue_item = [&](int i) {
+    int task, ka, kb, tt;
+    sc.item(i, task, ka, kb, tt);
+    if (i + 1 < n_items) {
+      int t2, a2, b2, tt2;
+      sc.item(i + 1, t2, a2, b2, tt2);
+      fetch_index(t2, i + 1);
+    }
+    setup_issue(task, i);
+    it_k = ka;
+    it_kb = kb;
+    it_len = kb - ka;
+  };
+
   int n_issued = 0;
   auto issue_next = [&]() {
-    if (it_task >= t_end) return;
+    if (it_i >= n_items) return;
     const uint32_t stage = smem_addr + (n_issued % NSTAGE) * STAGE_BYTES;
-    const size_t a_off = (size_t)it_kt * kBK * 2;
+    const size_t a_off = (size_t)it_k * kBK * 2;
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i) dma16(a_src[i] + a_off, stage + (wave * A_INSTR + i) * 1024);
-    const size_t b_off = KN ? (size_t)it_kt * kBK * N * 2 : (size_t)it_kt * kBK * 2;
+    const size_t b_off = KN ? (size_t)it_k * kBK * N * 2 : (size_t)it_k * kBK * 2;
 #pragma unroll
     for (int m = 0; m < NB; ++m)
 #pragma unroll
       for (int i = 0; i < B_INSTR; ++i)
         dma16(b_src[m][i] + b_off, stage + A_BYTES + m * B_BYTES + (wave * B_INSTR + i) * 1024);
     ++n_issued;
-    if (++it_kt == KT) {
-      it_kt = 0;
-      it_task += S;
-      ++it_seq;
-      if (it_task < t_end) {
-        // the table of it_task was fetched before the first slice of the
-        // previous task; with KT >= NSTAGE that slice has been awaited
-        if (KT < NSTAGE) wait_vmcnt<0>();
-        if (it_task + S < t_end) fetch_index(it_task + S, it_seq + 1);
-        setup_issue(it_task, it_seq);
+    if (++it_k == it_kb) {
+      ++it_i;
+      if (it_i < n_items) {
+        // the table of item it_i was fetched right before the first slice of
+        // the previous item; once NSTAGE of that item's slices were issued
+        // it has been awaited (DMA completes in order)
+        if (it_len < NSTAGE) wait_vmcnt<0>();
+        begin_issue_item(it_i);
       }
     }
   };
 
-  if (it_task < t_end) {
-    fetch_index(it_task, 0);
+  if (n_items > 0) {
+    int task, ka, kb, tt;
+    sc.item(0, task, ka, kb, tt);
+    fetch_index(task, 0);
     wait_vmcnt<0>();
-    if (it_task + S < t_end) fetch_index(it_task + S, 1);
-    setup_issue(it_task, 0);
+    begin_issue_item(0);
   }
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s) issue_next();
 
   // ---------------- compute (consumer) ----------------
   int n_consumed = 0;
-  int seq = 0;
-  for (int task = t_first; task < t_end; task += S, ++seq) {
+  for (int i = 0; i < n_items; ++i) {
+    int task, ka, kb, tt;
+    sc.item(i, task, ka, kb, tt);
     f32x16 acc[NB][MI][NI];
 #pragma unroll
     for (int m = 0; m < NB; ++m)
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int a = 0; a < MI; ++a)
 #pragma unroll
         for (int j = 0; j < NI; ++j)
-          for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.0f;
+          for (int r = 0; r < 16; ++r) acc[m][a][j][r] = 0.0f;
     int group = 0;
 
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = ka; kt < kb; ++kt) {
       // this wavefront's DMA for slice n_consumed has landed ...
       if (n_issued - n_consumed - 1 >= NSTAGE - 2)
         wait_vmcnt<LOADS * (NSTAGE - 2)>();
@@ -275,7 +412,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
       // ... and so has every other wavefront's; everyone is done with the
       // stage the next issue overwrites
       block_barrier();
-      if (kt == 0) group = my_idx[seq % IDX_SLOTS][32];
+      if (kt == ka) group = __builtin_amdgcn_readfirstlane(my_idx[i % IDX_SLOTS][32]);
       issue_next();
 
       const MOE_LDS unsigned char *sA =
@@ -284,12 +421,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
       for (int kk = 0; kk < kBK / 16; ++kk) {
         i16x4 a[MI][2];
 #pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          const int row = wm * 64 + i * 32 + (lane & 31);
+        for (int mi = 0; mi < MI; ++mi) {
+          const int row = wm * 64 + mi * 32 + (lane & 31);
           const int c = (kk * 2 + (lane >> 5)) ^ swz128(row);
           const u32x4 v = *(const MOE_LDS u32x4 *)(sA + row * 128 + c * 16);
-          a[i][0] = __builtin_bit_cast(i16x4, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
-          a[i][1] = __builtin_bit_cast(i16x4, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
+          a[mi][0] = __builtin_bit_cast(i16x4, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
+          a[mi][1] = __builtin_bit_cast(i16x4, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
         }
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
@@ -318,72 +455,160 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
               b1 = __builtin_bit_cast(i16x4, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
             }
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
-              acc[m][i][j] = mfma32<FP16>(a[i][0], a[i][1], b0, b1, acc[m][i][j]);
+            for (int mi = 0; mi < MI; ++mi)
+              acc[m][mi][j] = mfma32<FP16>(a[mi][0], a[mi][1], b0, b1, acc[m][mi][j]);
           }
         }
       }
       ++n_consumed;
     }
 
-    // ---------------- epilogue ----------------
     if (group < 0) continue; // block without a group: no output
-    const int b = task / ncol;
-    const int n0 = (task - b * ncol) * BN;
-    uint16_t *Dt = args.D + (size_t)b * kBM * N + n0;
+    if (ka == 0 && kb == KT) {
+      int b, n0;
+      coords(task, b, n0);
+      store_tile<BN, NB, FP16, MI, NI>(acc, args.D + (size_t)b * kBM * N + n0, N,
+                                       (MOE_LDS uint16_t *)epi_lds[wave], lane, wm, wn);
+    } else {
+      // a piece of a split tail task: store the fp32 partial tile
+      float *pt = partial_tile(args.partials, sc, sc.slot, tt - sc.bound(sc.slot) / KT, ACC);
+      const float *flat = reinterpret_cast<const float *>(&acc[0][0][0]);
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int col = wn * WN + j * 32 + (lane & 31);
-          float v = acc[0][i][j][r];
-          if constexpr (NB == 2) {
-            const float u = acc[1][i][j][r];
-            v = v / (1.0f + __expf(-v)) * u;
-          }
-          Dt[(size_t)row * N + col] = FP16 ? f32_to_f16(v) : f32_to_bf16(v);
-        }
+      for (int q = 0; q < ACC / 4; ++q) {
+        f32x4 v = {flat[4 * q], flat[4 * q + 1], flat[4 * q + 2], flat[4 * q + 3]};
+        *reinterpret_cast<f32x4 *>(pt + ((size_t)q * kThreads + tid) * 4) = v;
+      }
+    }
   }
   // drain any DMA still in flight before the workgroup retires its LDS
   wait_vmcnt<0>();
 }
 
+// Sums the partial tiles of every split tail task in k order (deterministic)
+// and runs the epilogue.  One workgroup per (XCD, tail task); launched with
+// the same grid size as the GEMM so the schedule is recomputed identically.
+template <int BN, int NB, bool FP16>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_fixup(GGArgs args, int gemm_grid) {
+  constexpr int WN = BN / 2;
+  constexpr int NI = WN / 32;
+  constexpr int MI = 2;
+  constexpr int ACC = NB * MI * NI * 16;
+  __shared__ __attribute__((aligned(16))) uint16_t epi_lds[4][32 * 40];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  Sched sc;
+  // blockIdx.x = xcd + nx * tail task index: reuse the XCD / slot fields
+  sc.init(args, BN, gemm_grid, blockIdx.x % (gemm_grid % 8 == 0 ? 8 : 1));
+  const int tt = blockIdx.x / sc.nx;
+  if (tt >= sc.rem) return;
+  const int KT = sc.KT;
+  // segments of tail task tt, in k order
+  int nseg = 0;
+  for (int s = 0; s < sc.S; ++s)
+    if (max(sc.bound(s), tt * KT) < min(sc.bound(s + 1), (tt + 1) * KT)) ++nseg;
+  if (nseg < 2) return; // finished in place by the GEMM kernel
+  const int task = sc.tx0 + sc.full + tt;
+  int b, n0;
+  task_coords(task, args.group_rows, sc.ncol, sc.nblk, BN, b, n0);
+  if (args.block_group[b] < 0) return;
+
+  f32x16 acc[NB][MI][NI];
+  float *flat = reinterpret_cast<float *>(&acc[0][0][0]);
+  bool first = true;
+  for (int s = 0; s < sc.S; ++s) {
+    if (!(max(sc.bound(s), tt * KT) < min(sc.bound(s + 1), (tt + 1) * KT))) continue;
+    const float *pt = partial_tile(args.partials, sc, s, tt - sc.bound(s) / KT, ACC);
+#pragma unroll
+    for (int q = 0; q < ACC / 4; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(pt + ((size_t)q * kThreads + tid) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) flat[4 * q + e] = first ? v[e] : flat[4 * q + e] + v[e];
+    }
+    first = false;
+  }
+  store_tile<BN, NB, FP16, MI, NI>(acc, args.D + (size_t)b * kBM * args.N + n0, args.N,
+                                   (MOE_LDS uint16_t *)epi_lds[wave], lane, wave >> 1, wave & 1);
+}
+
 template <int BN, int NB, bool KN, bool FP16, int NSTAGE>
 static hipError_t launch_one(const GGArgs &a, int grid, hipStream_t stream) {
   grouped_gemm_kernel<BN, NB, KN, FP16, NSTAGE><<<grid, kThreads, 0, stream>>>(a);
+  if (a.partials) grouped_gemm_fixup<BN, NB, FP16><<<grid, kThreads, 0, stream>>>(a, grid);
   return hipGetLastError();
 }
+
+// Tile configurations: BN (columns per matrix), ring depth, super-block rows.
+// The default of each epilogue can be overridden for tuning sweeps with
+// MOE_GG_TILE="<bn>,<stages>,<group rows>[,<split>]" (e.g. "128,3,4,0").
+struct TileCfg {
+  int bn, stages, group, split;
+};
+
+// instantiated (BN, stages) per B-matrix count; LDS: ring + 4 KiB index
+// tables + 10 KiB epilogue tiles <= 160 KiB
+static bool tile_supported(int nb, int bn, int stages) {
+  if (stages < 2 || stages > 4) return false;
+  if (bn == 64) return true;
+  if (bn == 128) return nb == 1 || stages <= 3;
+  if (bn == 256) return nb == 1 && stages <= 3;
+  return false;
+}
+
+static TileCfg tile_config(int epilogue, int N) {
+  TileCfg c = epilogue == 1 ? TileCfg{N % 128 == 0 ? 128 : 64, N % 128 == 0 ? 3 : 4, 1, 1}
+                            : TileCfg{N % 256 == 0 ? 256 : (N % 128 == 0 ? 128 : 64),
+                                      N % 256 == 0 ? 3 : 4, 1, 1};
+  if (const char *env = getenv("MOE_GG_TILE")) {
+    TileCfg e{0, 0, 0, 1};
+    const int n = sscanf(env, "%d,%d,%d,%d", &e.bn, &e.stages, &e.group, &e.split);
+    if (n >= 3 && e.group >= 1 && N % e.bn == 0 &&
+        tile_supported(epilogue == 1 ? 2 : 1, e.bn, e.stages))
+      c = e;
+  }
+  return c;
+}
+
+template <int NB, bool KN, bool FP16>
+static hipError_t launch_bn(const GGArgs &a, const TileCfg &c, int grid, hipStream_t s) {
+#define MOE_GG_CASE(BNV, NSV)                                                                 \
+  if (c.bn == BNV && c.stages == NSV) return launch_one<BNV, NB, KN, FP16, NSV>(a, grid, s);
+  MOE_GG_CASE(64, 2) MOE_GG_CASE(64, 3) MOE_GG_CASE(64, 4)
+  MOE_GG_CASE(128, 2) MOE_GG_CASE(128, 3)
+  if constexpr (NB == 1) {
+    MOE_GG_CASE(128, 4)
+    MOE_GG_CASE(256, 2) MOE_GG_CASE(256, 3)
+  }
+#undef MOE_GG_CASE
+  return hipErrorInvalidValue;
+}
+
+// Workspace for the split tail: two fp32 partial tiles per workgroup of the
+// largest tile shape (128 accumulator floats per thread).
+size_t gg_workspace_bytes(int grid) { return (size_t)grid * 2 * 128 * kThreads * sizeof(float); }
 
 // dtype 0 bf16 / 1 fp16; layout 0 KN / 1 NK; epilogue 0 STORE / 1 SILU_MUL
 hipError_t launch_grouped_gemm(int dtype, int N, int K, int cap, const uint16_t *A,
                                const int32_t *a_src_row, int a_src_div, const uint16_t *B,
                                const uint16_t *B2, int layout, const int32_t *block_group,
-                               const int32_t *num_rows, int epilogue, uint16_t *D, int num_cus,
-                               hipStream_t stream) {
-  GGArgs a{A, a_src_row, a_src_div, B, B2, block_group, num_rows, D, N, K, cap};
+                               const int32_t *num_rows, int epilogue, uint16_t *D, void *ws,
+                               size_t ws_bytes, int num_cus, hipStream_t stream) {
+  const TileCfg c = tile_config(epilogue, N);
   const int grid = num_cus; // one workgroup per CU (LDS-limited)
+  float *partials = (c.split && ws && ws_bytes >= gg_workspace_bytes(grid)) ? (float *)ws : nullptr;
+  GGArgs a{A, a_src_row, a_src_div, B, B2, block_group, num_rows, D, N, K, cap, c.group, partials};
   const bool fp16 = dtype == 1;
   const bool kn = layout == 0;
   if (epilogue == 1) {
-    // gate + up, 64 columns each
-    if (kn && !fp16) return launch_one<64, 2, true, false, 4>(a, grid, stream);
-    if (kn && fp16) return launch_one<64, 2, true, true, 4>(a, grid, stream);
-    if (!kn && !fp16) return launch_one<64, 2, false, false, 4>(a, grid, stream);
-    return launch_one<64, 2, false, true, 4>(a, grid, stream);
+    if (kn && !fp16) return launch_bn<2, true, false>(a, c, grid, stream);
+    if (kn && fp16) return launch_bn<2, true, true>(a, c, grid, stream);
+    if (!kn && !fp16) return launch_bn<2, false, false>(a, c, grid, stream);
+    return launch_bn<2, false, true>(a, c, grid, stream);
   }
-  if (N % 128 == 0) {
-    if (kn && !fp16) return launch_one<128, 1, true, false, 4>(a, grid, stream);
-    if (kn && fp16) return launch_one<128, 1, true, true, 4>(a, grid, stream);
-    if (!kn && !fp16) return launch_one<128, 1, false, false, 4>(a, grid, stream);
-    return launch_one<128, 1, false, true, 4>(a, grid, stream);
-  }
-  if (kn && !fp16) return launch_one<64, 1, true, false, 4>(a, grid, stream);
-  if (kn && fp16) return launch_one<64, 1, true, true, 4>(a, grid, stream);
-  if (!kn && !fp16) return launch_one<64, 1, false, false, 4>(a, grid, stream);
-  return launch_one<64, 1, false, true, 4>(a, grid, stream);
+  if (kn && !fp16) return launch_bn<1, true, false>(a, c, grid, stream);
+  if (kn && fp16) return launch_bn<1, true, true>(a, c, grid, stream);
+  if (!kn && !fp16) return launch_bn<1, false, false>(a, c, grid, stream);
+  return launch_bn<1, false, true>(a, c, grid, stream);
 }
 
 } // namespace moe

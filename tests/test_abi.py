@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in ["moe_route", "moe_permute", "grouped_gemm", "moe_combine", "moe_layer"]:
         assert n in names
     for n in names:
@@ -99,8 +99,8 @@ def test_permute_validation(lib):
 
 def test_grouped_gemm_validation(lib):
     def call(dtype=0, N=128, K=128, cap=256, A=FAKE, src=NULL, div=1, B=FAKE, B2=NULL, lay=0,
-             bg=FAKE, nr=FAKE, epi=0, D=FAKE):
-        return lib.grouped_gemm(dtype, N, K, cap, A, src, div, B, B2, lay, bg, nr, epi, D, NULL)
+             bg=FAKE, nr=FAKE, epi=0, D=FAKE, ws=NULL):
+        return lib.grouped_gemm(dtype, N, K, cap, A, src, div, B, B2, lay, bg, nr, epi, D, ws, 0, NULL)
     assert call(A=NULL) == moe.MOE_ERR_INVALID
     assert call(A=MISALIGNED) == moe.MOE_ERR_INVALID
     assert call(N=96) == moe.MOE_ERR_UNSUPPORTED
@@ -111,6 +111,8 @@ def test_grouped_gemm_validation(lib):
     assert call(epi=1) == moe.MOE_ERR_INVALID          # SiLU*up needs B2
     assert call(epi=7) == moe.MOE_ERR_UNSUPPORTED
     assert call(src=FAKE, div=0) == moe.MOE_ERR_INVALID
+    assert call(ws=MISALIGNED) == moe.MOE_ERR_INVALID
+    assert lib.grouped_gemm_workspace_size() > 0
 
 
 def test_combine_and_layer_validation(lib):

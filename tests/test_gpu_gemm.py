@@ -131,3 +131,90 @@ def test_dense_fp16_degenerate_case_sampled():
     assert_close(got, ref, "dense sampled")
     lib = (A.float() @ B.float().T)
     assert_close(to_f64(D), lib.double().cpu().numpy(), "dense vs library")
+
+
+TILES = [("store", "64,2,1"), ("store", "64,3,2"), ("store", "128,2,3"), ("store", "128,3,4"),
+         ("store", "128,4,1"), ("store", "256,2,4"), ("store", "256,3,2"),
+         ("silu_mul", "64,2,2"), ("silu_mul", "64,3,1"), ("silu_mul", "64,4,4"),
+         ("silu_mul", "128,2,4"), ("silu_mul", "128,3,3")]
+
+
+@pytest.mark.parametrize("epi,tile", TILES, ids=["%s-%s" % t for t in TILES])
+def test_tile_configurations_integer_exact(epi, tile, monkeypatch):
+    # every instantiated tile shape / ring depth / task order gives the exact result
+    monkeypatch.setenv("MOE_GG_TILE", tile)
+    G, N = 4, 512
+    cap = 11 * 128
+    bg = _groups(cap // 128, G, 17)
+    for K in (128, 320):
+        A = syn.ternary_bits((cap, K), 8)
+        B = syn.ternary_bits((G, K, N), 9)
+        B2 = syn.ternary_bits((G, K, N), 10) if epi == "silu_mul" else None
+        m_rows = 9 * 128
+        say("gemm tile", epi, tile, "K", K)
+        D = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16", B2_bits=B2, epi=epi)
+        ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, B2_bits=B2, epilogue=epi,
+                                  rows=np.arange(m_rows, dtype=np.int32))
+        got = to_f64(D)
+        if epi == "store":
+            assert np.array_equal(got[:m_rows], ref)
+        else:
+            assert_close(got[:m_rows], ref, "tile " + tile, max_frac=8e-3, rel_fro=4e-3)
+        assert np.all(np.isnan(got[m_rows:]))
+
+
+@pytest.mark.parametrize("epi,tile,K", [("store", "256,3,1", 320), ("store", "128,4,2", 128),
+                                        ("store", "64,3,4", 576), ("silu_mul", "128,3,1", 320),
+                                        ("silu_mul", "64,4,2", 192)])
+def test_split_tail_matches_whole_tasks(epi, tile, K, monkeypatch):
+    # a task count that leaves a partly filled last round on every XCD, so the
+    # tail is split along K (several segments per task) and finished by the
+    # fixup kernel; integer-exact inputs make both paths bit-identical
+    G, N = 5, 512
+    bn = int(tile.split(",")[0])
+    ncol = N // bn
+    nblk = (8 * 42 + ncol - 1) // ncol          # ~42 tasks per XCD: 32 whole + 10 split
+    cap = (nblk + 1) * 128
+    bg = _groups(cap // 128, G, 23)
+    A = syn.ternary_bits((cap, K), 11)
+    B = syn.ternary_bits((G, K, N), 12)
+    B2 = syn.ternary_bits((G, K, N), 13) if epi == "silu_mul" else None
+    m_rows = nblk * 128
+    say("gemm split tail", epi, tile, "K", K, "blocks", nblk)
+    monkeypatch.setenv("MOE_GG_TILE", tile + ",1")
+    D1 = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16", B2_bits=B2, epi=epi)
+    monkeypatch.setenv("MOE_GG_TILE", tile + ",0")
+    D0 = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16", B2_bits=B2, epi=epi)
+    assert torch.equal(D1[:m_rows].view(torch.int16), D0[:m_rows].view(torch.int16))
+    rows = np.random.default_rng(0).choice(m_rows, 64, replace=False).astype(np.int32)
+    ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, B2_bits=B2, epilogue=epi, rows=rows)
+    got = to_f64(D1)[rows]
+    if epi == "store":
+        assert np.array_equal(got, ref)
+    else:
+        assert_close(got, ref, "split " + tile, max_frac=8e-3, rel_fro=4e-3)
+    assert np.all(np.isnan(to_f64(D1)[m_rows:]))
+
+
+def test_split_tail_random_values_and_repeatability(monkeypatch):
+    # random bf16 values: split and whole paths agree to fp32 summation order,
+    # and the split path is bitwise repeatable
+    G, N, K = 4, 1024, 704
+    nblk = 8 * 40 // 4
+    cap = nblk * 128
+    bg = _groups(nblk, G, 31)
+    g = np.random.default_rng(3)
+    A = syn.bf16_bits(g.standard_normal((cap, K)).astype(np.float32))
+    B = syn.bf16_bits((g.standard_normal((G, K, N)) / np.sqrt(K)).astype(np.float32))
+    say("gemm split random")
+    monkeypatch.setenv("MOE_GG_TILE", "256,3,1,1")
+    D1 = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=cap, dtype="bf16")
+    D1b = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=cap, dtype="bf16")
+    monkeypatch.setenv("MOE_GG_TILE", "256,3,1,0")
+    D0 = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=cap, dtype="bf16")
+    assert torch.equal(D1.view(torch.int16), D1b.view(torch.int16))
+    diff = (D1.float() - D0.float()).abs().max().item()
+    assert diff <= 2 ** -6 * D0.float().abs().max().item()
+    rows = g.choice(cap, 48, replace=False).astype(np.int32)
+    ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, rows=rows)
+    assert_close(to_f64(D1)[rows], ref, "split random")
