@@ -76,14 +76,17 @@ template <int BN> __device__ __forceinline__ int swz_kn(int k) {
 // Direct global->LDS DMA.  Issued through inline asm so that the compiler
 // neither tracks these loads nor inserts its own (conservative) waits for
 // them: lane i of the wavefront writes bytes [16 i, 16 i + 16) (or [4 i, 4 i
-// + 4) for the dword form) after the wave-uniform LDS byte address in M0.
-// Completion is awaited explicitly with wait_vmcnt.
+// + 4) for the dword form) after the wave-uniform LDS byte address in M0
+// (one wait state between the M0 write and its use).  Completion is awaited
+// explicitly with wait_vmcnt.
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+               "s"(lds_addr)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void *g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr)
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g),
+               "s"(lds_addr)
                : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
@@ -353,18 +356,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   };
 
   int n_issued = 0;
-  auto issue_next = [&]() {
-    if (it_i >= n_items) return;
+  // DMA instruction q (0 <= q < LOADS) of the slice being issued: A first,
+  // then each B matrix.
+  auto issue_dma = [&](int q) {
     const uint32_t stage = smem_addr + (n_issued % NSTAGE) * STAGE_BYTES;
-    const size_t a_off = (size_t)it_k * kBK * 2;
-#pragma unroll
-    for (int i = 0; i < A_INSTR; ++i) dma16(a_src[i] + a_off, stage + (wave * A_INSTR + i) * 1024);
-    const size_t b_off = KN ? (size_t)it_k * kBK * N * 2 : (size_t)it_k * kBK * 2;
-#pragma unroll
-    for (int m = 0; m < NB; ++m)
-#pragma unroll
-      for (int i = 0; i < B_INSTR; ++i)
-        dma16(b_src[m][i] + b_off, stage + A_BYTES + m * B_BYTES + (wave * B_INSTR + i) * 1024);
+    if (q < A_INSTR) {
+      dma16(a_src[q] + (size_t)it_k * kBK * 2, stage + (wave * A_INSTR + q) * 1024);
+    } else {
+      const int m = (q - A_INSTR) / B_INSTR;
+      const int i = (q - A_INSTR) - m * B_INSTR;
+      const size_t b_off = KN ? (size_t)it_k * kBK * N * 2 : (size_t)it_k * kBK * 2;
+      dma16(b_src[m][i] + b_off,
+            stage + A_BYTES + m * B_BYTES + (wave * B_INSTR + i) * 1024);
+    }
+  };
+  // bookkeeping once every instruction of the slice is out
+  auto issue_done = [&]() {
     ++n_issued;
     if (++it_k == it_kb) {
       ++it_i;
@@ -376,6 +383,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
         begin_issue_item(it_i);
       }
     }
+  };
+  auto issue_next = [&]() {
+    if (it_i >= n_items) return;
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) issue_dma(q);
+    issue_done();
   };
 
   if (n_items > 0) {
@@ -413,13 +426,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
       // stage the next issue overwrites
       block_barrier();
       if (kt == ka) group = __builtin_amdgcn_readfirstlane(my_idx[i % IDX_SLOTS][32]);
-      issue_next();
+      // the next slice's DMA is spread over the k steps of this one, so the
+      // address unit drains it in the background of the MFMAs
+      const bool issuing = it_i < n_items;
+      constexpr int PER = (LOADS + 3) / 4;
 
       const MOE_LDS unsigned char *sA =
           (const MOE_LDS unsigned char *)(smem + (n_consumed % NSTAGE) * STAGE_BYTES);
-#pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        i16x4 a[MI][2];
+      // Fragments of one 16-deep k step, double-buffered in registers: the
+      // LDS reads of step kk+1 are issued before the MFMAs of step kk, so
+      // their latency hides behind matrix work (one wavefront per SIMD
+      // leaves nothing else to hide it).
+      i16x4 fa[2][MI][2];
+      i16x4 fb[2][NB][NI][2];
+      auto load_frags = [&](int kk, i16x4 (&a)[MI][2], i16x4 (&b)[NB][NI][2]) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
           const int row = wm * 64 + mi * 32 + (lane & 31);
@@ -433,7 +453,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
           const MOE_LDS unsigned char *sB = sA + A_BYTES + m * B_BYTES;
 #pragma unroll
           for (int j = 0; j < NI; ++j) {
-            i16x4 b0, b1;
             if constexpr (KN) {
               // lane group G = lane/16 reads columns n0 + 16*(G&1) .. +16 at
               // k = 8*(G>>1) + 4*r + (lane%16)/4; each lane points at 4
@@ -445,21 +464,39 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
               const int k1 = k0 + 4;
               const int o0 = k0 * (BN * 2) + (((n >> 3) ^ swz_kn<BN>(k0)) << 4) + ((n & 7) << 1);
               const int o1 = k1 * (BN * 2) + (((n >> 3) ^ swz_kn<BN>(k1)) << 4) + ((n & 7) << 1);
-              b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4 *)(sB + o0));
-              b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4 *)(sB + o1));
+              b[m][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4 *)(sB + o0));
+              b[m][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4 *)(sB + o1));
             } else {
               const int n = wn * WN + j * 32 + (lane & 31);
               const int c = (kk * 2 + (lane >> 5)) ^ swz128(n);
               const u32x4 v = *(const MOE_LDS u32x4 *)(sB + n * 128 + c * 16);
-              b0 = __builtin_bit_cast(i16x4, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
-              b1 = __builtin_bit_cast(i16x4, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
+              b[m][j][0] = __builtin_bit_cast(i16x4, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
+              b[m][j][1] = __builtin_bit_cast(i16x4, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
             }
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-              acc[m][mi][j] = mfma32<FP16>(a[mi][0], a[mi][1], b0, b1, acc[m][mi][j]);
           }
         }
+      };
+      load_frags(0, fa[0], fb[0]);
+#pragma unroll
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        const int cur = kk & 1;
+        if (kk + 1 < kBK / 16) load_frags(kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+        if (issuing) {
+#pragma unroll
+          for (int q = kk * PER; q < (kk + 1) * PER && q < LOADS; ++q) issue_dma(q);
+        }
+        // keep the next step's reads and this DMA share ahead of the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+              acc[m][mi][j] = mfma32<FP16>(fa[cur][mi][0], fa[cur][mi][1], fb[cur][m][j][0],
+                                           fb[cur][m][j][1], acc[m][mi][j]);
       }
+      if (issuing) issue_done();
       ++n_consumed;
     }
 
@@ -538,9 +575,13 @@ static hipError_t launch_one(const GGArgs &a, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile configurations: BN (columns per matrix), ring depth, super-block rows.
-// The default of each epilogue can be overridden for tuning sweeps with
-// MOE_GG_TILE="<bn>,<stages>,<group rows>[,<split>]" (e.g. "128,3,4,0").
+// Tile configurations: BN (columns per matrix), ring depth, super-block rows,
+// split tail on/off.  Defaults (measured on the MI355X at the shapes of the
+// MoE layer share): gate/up 128 gate + 128 up columns with a 3-deep ring,
+// down / dense 256 columns with a 3-deep ring; the split tail is off (its
+// fp32 partial-tile round trip cost more than the balance it bought).  Each
+// can be overridden for tuning sweeps with
+// MOE_GG_TILE="<bn>,<stages>,<group rows>[,<split>]" (e.g. "128,3,4,1").
 struct TileCfg {
   int bn, stages, group, split;
 };
@@ -556,11 +597,11 @@ static bool tile_supported(int nb, int bn, int stages) {
 }
 
 static TileCfg tile_config(int epilogue, int N) {
-  TileCfg c = epilogue == 1 ? TileCfg{N % 128 == 0 ? 128 : 64, N % 128 == 0 ? 3 : 4, 1, 1}
+  TileCfg c = epilogue == 1 ? TileCfg{N % 128 == 0 ? 128 : 64, N % 128 == 0 ? 3 : 4, 1, 0}
                             : TileCfg{N % 256 == 0 ? 256 : (N % 128 == 0 ? 128 : 64),
-                                      N % 256 == 0 ? 3 : 4, 1, 1};
+                                      N % 256 == 0 ? 3 : 4, 1, 0};
   if (const char *env = getenv("MOE_GG_TILE")) {
-    TileCfg e{0, 0, 0, 1};
+    TileCfg e{0, 0, 0, 0};
     const int n = sscanf(env, "%d,%d,%d,%d", &e.bn, &e.stages, &e.group, &e.split);
     if (n >= 3 && e.group >= 1 && N % e.bn == 0 &&
         tile_supported(epilogue == 1 ? 2 : 1, e.bn, e.stages))
