@@ -42,7 +42,21 @@ namespace moe {
 
 constexpr int kBM = 128;
 constexpr int kBK = 64;
-constexpr int kThreads = 256;
+
+// Wavefront layout of a workgroup: WAVES = 4 (one per SIMD, a 2 x 2 grid of
+// 64 x BN/2 wave tiles) or 8 (two per SIMD, so one wavefront's LDS and DMA
+// waits hide behind the other's MFMAs: a 2 x 4 grid of 64 x BN/4 wave tiles,
+// or 4 x 2 of 32 x BN/2 when BN = 64).
+template <int BN, int WAVES> struct WaveGrid {
+  static constexpr int kThreads = 64 * WAVES;
+  static constexpr int WMR = WAVES == 4 ? 2 : (BN >= 128 ? 2 : 4); // wave rows
+  static constexpr int WNC = WAVES / WMR;                          // wave columns
+  static constexpr int WR = kBM / WMR;                             // rows per wave
+  static constexpr int WC = BN / WNC;                              // columns per wave (per matrix)
+  static constexpr int MI = WR / 32;
+  static constexpr int NI = WC / 32;
+  static_assert(WC >= 32 && WR >= 32, "wave tile");
+};
 
 struct GGArgs {
   const uint16_t *A;
@@ -178,44 +192,45 @@ struct Sched {
 };
 
 // Partial tile of one tail segment: ACC floats per thread, stored as
-// [ACC/4][256 threads][4] so each store and load is one coalesced 16-byte
-// access per lane.  Buffer (xcd, slot, j) holds the j-th tail segment
-// (j < 2) of that workgroup.
+// [ACC/4][threads][4] so each store and load is one coalesced 16-byte access
+// per lane.  Buffer (xcd, slot, j) holds the j-th tail segment (j < 2) of
+// that workgroup.
 __device__ __forceinline__ float *partial_tile(float *base, const Sched &sc, int s, int j,
-                                               int acc_per_thread) {
-  return base + ((size_t)(sc.xcd * sc.S + s) * 2 + j) * (size_t)acc_per_thread * kThreads;
+                                               int acc_per_thread, int threads) {
+  return base + ((size_t)(sc.xcd * sc.S + s) * 2 + j) * (size_t)acc_per_thread * threads;
 }
 
-// Epilogue of one 128 x BN output tile: every 32x32 accumulator tile goes
-// through a per-wavefront LDS tile so that each lane writes 16-byte row
-// pieces (the MFMA layout gives each lane one column of 4-row groups).
-template <int BN, int NB, bool FP16, int MI, int NI>
+// Epilogue of one 128 x BN output tile: every 32x32 accumulator tile goes,
+// 16 rows at a time, through a per-wavefront LDS tile so that each lane
+// writes one 16-byte row piece (the MFMA layout gives each lane one column
+// of 4-row groups; registers 0-7 hold rows 0-15, registers 8-15 rows 16-31).
+constexpr int kEpiLd = 40; // row pitch (elements) of the staging tile
+template <int NB, bool FP16, int MI, int NI>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint16_t *Dt, int N,
-                                           MOE_LDS uint16_t *stg, int lane, int wm, int wn) {
-  constexpr int WN = BN / 2;
-  constexpr int EPI_LD = 40;
+                                           MOE_LDS uint16_t *stg, int lane, int row0,
+                                           int col0) {
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
+    for (int j = 0; j < NI; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        float v = acc[0][i][j][r];
-        if constexpr (NB == 2) {
-          const float u = acc[1][i][j][r];
-          v = v / (1.0f + __expf(-v)) * u;
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int r = 8 * h; r < 8 * h + 8; ++r) {
+          const int row = 8 * ((r >> 2) & 1) + 4 * (lane >> 5) + (r & 3);
+          float v = acc[0][i][j][r];
+          if constexpr (NB == 2) {
+            const float u = acc[1][i][j][r];
+            v = v / (1.0f + __expf(-v)) * u;
+          }
+          stg[row * kEpiLd + (lane & 31)] = FP16 ? f32_to_f16(v) : f32_to_bf16(v);
         }
-        stg[row * EPI_LD + (lane & 31)] = FP16 ? f32_to_f16(v) : f32_to_bf16(v);
+        const int row = lane >> 2;
+        const int col = (lane & 3) * 8;
+        const u32x4 q = *(const MOE_LDS u32x4 *)(stg + row * kEpiLd + col);
+        uint16_t *dst = Dt + (size_t)(row0 + i * 32 + 16 * h + row) * N + col0 + j * 32 + col;
+        *reinterpret_cast<u32x4 *>(dst) = q;
       }
-      const int row = lane >> 1;
-      const int col = (lane & 1) * 16;
-      const u32x4 q0 = *(const MOE_LDS u32x4 *)(stg + row * EPI_LD + col);
-      const u32x4 q1 = *(const MOE_LDS u32x4 *)(stg + row * EPI_LD + col + 8);
-      uint16_t *dst = Dt + (size_t)(wm * 64 + i * 32 + row) * N + wn * WN + j * 32 + col;
-      *reinterpret_cast<u32x4 *>(dst) = q0;
-      *reinterpret_cast<u32x4 *>(dst + 8) = q1;
-    }
 }
 
 // Task order inside the whole-task phase: super-blocks of `group_rows` row
@@ -235,33 +250,36 @@ __device__ __forceinline__ void task_coords(int task, int GR, int ncol, int nblk
 }
 
 // BN: output columns per task (per B matrix); NB: 1 (STORE) or 2 (gate+up);
-// KN: B stored [K][N] (else [N][K]); NSTAGE: LDS ring depth.
-template <int BN, int NB, bool KN, bool FP16, int NSTAGE>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) {
+// KN: B stored [K][N] (else [N][K]); NSTAGE: LDS ring depth; WAVES: 4 or 8.
+template <int BN, int NB, bool KN, bool FP16, int NSTAGE, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void grouped_gemm_kernel(GGArgs args) {
+  using WG = WaveGrid<BN, WAVES>;
+  constexpr int NT = WG::kThreads;
   constexpr int A_BYTES = kBM * kBK * 2;
   constexpr int B_BYTES = kBK * BN * 2;
   constexpr int STAGE_BYTES = A_BYTES + NB * B_BYTES;
-  constexpr int WN = BN / 2;       // columns per wavefront per matrix
-  constexpr int NI = WN / 32;      // 32-wide MFMA tiles per wavefront per matrix
-  constexpr int MI = 2;            // 32-high MFMA tiles per wavefront
-  constexpr int A_INSTR = 4;       // DMA instructions per wavefront per A slice
-  constexpr int B_INSTR = BN / 32; // per wavefront per B matrix per slice
+  constexpr int MI = WG::MI;       // 32-high MFMA tiles per wavefront
+  constexpr int NI = WG::NI;       // 32-wide MFMA tiles per wavefront per matrix
+  constexpr int A_INSTR = 16 / WAVES;         // DMA instructions per wavefront per A slice
+  constexpr int B_INSTR = BN / (8 * WAVES);   // per wavefront per B matrix per slice
   constexpr int LOADS = A_INSTR + NB * B_INSTR; // DMA ops per wavefront per slice
+  constexpr int ROWS_PW = 8 * A_INSTR;        // A rows each wavefront loads
   constexpr int IDX_SLOTS = 4;     // per-wavefront ring of task index tables
-  constexpr int IDX_WORDS = 64;    // words per table: 32 source rows, then the group
+  constexpr int IDX_WORDS = 40;    // words per table: source rows, the group at word 32
   constexpr int ACC = NB * MI * NI * 16; // accumulator floats per thread
+  static_assert(B_INSTR >= 1 && ROWS_PW <= 32, "DMA split");
   static_assert(LOADS * (NSTAGE - 2) < 64, "vmcnt range");
   static_assert(NSTAGE >= 2 && NSTAGE <= IDX_SLOTS, "ring depth");
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE_BYTES];
-  __shared__ __attribute__((aligned(256))) int32_t idx_lds[4][IDX_SLOTS][IDX_WORDS];
-  __shared__ __attribute__((aligned(16))) uint16_t epi_lds[4][32 * 40];
+  __shared__ __attribute__((aligned(16))) int32_t idx_lds[WAVES][IDX_SLOTS][IDX_WORDS];
+  __shared__ __attribute__((aligned(16))) uint16_t epi_lds[WAVES][16 * kEpiLd];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / WG::WNC;
+  const int wn = wave % WG::WNC;
   const int N = args.N, K = args.K;
 
   Sched sc;
@@ -282,8 +300,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
     coords(task, b, n0);
     const uint32_t dst = (uint32_t)(uintptr_t)&my_idx[seq % IDX_SLOTS][0];
     if (args.a_src_row) {
-      if (lane < 32)
-        dma4(args.a_src_row + (size_t)b * kBM + wave * 32 + lane, dst);
+      if (lane < ROWS_PW)
+        dma4(args.a_src_row + (size_t)b * kBM + wave * ROWS_PW + lane, dst);
       else if (lane == 32)
         dma4(args.block_group + b, dst); // lane 32 lands at word 32
     } else if (lane == 32) {
@@ -308,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
     const int g = tab[32];
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i) {
-      // instruction i covers tile rows (wave*4+i)*8 .. +8, lane row lane/8
+      // instruction i covers tile rows (wave*A_INSTR+i)*8 .. +8, lane row lane/8
       const int row = (wave * A_INSTR + i) * 8 + (lane >> 3);
       int src = b * kBM + row;
       if (args.a_src_row) {
@@ -442,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
       auto load_frags = [&](int kk, i16x4 (&a)[MI][2], i16x4 (&b)[NB][NI][2]) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
-          const int row = wm * 64 + mi * 32 + (lane & 31);
+          const int row = wm * WG::WR + mi * 32 + (lane & 31);
           const int c = (kk * 2 + (lane >> 5)) ^ swz128(row);
           const u32x4 v = *(const MOE_LDS u32x4 *)(sA + row * 128 + c * 16);
           a[mi][0] = __builtin_bit_cast(i16x4, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
@@ -459,7 +477,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
               // consecutive columns, the transpose read returns 4 k of one column
               const int G = lane >> 4;
               const int q = lane & 15;
-              const int n = wn * WN + j * 32 + 16 * (G & 1) + 4 * (q & 3);
+              const int n = wn * WG::WC + j * 32 + 16 * (G & 1) + 4 * (q & 3);
               const int k0 = kk * 16 + 8 * (G >> 1) + (q >> 2);
               const int k1 = k0 + 4;
               const int o0 = k0 * (BN * 2) + (((n >> 3) ^ swz_kn<BN>(k0)) << 4) + ((n & 7) << 1);
@@ -467,7 +485,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
               b[m][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4 *)(sB + o0));
               b[m][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4 *)(sB + o1));
             } else {
-              const int n = wn * WN + j * 32 + (lane & 31);
+              const int n = wn * WG::WC + j * 32 + (lane & 31);
               const int c = (kk * 2 + (lane >> 5)) ^ swz128(n);
               const u32x4 v = *(const MOE_LDS u32x4 *)(sB + n * 128 + c * 16);
               b[m][j][0] = __builtin_bit_cast(i16x4, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
@@ -504,16 +522,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
     if (ka == 0 && kb == KT) {
       int b, n0;
       coords(task, b, n0);
-      store_tile<BN, NB, FP16, MI, NI>(acc, args.D + (size_t)b * kBM * N + n0, N,
-                                       (MOE_LDS uint16_t *)epi_lds[wave], lane, wm, wn);
+      store_tile<NB, FP16, MI, NI>(acc, args.D + (size_t)b * kBM * N + n0, N,
+                                   (MOE_LDS uint16_t *)epi_lds[wave], lane, wm * WG::WR,
+                                   wn * WG::WC);
     } else {
       // a piece of a split tail task: store the fp32 partial tile
-      float *pt = partial_tile(args.partials, sc, sc.slot, tt - sc.bound(sc.slot) / KT, ACC);
+      float *pt = partial_tile(args.partials, sc, sc.slot, tt - sc.bound(sc.slot) / KT, ACC, NT);
       const float *flat = reinterpret_cast<const float *>(&acc[0][0][0]);
 #pragma unroll
       for (int q = 0; q < ACC / 4; ++q) {
         f32x4 v = {flat[4 * q], flat[4 * q + 1], flat[4 * q + 2], flat[4 * q + 3]};
-        *reinterpret_cast<f32x4 *>(pt + ((size_t)q * kThreads + tid) * 4) = v;
+        *reinterpret_cast<f32x4 *>(pt + ((size_t)q * NT + tid) * 4) = v;
       }
     }
   }
@@ -524,13 +543,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
 // Sums the partial tiles of every split tail task in k order (deterministic)
 // and runs the epilogue.  One workgroup per (XCD, tail task); launched with
 // the same grid size as the GEMM so the schedule is recomputed identically.
-template <int BN, int NB, bool FP16>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_fixup(GGArgs args, int gemm_grid) {
-  constexpr int WN = BN / 2;
-  constexpr int NI = WN / 32;
-  constexpr int MI = 2;
+template <int BN, int NB, bool FP16, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void grouped_gemm_fixup(GGArgs args, int gemm_grid) {
+  using WG = WaveGrid<BN, WAVES>;
+  constexpr int NT = WG::kThreads;
+  constexpr int MI = WG::MI;
+  constexpr int NI = WG::NI;
   constexpr int ACC = NB * MI * NI * 16;
-  __shared__ __attribute__((aligned(16))) uint16_t epi_lds[4][32 * 40];
+  __shared__ __attribute__((aligned(16))) uint16_t epi_lds[WAVES][16 * kEpiLd];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -555,23 +575,25 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fixup(GGArgs args, int 
   bool first = true;
   for (int s = 0; s < sc.S; ++s) {
     if (!(max(sc.bound(s), tt * KT) < min(sc.bound(s + 1), (tt + 1) * KT))) continue;
-    const float *pt = partial_tile(args.partials, sc, s, tt - sc.bound(s) / KT, ACC);
+    const float *pt = partial_tile(args.partials, sc, s, tt - sc.bound(s) / KT, ACC, NT);
 #pragma unroll
     for (int q = 0; q < ACC / 4; ++q) {
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(pt + ((size_t)q * kThreads + tid) * 4);
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(pt + ((size_t)q * NT + tid) * 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) flat[4 * q + e] = first ? v[e] : flat[4 * q + e] + v[e];
     }
     first = false;
   }
-  store_tile<BN, NB, FP16, MI, NI>(acc, args.D + (size_t)b * kBM * args.N + n0, args.N,
-                                   (MOE_LDS uint16_t *)epi_lds[wave], lane, wave >> 1, wave & 1);
+  store_tile<NB, FP16, MI, NI>(acc, args.D + (size_t)b * kBM * args.N + n0, args.N,
+                               (MOE_LDS uint16_t *)epi_lds[wave], lane, (wave / WG::WNC) * WG::WR,
+                               (wave % WG::WNC) * WG::WC);
 }
 
-template <int BN, int NB, bool KN, bool FP16, int NSTAGE>
+template <int BN, int NB, bool KN, bool FP16, int NSTAGE, int WAVES>
 static hipError_t launch_one(const GGArgs &a, int grid, hipStream_t stream) {
-  grouped_gemm_kernel<BN, NB, KN, FP16, NSTAGE><<<grid, kThreads, 0, stream>>>(a);
-  if (a.partials) grouped_gemm_fixup<BN, NB, FP16><<<grid, kThreads, 0, stream>>>(a, grid);
+  grouped_gemm_kernel<BN, NB, KN, FP16, NSTAGE, WAVES><<<grid, 64 * WAVES, 0, stream>>>(a);
+  if (a.partials)
+    grouped_gemm_fixup<BN, NB, FP16, WAVES><<<grid, 64 * WAVES, 0, stream>>>(a, grid);
   return hipGetLastError();
 }
 
@@ -583,7 +605,7 @@ static hipError_t launch_one(const GGArgs &a, int grid, hipStream_t stream) {
 // can be overridden for tuning sweeps with
 // MOE_GG_TILE="<bn>,<stages>,<group rows>[,<split>]" (e.g. "128,3,4,1").
 struct TileCfg {
-  int bn, stages, group, split;
+  int bn, stages, group, split, waves;
 };
 
 // instantiated (BN, stages) per B-matrix count; LDS: ring + 4 KiB index
@@ -597,13 +619,14 @@ static bool tile_supported(int nb, int bn, int stages) {
 }
 
 static TileCfg tile_config(int epilogue, int N) {
-  TileCfg c = epilogue == 1 ? TileCfg{N % 128 == 0 ? 128 : 64, N % 128 == 0 ? 3 : 4, 1, 0}
+  TileCfg c = epilogue == 1 ? TileCfg{N % 128 == 0 ? 128 : 64, N % 128 == 0 ? 3 : 4, 1, 0, 4}
                             : TileCfg{N % 256 == 0 ? 256 : (N % 128 == 0 ? 128 : 64),
-                                      N % 256 == 0 ? 3 : 4, 1, 0};
+                                      N % 256 == 0 ? 3 : 4, 1, 0, 4};
   if (const char *env = getenv("MOE_GG_TILE")) {
-    TileCfg e{0, 0, 0, 0};
-    const int n = sscanf(env, "%d,%d,%d,%d", &e.bn, &e.stages, &e.group, &e.split);
-    if (n >= 3 && e.group >= 1 && N % e.bn == 0 &&
+    TileCfg e{0, 0, 0, 0, 4};
+    const int n =
+        sscanf(env, "%d,%d,%d,%d,%d", &e.bn, &e.stages, &e.group, &e.split, &e.waves);
+    if (n >= 3 && e.group >= 1 && N % e.bn == 0 && (e.waves == 4 || e.waves == 8) &&
         tile_supported(epilogue == 1 ? 2 : 1, e.bn, e.stages))
       c = e;
   }
@@ -613,7 +636,9 @@ static TileCfg tile_config(int epilogue, int N) {
 template <int NB, bool KN, bool FP16>
 static hipError_t launch_bn(const GGArgs &a, const TileCfg &c, int grid, hipStream_t s) {
 #define MOE_GG_CASE(BNV, NSV)                                                                 \
-  if (c.bn == BNV && c.stages == NSV) return launch_one<BNV, NB, KN, FP16, NSV>(a, grid, s);
+  if (c.bn == BNV && c.stages == NSV)                                                         \
+    return c.waves == 8 ? launch_one<BNV, NB, KN, FP16, NSV, 8>(a, grid, s)                   \
+                        : launch_one<BNV, NB, KN, FP16, NSV, 4>(a, grid, s);
   MOE_GG_CASE(64, 2) MOE_GG_CASE(64, 3) MOE_GG_CASE(64, 4)
   MOE_GG_CASE(128, 2) MOE_GG_CASE(128, 3)
   if constexpr (NB == 1) {
@@ -626,7 +651,7 @@ static hipError_t launch_bn(const GGArgs &a, const TileCfg &c, int grid, hipStre
 
 // Workspace for the split tail: two fp32 partial tiles per workgroup of the
 // largest tile shape (128 accumulator floats per thread).
-size_t gg_workspace_bytes(int grid) { return (size_t)grid * 2 * 128 * kThreads * sizeof(float); }
+size_t gg_workspace_bytes(int grid) { return (size_t)grid * 2 * 128 * 256 * sizeof(float); }
 
 // dtype 0 bf16 / 1 fp16; layout 0 KN / 1 NK; epilogue 0 STORE / 1 SILU_MUL
 hipError_t launch_grouped_gemm(int dtype, int N, int K, int cap, const uint16_t *A,

@@ -133,10 +133,14 @@ def test_dense_fp16_degenerate_case_sampled():
     assert_close(to_f64(D), lib.double().cpu().numpy(), "dense vs library")
 
 
+# bn, ring stages, super-block rows[, split tail, wavefronts]
 TILES = [("store", "64,2,1"), ("store", "64,3,2"), ("store", "128,2,3"), ("store", "128,3,4"),
          ("store", "128,4,1"), ("store", "256,2,4"), ("store", "256,3,2"),
          ("silu_mul", "64,2,2"), ("silu_mul", "64,3,1"), ("silu_mul", "64,4,4"),
-         ("silu_mul", "128,2,4"), ("silu_mul", "128,3,3")]
+         ("silu_mul", "128,2,4"), ("silu_mul", "128,3,3"),
+         ("store", "64,3,1,0,8"), ("store", "128,4,2,0,8"), ("store", "256,3,1,0,8"),
+         ("store", "256,3,1,1,8"), ("silu_mul", "64,4,1,0,8"), ("silu_mul", "128,3,1,0,8"),
+         ("silu_mul", "128,3,2,1,8")]
 
 
 @pytest.mark.parametrize("epi,tile", TILES, ids=["%s-%s" % t for t in TILES])
@@ -166,7 +170,8 @@ def test_tile_configurations_integer_exact(epi, tile, monkeypatch):
 @pytest.mark.parametrize("epi,tile,K", [("store", "256,3,1", 320), ("store", "128,4,2", 128),
                                         ("store", "64,3,4", 576), ("silu_mul", "128,3,1", 320),
                                         ("silu_mul", "64,4,2", 192)])
-def test_split_tail_matches_whole_tasks(epi, tile, K, monkeypatch):
+@pytest.mark.parametrize("waves", [4, 8])
+def test_split_tail_matches_whole_tasks(epi, tile, K, waves, monkeypatch):
     # a task count that leaves a partly filled last round on every XCD, so the
     # tail is split along K (several segments per task) and finished by the
     # fixup kernel; integer-exact inputs make both paths bit-identical
@@ -181,9 +186,9 @@ def test_split_tail_matches_whole_tasks(epi, tile, K, monkeypatch):
     B2 = syn.ternary_bits((G, K, N), 13) if epi == "silu_mul" else None
     m_rows = nblk * 128
     say("gemm split tail", epi, tile, "K", K, "blocks", nblk)
-    monkeypatch.setenv("MOE_GG_TILE", tile + ",1")
+    monkeypatch.setenv("MOE_GG_TILE", tile + ",1,%d" % waves)
     D1 = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16", B2_bits=B2, epi=epi)
-    monkeypatch.setenv("MOE_GG_TILE", tile + ",0")
+    monkeypatch.setenv("MOE_GG_TILE", tile + ",0,%d" % waves)
     D0 = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16", B2_bits=B2, epi=epi)
     assert torch.equal(D1[:m_rows].view(torch.int16), D0[:m_rows].view(torch.int16))
     rows = np.random.default_rng(0).choice(m_rows, 64, replace=False).astype(np.int32)
