@@ -54,6 +54,8 @@ def _bind(path):
     lib.oracle_grouped_gemm.restype = None
     lib.oracle_combine.argtypes = [P, I, P, P, I, I, P]
     lib.oracle_combine.restype = None
+    lib.oracle_weighted_scatter.argtypes = [P, I, I, P, P, I, I, P]
+    lib.oracle_weighted_scatter.restype = None
     lib.oracle_moe_tokens.argtypes = [P, P, P, P, P, P, I, I, I, I, P, I, P]
     lib.oracle_moe_tokens.restype = None
     lib.oracle_num_threads.argtypes = []
@@ -209,6 +211,21 @@ def combine(y_bits, pair_to_row, w):
     H = yb.shape[1]
     out = np.empty((T, H), np.float64)
     _load().oracle_combine(yp, H, pp, wp, T, k, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def weighted_scatter(Y, row_to_pair, w, k, T):
+    """out[p // k] += w[p] * Y[r] for every row r with p = row_to_pair[r] >= 0,
+    in double; Y is [M, N] double (rows in permuted order), w is [T*k] fp32."""
+    Ya = np.ascontiguousarray(Y, dtype=np.float64)
+    rp, rpp = _c(row_to_pair, np.int32)
+    wa, wp = _c(np.asarray(w, dtype=np.float32).reshape(-1), np.float32)
+    M, N = Ya.shape
+    if rp.shape[0] < M:
+        raise ValueError("row_to_pair shorter than Y")
+    out = np.empty((T, N), np.float64)
+    _load().oracle_weighted_scatter(Ya.ctypes.data_as(ctypes.c_void_p), M, N, rpp, wp, k, T,
+                                    out.ctypes.data_as(ctypes.c_void_p))
     return out
 
 

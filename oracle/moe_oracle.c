@@ -237,6 +237,27 @@ void oracle_combine(const uint16_t *y, int H, const int32_t *pair_to_row,
 }
 
 /* ------------------------------------------------------------------ */
+/* O6' weighted scatter (the combine folded into the down GEMM's         */
+/* epilogue, part (1), section 4, MoE layer1 row): every real row r of   */
+/* the row-ordered products Y [M][N] (double) adds w[p] * Y[r] into the  */
+/* token row p / k of out [T][N], p = row_to_pair[r]; padding rows       */
+/* (p < 0) add nothing.  Rows are visited in ascending order.            */
+/* ------------------------------------------------------------------ */
+void oracle_weighted_scatter(const double *Y, int M, int N,
+                             const int32_t *row_to_pair, const float *w,
+                             int k, int T, double *out) {
+  for (size_t i = 0; i < (size_t)T * N; ++i) out[i] = 0.0;
+  for (int r = 0; r < M; ++r) {
+    int p = row_to_pair[r];
+    if (p < 0) continue;
+    double wp = (double)w[p];
+    double *o = out + (size_t)(p / k) * N;
+    const double *yr = Y + (size_t)r * N;
+    for (int n = 0; n < N; ++n) o[n] += wp * yr[n];
+  }
+}
+
+/* ------------------------------------------------------------------ */
 /* The whole layer for a list of tokens, by its definition:              */
 /*   out[t] = sum_j w[t][j] * FFN_{idx[t][j]}(x[t])                       */
 /*   FFN_e(z) = (SiLU(z.Wg[e]) * (z.Wu[e])) . Wd[e]                      */

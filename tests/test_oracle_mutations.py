@@ -37,6 +37,10 @@ MUTATIONS = [
     ("bf16_shift", "uint32_t u = ((uint32_t)b) << 16;", "uint32_t u = ((uint32_t)b) << 15;"),
     ("block_expert_off_by_one", "block_expert[r / ROW_BLOCK] = e;",
      "block_expert[r / ROW_BLOCK + 1 < nblk ? r / ROW_BLOCK + 1 : r / ROW_BLOCK] = e;"),
+    ("scatter_wrong_token", "double *o = out + (size_t)(p / k) * N;",
+     "double *o = out + (size_t)(p % T) * N;"),
+    ("scatter_weight_dropped", "for (int n = 0; n < N; ++n) o[n] += wp * yr[n];",
+     "for (int n = 0; n < N; ++n) o[n] += yr[n];"),
 ]
 
 

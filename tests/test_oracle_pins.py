@@ -274,6 +274,42 @@ def pin_combine(O):
     assert np.array_equal(oh, yf[P["pair_to_row"].reshape(T, k)[:, 1]])
 
 
+def pin_weighted_scatter(O):
+    rng = np.random.default_rng(12)
+    T, k, E, N = 50, 3, 7, 24
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    idx, w = O.route(lg, k)
+    P = O.permute(idx, E)
+    r2p = P["row_to_pair"]
+    Y = rng.standard_normal((P["cap"], N))
+    Y[r2p < 0] = np.nan  # padding rows carry no value and must add nothing
+    out = O.weighted_scatter(Y, r2p, w, k, T)
+    # brute force over rows
+    ref = np.zeros((T, N))
+    for r in range(P["cap"]):
+        p = int(r2p[r])
+        if p >= 0:
+            ref[p // k] += float(w.reshape(-1)[p]) * Y[r]
+    assert np.max(np.abs(out - ref)) <= 1e-13
+    # the same sum as the gather-side combine over pair_to_row (k slots per token)
+    ref2 = np.zeros((T, N))
+    for t in range(T):
+        for j in range(k):
+            ref2[t] += float(w[t, j]) * Y[P["pair_to_row"][t * k + j]]
+    assert np.max(np.abs(out - ref2)) <= 1e-13
+    # k = 1, weight 1: a pure un-permutation, bit for bit
+    idx1, w1 = O.route(lg, 1)
+    P1 = O.permute(idx1, E)
+    Y1 = rng.standard_normal((P1["cap"], N))
+    o1 = O.weighted_scatter(Y1, P1["row_to_pair"], w1, 1, T)
+    assert np.array_equal(o1, Y1[P1["pair_to_row"]])
+    # one-hot weights select one slot
+    wh = np.zeros((T, k), np.float32)
+    wh[:, 2] = 1.0
+    oh = O.weighted_scatter(Y, r2p, wh, k, T)
+    assert np.array_equal(oh, Y[P["pair_to_row"].reshape(T, k)[:, 2]])
+
+
 def _layer_inputs(T, H, E, k, I, seed):
     d = syn.make_moe(T, H, E, k, I, seed=seed)
     idx, w = ORC.route(d["logits"], k)
@@ -344,7 +380,7 @@ def pin_pipeline_equals_definition(O):
 
 
 PINS = [pin_route_bruteforce, pin_route_closed_forms, pin_route_golden, pin_permute, pin_gather,
-        pin_gemm_random, pin_gemm_integer_exact, pin_fp16_decode, pin_silu, pin_combine,
+        pin_gemm_random, pin_gemm_integer_exact, pin_fp16_decode, pin_silu, pin_combine, pin_weighted_scatter,
         pin_layer_dense_special_case, pin_layer_bruteforce, pin_layer_golden,
         pin_pipeline_equals_definition]
 
