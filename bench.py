@@ -8,7 +8,11 @@ SiLU*up epilogue -> down grouped GEMM -> top-k weighted combine (moe_layer).
 W untimed steps, then exactly K timed steps bracketed by device
 synchronizations.  Per-kernel durations come from HIP events recorded on the
 launch stream around each step of the same path called entry point by entry
-point.  Prints one JSON line.
+point.  Also reported: per-step percentiles with the Infinity Cache warm and
+flushed (a 512 MiB write before each step, outside the events), the
+weighted-scatter variant of the combine (moe_layer_ex), and the part's
+measured MFMA and HBM-read peaks next to the published ones.  Prints one
+JSON line.
 """
 import argparse
 import json
@@ -92,6 +96,15 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / a.steps
+    stats = step_stats(step, a.steps)
+
+    def step_scatter():
+        moe.layer(x, wg, wu, wd, k, logits=logits, topk_idx=tidx, topk_w=tw, workspace=ws, out=out,
+                  combine="scatter")
+
+    for _ in range(a.warmup):
+        step_scatter()
+    stats_scatter = step_stats(step_scatter, a.steps, cold=False)
 
     # ---- per-kernel durations: HIP events on the launch stream, same path step by step
     stream = torch.cuda.current_stream()
@@ -118,6 +131,24 @@ def main():
             timed.append(e)
     torch.cuda.synchronize()
     dur = {n: float(np.mean([es[i].elapsed_time(es[i + 1]) for es in timed])) for i, n in enumerate(names)}
+    # the weighted-scatter down GEMM and its finalize, same inputs
+    acc = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    sc = []
+    for it in range(a.warmup + a.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        acc.zero_()
+        e[1].record(stream)
+        moe.grouped_gemm(h, wd, P.block_expert, P.num_padded_rows, N=H, K=I, cap=P.cap,
+                         epilogue="weighted_scatter", row_pair=P.row_to_pair, pair_w=w_t, out=acc)
+        e[2].record(stream)
+        moe.finalize(acc, out=out)
+        e[3].record(stream)
+        if it >= a.warmup:
+            sc.append(e)
+    torch.cuda.synchronize()
+    dur_sc = {n: float(np.mean([es[i].elapsed_time(es[i + 1]) for es in sc]))
+              for i, n in enumerate(["zero", "down_scatter", "finalize"])}
     m_pad = int(P.num_padded_rows.item())
     counts = P.counts.cpu().numpy()
     e_act = int((counts > 0).sum())
@@ -152,6 +183,10 @@ def main():
         "gemm_tflops": round(gemm_flops / gemm_s / 1e12, 2),
         "gemm_mfma_peak_frac": round(gemm_flops / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernel_us": {n: round(v * 1e3, 2) for n, v in dur.items()},
+        "layer_us_per_step": stats,
+        "scatter_combine": {"layer_us_per_step": stats_scatter,
+                            "kernel_us": {n: round(v * 1e3, 2) for n, v in dur_sc.items()}},
+        "measured_peaks": measured_peaks(),
         "roofline": {
             "kernel": "grouped_gemm gate/up (SiLU*up epilogue)",
             "bound": "hbm",
@@ -212,8 +247,99 @@ def bench_dense(a):
     }), flush=True)
 
 
-GEMM_SRC = os.path.join(ROOT, "moe_expert_grouped_amd", "csrc", "grouped_gemm.hip")
+CSRC = os.path.join(ROOT, "moe_expert_grouped_amd", "csrc")
+GEMM_SRCS = [os.path.join(CSRC, f) for f in ("gg_kernel.h", "gg_inst.hip", "grouped_gemm.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
+
+
+def gemm_source_sha256():
+    """SHA-256 of the grouped GEMM sources (kernel header, instantiation
+    unit, dispatcher), concatenated in that order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def _pcts(ms):
+    us = np.asarray(ms) * 1e3
+    return {"median": round(float(np.median(us)), 2), "p10": round(float(np.percentile(us, 10)), 2),
+            "p90": round(float(np.percentile(us, 90)), 2), "n": int(len(us))}
+
+
+def step_stats(step, n, cold=True):
+    """Per-step layer time from HIP events on the launch stream: with the
+    caches warm (steps back to back), and, if `cold`, with a 512 MiB write
+    before every step (outside the events) to evict the 256 MB Infinity Cache."""
+    import torch
+    stream = torch.cuda.current_stream()
+    res = {}
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if cold else None
+    for mode in (("warm", "cold") if cold else ("warm",)):
+        ev = []
+        for i in range(n):
+            if mode == "cold":
+                flush.fill_(i & 0xff)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        res[mode] = _pcts([a.elapsed_time(b) for a, b in ev])
+    del flush
+    return res
+
+
+PEAK_LIB = os.path.join(ROOT, "moe_expert_grouped_amd", "libmoe_peak_gfx950.so")
+
+
+def measured_peaks():
+    """The part's MFMA-only bf16 throughput and read-only HBM bandwidth,
+    measured with the kernels of libmoe_peak_gfx950.so (median of 5)."""
+    import ctypes
+    import torch
+    if not os.path.exists(PEAK_LIB):
+        return None
+    lib = ctypes.CDLL(PEAK_LIB)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.moe_peak_mfma_flops.argtypes, lib.moe_peak_mfma_flops.restype = [I, I], ctypes.c_longlong
+    lib.moe_peak_mfma.argtypes, lib.moe_peak_mfma.restype = [I, I, P, P], I
+    lib.moe_peak_read.argtypes, lib.moe_peak_read.restype = [P, Z, I, P, P], I
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(launch, reps=5):
+        launch()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if launch() != 0:
+                raise RuntimeError("peak kernel launch failed")
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e-3
+
+    wgs, iters = 2 * cus, 20000
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    t = timed(lambda: lib.moe_peak_mfma(wgs, iters, ctypes.c_void_p(sink.data_ptr()), sp))
+    mfma = lib.moe_peak_mfma_flops(wgs, iters) / t / 1e12
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    rwgs = 8 * cus
+    rsink = torch.empty(rwgs, dtype=torch.int32, device="cuda")
+    t = timed(lambda: lib.moe_peak_read(ctypes.c_void_p(buf.data_ptr()), nbytes, rwgs,
+                                        ctypes.c_void_p(rsink.data_ptr()), sp))
+    hbm = nbytes / t / 1e9
+    del buf
+    return {"mfma_bf16_tflops": round(mfma, 1), "mfma_published": PEAK_BF16_TFLOPS,
+            "hbm_read_gbs": round(hbm, 1), "hbm_published": PEAK_HBM_GBS,
+            "how": "MFMA-only loop (8 independent 32x32x16 bf16 chains per wavefront, %d workgroups); "
+                   "read-only stream of 2 GiB, 16-byte non-temporal loads" % wgs}
 
 
 def recorded_traffic(name):
@@ -224,7 +350,7 @@ def recorded_traffic(name):
     path = os.path.join(PROFILES, name + ".md")
     if not os.path.exists(path):
         return None
-    want = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    want = gemm_source_sha256()
     vals = {}
     for line in open(path):
         if ":" in line and line.strip().startswith(("traffic_bytes_per_launch", "kernel_source_sha256")):

@@ -69,6 +69,11 @@ extern "C" {
 /* Epilogues of grouped_gemm. */
 #define MOE_EPI_STORE 0    /* D[r][n] = round(acc)                              */
 #define MOE_EPI_SILU_MUL 1 /* D[r][n] = round(SiLU(A.B)[r][n] * (A.B2)[r][n])  */
+#define MOE_EPI_WEIGHTED_SCATTER 2 /* D[p/k][n] += w[p] * (A.B)[r][n], fp32 D      */
+
+/* How moe_layer_ex returns expert outputs to token order. */
+#define MOE_COMBINE_GATHER 0  /* y stored per row, then moe_combine (deterministic) */
+#define MOE_COMBINE_SCATTER 1 /* down GEMM scatters w*y into fp32 rows, moe_finalize */
 
 #define MOE_ROW_BLOCK 128 /* rows per task and per-expert alignment unit [P1 s.4] */
 
@@ -133,12 +138,23 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, const void *x,
  *                                       row_to_pair and k: the row gather
  *                                       of the reorder-by-route prologue)
  * Rows with a_src_row[r] < 0 are padding: their outputs are unspecified.
- *   dtype      MOE_BF16 or MOE_FP16 (A, B, B2 and D all of this type)
+ *   dtype      MOE_BF16 or MOE_FP16 (A, B, B2 and D all of this type, except
+ *              D of MOE_EPI_WEIGHTED_SCATTER, which is fp32)
  *   A          [*][K]   (rows addressed by a(r))
  *   B, B2      [G][K][N] (MOE_B_KN) or [G][N][K] (MOE_B_NK); B2 only for
  *              MOE_EPI_SILU_MUL (the up weights; B holds the gate weights)
- *   D          [cap][N]
- * Accumulation is fp32 (MFMA); the epilogue rounds to nearest even.
+ *   D          [cap][N] for MOE_EPI_STORE and MOE_EPI_SILU_MUL.
+ *   epi_row_pair, pair_w, k   used by MOE_EPI_WEIGHTED_SCATTER only (pass
+ *              NULL, NULL, 0 otherwise): the top-k weighted reduction of
+ *              [P2 s.4] (MoE layer1 row) done by the epilogue.  Row r with
+ *              p = epi_row_pair[r] >= 0 adds pair_w[p] * (A.B)[r] into
+ *              D[p / k], an fp32 [T][N] buffer the caller has zeroed; rows
+ *              with p < 0 add nothing.  The adds are fp32 device-scope
+ *              atomics: the k contributions to a token sum in no fixed
+ *              order, so results are reproducible only up to fp32 rounding
+ *              order.  MOE_B_KN only.  For the MoE down GEMM:
+ *              epi_row_pair = row_to_pair, pair_w = topk_w.
+ * Accumulation is fp32 (MFMA); the store epilogues round to nearest even.
  * Requires N % 64 == 0, K % 64 == 0, cap % 128 == 0.
  * workspace (optional, may be NULL): scratch of at least
  * grouped_gemm_workspace_size() bytes, 256-byte aligned, contents need not be
@@ -151,8 +167,9 @@ size_t grouped_gemm_workspace_size(void);
 int grouped_gemm(int dtype, int N, int K, int cap, const void *A,
                  const int32_t *a_src_row, int a_src_div, const void *B,
                  const void *B2, int b_layout, const int32_t *block_group,
-                 const int32_t *num_rows, int epilogue, void *D,
-                 void *workspace, size_t ws_bytes, void *stream);
+                 const int32_t *num_rows, int epilogue,
+                 const int32_t *epi_row_pair, const float *pair_w, int k,
+                 void *D, void *workspace, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * moe_combine -- top-k weighted reduction back to token order.    [P2 s.4]
@@ -165,6 +182,14 @@ int moe_combine(const void *y, int H, const int32_t *pair_to_row,
                 const float *topk_w, int T, int k, void *out, void *stream);
 
 /* ------------------------------------------------------------------------
+ * moe_finalize -- last step of the weighted-scatter combine:      [P2 s.4]
+ *   out[i] = round_bf16(acc[i]) for 0 <= i < n.
+ *   acc [n] fp32 (the D of grouped_gemm MOE_EPI_WEIGHTED_SCATTER),
+ *   out [n] bf16.  Requires n >= 1.
+ * ---------------------------------------------------------------------- */
+int moe_finalize(const float *acc, size_t n, void *out, void *stream);
+
+/* ------------------------------------------------------------------------
  * moe_layer -- the whole share:                               [P2 s.1, s.4]
  *   out[t] = sum_j w[t][j] * ( SiLU(x[t] . Wg[e]) * (x[t] . Wu[e]) ) . Wd[e],
  *   e = topk_idx[t][j].
@@ -173,7 +198,8 @@ int moe_combine(const void *y, int H, const int32_t *pair_to_row,
  *   x [T][H] bf16; w_gate, w_up [E][H][I] bf16; w_down [E][I][H] bf16;
  *   out [T][H] bf16.
  * Intermediates: h = SiLU(gate)*up stored as bf16 [M_pad][I], expert outputs
- * y stored as bf16 [M_pad][H]; both live in the workspace.
+ * y stored as bf16 [M_pad][H]; both live in the workspace.  The combine is
+ * MOE_COMBINE_GATHER (deterministic: same input, same bits).
  * Requires H % 64 == 0, I % 64 == 0, plus the limits of the steps.
  * Workspace: moe_layer_workspace_size(T, H, E, k, I) bytes, 256-byte aligned.
  * ---------------------------------------------------------------------- */
@@ -187,15 +213,30 @@ size_t moe_layer_workspace_size(int T, int H, int E, int k, int I);
  *   6 block_expert [cap/128]    7 num_padded_rows [1] int32
  *   8 h [cap][I] bf16           9 y [cap][H] bf16
  *  10 permute scratch          11 grouped-GEMM scratch
- *  12 total size
+ *  12 out_acc [T][H] fp32 (MOE_COMBINE_SCATTER only)
+ *  13 total size
  * Returns MOE_OK or MOE_ERR_INVALID. */
 int moe_layer_workspace_layout(int T, int H, int E, int k, int I,
-                               size_t off[13]);
+                               size_t off[14]);
 
 int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
               const float *topk_w_in, const void *w_gate, const void *w_up,
               const void *w_down, int T, int H, int E, int k, int I, void *out,
               void *workspace, size_t ws_bytes, void *stream);
+
+/* moe_layer with a choice of combine ([P2 s.4], MoE layer1 row: the top-k
+ * weighted reduction either after the down GEMM or inside its epilogue):
+ *   MOE_COMBINE_GATHER   exactly moe_layer;
+ *   MOE_COMBINE_SCATTER  the down GEMM adds w * y into out_acc (fp32, zeroed
+ *                        by the call) with MOE_EPI_WEIGHTED_SCATTER, then
+ *                        moe_finalize rounds it into out; y is never stored.
+ *                        Sums of a token's k slots are in no fixed order.
+ * Same arguments, workspace and limits as moe_layer otherwise. */
+int moe_layer_ex(const void *x, const float *logits,
+                 const int32_t *topk_idx_in, const float *topk_w_in,
+                 const void *w_gate, const void *w_up, const void *w_down,
+                 int T, int H, int E, int k, int I, void *out, int combine,
+                 void *workspace, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

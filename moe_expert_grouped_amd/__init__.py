@@ -14,6 +14,13 @@ library is not built, or no GPU is present, calls raise.
     y      = grouped_gemm(h, wd, perm.block_expert, perm.num_padded_rows, N=H, K=I, cap=perm.cap)
     out    = combine(y, perm.pair_to_row, w)
     out    = layer(x, wg, wu, wd, k, logits=logits)   # all of the above in one call
+
+The combine can instead be folded into the down GEMM (fp32 atomics into token
+rows, then a rounding pass):
+    acc    = grouped_gemm(h, wd, ..., epilogue="weighted_scatter",
+                          row_pair=perm.row_to_pair, pair_w=w, T=T)
+    out    = finalize(acc)
+    out    = layer(x, wg, wu, wd, k, logits=logits, combine="scatter")
 """
 from __future__ import annotations
 
@@ -30,7 +37,8 @@ ROW_BLOCK = 128
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 _DTYPES = {torch.bfloat16: 0, torch.float16: 1}
 _LAYOUTS = {"kn": 0, "nk": 1}
-_EPIS = {"store": 0, "silu_mul": 1}
+_EPIS = {"store": 0, "silu_mul": 1, "weighted_scatter": 2}
+_COMBINES = {"gather": 0, "scatter": 1}
 
 _lib = None
 
@@ -59,11 +67,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "moe_permute_workspace_size": ([I, I, I], Z),
             "moe_permute": ([P, I, I, I, P, I, P, P, P, P, P, P, P, I, P, Z, P], I),
             "grouped_gemm_workspace_size": ([], Z),
-            "grouped_gemm": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P, Z, P], I),
+            "grouped_gemm": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P, I, P, P, Z, P], I),
             "moe_combine": ([P, I, P, P, I, I, P, P], I),
+            "moe_finalize": ([P, Z, P, P], I),
             "moe_layer_workspace_size": ([I, I, I, I, I], Z),
             "moe_layer_workspace_layout": ([I, I, I, I, I, ctypes.POINTER(Z)], I),
             "moe_layer": ([P, P, P, P, P, P, P, I, I, I, I, I, P, P, Z, P], I),
+            "moe_layer_ex": ([P, P, P, P, P, P, P, I, I, I, I, I, P, I, P, Z, P], I),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -168,10 +178,17 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
                  num_rows: torch.Tensor, *, N: int, K: int, cap: int,
                  a_src_row: torch.Tensor | None = None, a_src_div: int = 1,
                  B2: torch.Tensor | None = None, b_layout: str = "kn", epilogue: str = "store",
-                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                 split_tail: bool = True) -> torch.Tensor:
+                 row_pair: torch.Tensor | None = None, pair_w: torch.Tensor | None = None,
+                 T: int | None = None, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None, split_tail: bool = True) -> torch.Tensor:
     """D[r] = A[a(r)] . B[block_group[r // 128]] for r < min(num_rows, cap),
     or SiLU(A.B) * (A.B2) with epilogue="silu_mul".  Returns D [cap, N].
+
+    epilogue="weighted_scatter": row r with p = row_pair[r] >= 0 adds
+    pair_w[p] * (A.B)[r] into the fp32 row p // k of D [T, N] (k = pair_w's
+    second dimension); D is zero-filled here unless `out` is given, in which
+    case it is accumulated into.
+
     With split_tail, a scratch workspace lets the last partly filled round of
     tasks be split along K (allocated here if not given)."""
     _need(A, "A", (torch.bfloat16, torch.float16))
@@ -182,7 +199,20 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
         _need(B2, "B2", A.dtype)
     if a_src_row is not None:
         _need(a_src_row, "a_src_row", torch.int32)
-    if out is None:
+    k = 0
+    if epilogue == "weighted_scatter":
+        _need(row_pair, "row_pair", torch.int32)
+        _need(pair_w, "pair_w", torch.float32, 2)
+        k = pair_w.shape[1]
+        if T is None:
+            T = pair_w.shape[0]
+        if out is None:
+            out = torch.zeros((T, N), dtype=torch.float32, device=A.device)
+        else:
+            _need(out, "out", torch.float32)
+            if out.numel() < T * N:
+                raise ValueError("out must hold [T, N] = [%d, %d] floats" % (T, N))
+    elif out is None:
         out = torch.empty((cap, N), dtype=A.dtype, device=A.device)
     else:
         _need(out, "out", A.dtype)
@@ -193,8 +223,9 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
         workspace = None
     _check("grouped_gemm", lib.grouped_gemm(
         _DTYPES[A.dtype], N, K, cap, _ptr(A), _ptr(a_src_row), a_src_div, _ptr(B), _ptr(B2),
-        _LAYOUTS[b_layout], _ptr(block_group), _ptr(num_rows), _EPIS[epilogue], _ptr(out),
-        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream()))
+        _LAYOUTS[b_layout], _ptr(block_group), _ptr(num_rows), _EPIS[epilogue], _ptr(row_pair),
+        _ptr(pair_w), k, _ptr(out), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _stream()))
     return out
 
 
@@ -229,17 +260,30 @@ def combine(y: torch.Tensor, pair_to_row: torch.Tensor, topk_w: torch.Tensor,
     return out
 
 
+def finalize(acc: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """out = bf16(acc), round to nearest even (the weighted-scatter combine's last step)."""
+    _need(acc, "acc", torch.float32)
+    if out is None:
+        out = torch.empty(acc.shape, dtype=torch.bfloat16, device=acc.device)
+    else:
+        _need(out, "out", torch.bfloat16)
+        if out.numel() != acc.numel():
+            raise ValueError("out must have as many elements as acc")
+    _check("moe_finalize", load_library().moe_finalize(_ptr(acc), acc.numel(), _ptr(out), _stream()))
+    return out
+
+
 # ---------------------------------------------------------------- whole layer
 
 LAYOUT_NAMES = ["topk_idx", "topk_w", "expert_counts", "expert_offsets", "pair_to_row",
                 "row_to_pair", "block_expert", "num_padded_rows", "h", "y", "permute_scratch",
-                "gemm_scratch"]
+                "gemm_scratch", "out_acc"]
 
 
 def layer_workspace_layout(T, H, E, k, I):
-    arr = (ctypes.c_size_t * 13)()
+    arr = (ctypes.c_size_t * 14)()
     _check("moe_layer_workspace_layout", load_library().moe_layer_workspace_layout(T, H, E, k, I, arr))
-    return {name: int(arr[i]) for i, name in enumerate(LAYOUT_NAMES)} | {"total": int(arr[12])}
+    return {name: int(arr[i]) for i, name in enumerate(LAYOUT_NAMES)} | {"total": int(arr[13])}
 
 
 def layer_workspace(T, H, E, k, I, device="cuda") -> torch.Tensor:
@@ -252,9 +296,11 @@ def layer_workspace(T, H, E, k, I, device="cuda") -> torch.Tensor:
 def layer(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, k: int,
           logits: torch.Tensor | None = None, topk_idx: torch.Tensor | None = None,
           topk_w: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-          out: torch.Tensor | None = None) -> torch.Tensor:
+          out: torch.Tensor | None = None, combine: str = "gather") -> torch.Tensor:
     """The MoE layer share: route (or the given routing) -> permute -> gate/up
-    grouped GEMM with SiLU*up -> down grouped GEMM -> top-k weighted combine."""
+    grouped GEMM with SiLU*up -> down grouped GEMM -> top-k weighted combine.
+    combine="gather" (deterministic) stores y and runs the combine kernel;
+    "scatter" folds the weighted sum into the down GEMM's epilogue."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w_gate, "w_gate", torch.bfloat16, 3)
     _need(w_up, "w_up", torch.bfloat16, 3)
@@ -270,9 +316,15 @@ def layer(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: tor
         workspace = layer_workspace(T, H, E, k, I, x.device)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
-    _check("moe_layer", load_library().moe_layer(
-        _ptr(x), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
-        _ptr(w_down), T, H, E, k, I, _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    if combine == "gather":
+        _check("moe_layer", load_library().moe_layer(
+            _ptr(x), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
+            _ptr(w_down), T, H, E, k, I, _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    else:
+        _check("moe_layer_ex", load_library().moe_layer_ex(
+            _ptr(x), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
+            _ptr(w_down), T, H, E, k, I, _ptr(out), _COMBINES[combine], _ptr(workspace),
+            workspace.numel(), _stream()))
     return out
 
 
@@ -286,6 +338,7 @@ def workspace_view(workspace: torch.Tensor, T, H, E, k, I, name: str) -> torch.T
         "pair_to_row": ((T * k,), torch.int32), "row_to_pair": ((cap,), torch.int32),
         "block_expert": ((cap // ROW_BLOCK,), torch.int32), "num_padded_rows": ((1,), torch.int32),
         "h": ((cap, I), torch.bfloat16), "y": ((cap, H), torch.bfloat16),
+        "out_acc": ((T, H), torch.float32),
     }
     shape, dt = shapes[name]
     n = 1

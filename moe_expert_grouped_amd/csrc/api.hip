@@ -14,11 +14,13 @@ hipError_t launch_permute(const int32_t *, int, int, int, const uint16_t *, int,
                           void *, hipStream_t);
 hipError_t launch_grouped_gemm(int, int, int, int, const uint16_t *, const int32_t *, int,
                                const uint16_t *, const uint16_t *, int, const int32_t *,
-                               const int32_t *, int, uint16_t *, void *, size_t, int,
-                               hipStream_t);
+                               const int32_t *, int, const int32_t *, const float *, int, void *,
+                               void *, size_t, int, hipStream_t);
 size_t gg_workspace_bytes(int grid);
 hipError_t launch_combine(const uint16_t *, int, const int32_t *, const float *, int, int,
                           uint16_t *, hipStream_t);
+hipError_t launch_finalize(const float *, long, uint16_t *, hipStream_t);
+hipError_t launch_zero(float *, long, hipStream_t);
 } // namespace moe
 
 namespace {
@@ -125,7 +127,8 @@ size_t grouped_gemm_workspace_size(void) {
 
 int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t *a_src_row,
                  int a_src_div, const void *B, const void *B2, int b_layout,
-                 const int32_t *block_group, const int32_t *num_rows, int epilogue, void *D,
+                 const int32_t *block_group, const int32_t *num_rows, int epilogue,
+                 const int32_t *epi_row_pair, const float *pair_w, int k, void *D,
                  void *workspace, size_t ws_bytes, void *stream) {
   if (!A || !B || !block_group || !num_rows || !D) return MOE_ERR_INVALID;
   if (!aligned16(A) || !aligned16(B) || !aligned16(D) || (B2 && !aligned16(B2)))
@@ -133,8 +136,14 @@ int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t 
   if (N <= 0 || K <= 0 || cap <= 0) return MOE_ERR_INVALID;
   if (dtype != MOE_BF16 && dtype != MOE_FP16) return MOE_ERR_UNSUPPORTED;
   if (b_layout != MOE_B_KN && b_layout != MOE_B_NK) return MOE_ERR_UNSUPPORTED;
-  if (epilogue != MOE_EPI_STORE && epilogue != MOE_EPI_SILU_MUL) return MOE_ERR_UNSUPPORTED;
+  if (epilogue != MOE_EPI_STORE && epilogue != MOE_EPI_SILU_MUL &&
+      epilogue != MOE_EPI_WEIGHTED_SCATTER)
+    return MOE_ERR_UNSUPPORTED;
   if (epilogue == MOE_EPI_SILU_MUL && !B2) return MOE_ERR_INVALID;
+  if (epilogue == MOE_EPI_WEIGHTED_SCATTER) {
+    if (!epi_row_pair || !pair_w || k <= 0) return MOE_ERR_INVALID;
+    if (b_layout != MOE_B_KN) return MOE_ERR_UNSUPPORTED;
+  }
   if (a_src_row && a_src_div <= 0) return MOE_ERR_INVALID;
   if (N % 64 != 0 || K % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (cap % MOE_ROW_BLOCK != 0) return MOE_ERR_INVALID;
@@ -143,8 +152,8 @@ int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t 
   if (cus == 0) return MOE_ERR_DEVICE;
   return launch_status(moe::launch_grouped_gemm(
       dtype, N, K, cap, (const uint16_t *)A, a_src_row, a_src_div, (const uint16_t *)B,
-      (const uint16_t *)B2, b_layout, block_group, num_rows, epilogue, (uint16_t *)D,
-      workspace, workspace ? ws_bytes : 0, cus, (hipStream_t)stream));
+      (const uint16_t *)B2, b_layout, block_group, num_rows, epilogue, epi_row_pair, pair_w, k,
+      D, workspace, workspace ? ws_bytes : 0, cus, (hipStream_t)stream));
 }
 
 int moe_combine(const void *y, int H, const int32_t *pair_to_row, const float *topk_w, int T,
@@ -158,7 +167,16 @@ int moe_combine(const void *y, int H, const int32_t *pair_to_row, const float *t
                                            (uint16_t *)out, (hipStream_t)stream));
 }
 
-int moe_layer_workspace_layout(int T, int H, int E, int k, int I, size_t off[13]) {
+int moe_finalize(const float *acc, size_t n, void *out, void *stream) {
+  if (!acc || !out || n == 0) return MOE_ERR_INVALID;
+  if (!aligned16(acc) || !aligned16(out)) return MOE_ERR_INVALID;
+  if (n > ((size_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  if (device_cus() == 0) return MOE_ERR_DEVICE;
+  return launch_status(
+      moe::launch_finalize(acc, (long)n, (uint16_t *)out, (hipStream_t)stream));
+}
+
+int moe_layer_workspace_layout(int T, int H, int E, int k, int I, size_t off[14]) {
   if (!off || T <= 0 || H <= 0 || E <= 0 || k <= 0 || I <= 0 || k > E) return MOE_ERR_INVALID;
   const long R = (long)T * k;
   const long cap = padded_cap(T, k, E);
@@ -179,20 +197,29 @@ int moe_layer_workspace_layout(int T, int H, int E, int k, int I, size_t off[13]
   take(9, (size_t)cap * H * 2);
   take(10, moe::permute_workspace_bytes(R, E));
   take(11, grouped_gemm_workspace_size());
-  off[12] = o;
+  take(12, (size_t)T * H * 4);
+  off[13] = o;
   return MOE_OK;
 }
 
 size_t moe_layer_workspace_size(int T, int H, int E, int k, int I) {
-  size_t off[13];
+  size_t off[14];
   if (moe_layer_workspace_layout(T, H, E, k, I, off) != MOE_OK) return 0;
-  return off[12];
+  return off[13];
 }
 
 int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
               const float *topk_w_in, const void *w_gate, const void *w_up, const void *w_down,
               int T, int H, int E, int k, int I, void *out, void *workspace, size_t ws_bytes,
               void *stream) {
+  return moe_layer_ex(x, logits, topk_idx_in, topk_w_in, w_gate, w_up, w_down, T, H, E, k, I,
+                      out, MOE_COMBINE_GATHER, workspace, ws_bytes, stream);
+}
+
+int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
+                 const float *topk_w_in, const void *w_gate, const void *w_up,
+                 const void *w_down, int T, int H, int E, int k, int I, void *out, int combine,
+                 void *workspace, size_t ws_bytes, void *stream) {
   if (!x || !w_gate || !w_up || !w_down || !out || !workspace) return MOE_ERR_INVALID;
   if (!logits && (!topk_idx_in || !topk_w_in)) return MOE_ERR_INVALID;
   if (T <= 0 || H <= 0 || E <= 0 || k <= 0 || I <= 0 || k > E) return MOE_ERR_INVALID;
@@ -202,9 +229,10 @@ int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
   if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (E > 1024 || k > 16) return MOE_ERR_UNSUPPORTED;
   if ((long)T * k > 0x7fffffffL / 2) return MOE_ERR_UNSUPPORTED;
-  size_t off[13];
+  if (combine != MOE_COMBINE_GATHER && combine != MOE_COMBINE_SCATTER) return MOE_ERR_UNSUPPORTED;
+  size_t off[14];
   moe_layer_workspace_layout(T, H, E, k, I, off);
-  if (ws_bytes < off[12]) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < off[13]) return MOE_ERR_WORKSPACE;
   const int cus = device_cus();
   if (cus == 0) return MOE_ERR_DEVICE;
 
@@ -223,6 +251,7 @@ int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
   void *pws = ws + off[10];
   void *gws = ws + off[11];
   const size_t gws_bytes = off[12] - off[11];
+  float *oacc = (float *)(ws + off[12]);
   const int cap = (int)padded_cap(T, k, E);
 
   const int32_t *ridx = topk_idx_in;
@@ -239,11 +268,21 @@ int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   e = moe::launch_grouped_gemm(MOE_BF16, I, H, cap, (const uint16_t *)x, r2p, k,
                                (const uint16_t *)w_gate, (const uint16_t *)w_up, MOE_B_KN, bexp,
-                               mpad, MOE_EPI_SILU_MUL, h, gws, gws_bytes, cus, s);
-  if (e != hipSuccess) return MOE_ERR_DEVICE;
-  e = moe::launch_grouped_gemm(MOE_BF16, H, I, cap, h, nullptr, 1, (const uint16_t *)w_down,
-                               nullptr, MOE_B_KN, bexp, mpad, MOE_EPI_STORE, y, gws, gws_bytes,
+                               mpad, MOE_EPI_SILU_MUL, nullptr, nullptr, 0, h, gws, gws_bytes,
                                cus, s);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  if (combine == MOE_COMBINE_SCATTER) {
+    e = moe::launch_zero(oacc, (long)T * H, s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    e = moe::launch_grouped_gemm(MOE_BF16, H, I, cap, h, nullptr, 1, (const uint16_t *)w_down,
+                                 nullptr, MOE_B_KN, bexp, mpad, MOE_EPI_WEIGHTED_SCATTER, r2p, rw,
+                                 k, oacc, gws, gws_bytes, cus, s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    return launch_status(moe::launch_finalize(oacc, (long)T * H, (uint16_t *)out, s));
+  }
+  e = moe::launch_grouped_gemm(MOE_BF16, H, I, cap, h, nullptr, 1, (const uint16_t *)w_down,
+                               nullptr, MOE_B_KN, bexp, mpad, MOE_EPI_STORE, nullptr, nullptr, 0,
+                               y, gws, gws_bytes, cus, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   e = moe::launch_combine(y, H, p2r, rw, T, k, (uint16_t *)out, s);
   return launch_status(e);

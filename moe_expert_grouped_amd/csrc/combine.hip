@@ -70,4 +70,46 @@ hipError_t launch_combine(const uint16_t *y, int H, const int32_t *pair_to_row, 
   return hipGetLastError();
 }
 
+// Finalize of the weighted-scatter variant: out[i] = round_bf16(acc[i]),
+// 8 elements (32 bytes in, 16 bytes out) per thread; the scalar tail covers
+// n % 8.  HBM-bound: 6 bytes per element.
+__global__ __launch_bounds__(256) void finalize_kernel(const float *__restrict__ acc, long n,
+                                                       uint16_t *__restrict__ out) {
+  const long i = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (i + 8 <= n) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(acc + i);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(acc + i + 4);
+    u32x4 o;
+    o[0] = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
+    o[1] = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
+    o[2] = (uint32_t)f32_to_bf16(b[0]) | ((uint32_t)f32_to_bf16(b[1]) << 16);
+    o[3] = (uint32_t)f32_to_bf16(b[2]) | ((uint32_t)f32_to_bf16(b[3]) << 16);
+    *reinterpret_cast<u32x4 *>(out + i) = o;
+  } else {
+    for (long j = i; j < n; ++j) out[j] = f32_to_bf16(acc[j]);
+  }
+}
+
+// Clears n floats (16 bytes per thread, scalar tail).  A kernel rather than
+// a memset node, so the layer stays capturable in a HIP graph.
+__global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ p, long n) {
+  const long i = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i + 4 <= n)
+    *reinterpret_cast<f32x4 *>(p + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+  else
+    for (long j = i; j < n; ++j) p[j] = 0.f;
+}
+
+hipError_t launch_finalize(const float *acc, long n, uint16_t *out, hipStream_t stream) {
+  const long threads = (n + 7) / 8;
+  finalize_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(acc, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(float *p, long n, hipStream_t stream) {
+  const long threads = (n + 3) / 4;
+  zero_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(p, n);
+  return hipGetLastError();
+}
+
 } // namespace moe

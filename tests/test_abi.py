@@ -28,8 +28,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12, names
-    for n in ["moe_route", "moe_permute", "grouped_gemm", "moe_combine", "moe_layer"]:
+    assert len(names) == 14, names
+    for n in ["moe_route", "moe_permute", "grouped_gemm", "moe_combine", "moe_finalize", "moe_layer",
+              "moe_layer_ex"]:
         assert n in names
     for n in names:
         assert hasattr(lib, n), "missing export " + n
@@ -61,7 +62,8 @@ def test_layer_workspace_layout(lib):
     assert all(o % 256 == 0 for o in offs)
     cap = moe.padded_capacity(T, k, E)
     assert lay["y"] - lay["h"] >= cap * I * 2
-    assert lay["total"] - lay["y"] >= cap * H * 2
+    assert lay["permute_scratch"] - lay["y"] >= cap * H * 2
+    assert lay["total"] - lay["out_acc"] >= T * H * 4
     assert lib.moe_layer_workspace_size(T, H, E, k, I) == lay["total"]
     assert lib.moe_layer_workspace_size(T, H, E, 65, I) == 0  # k > E
 
@@ -99,8 +101,9 @@ def test_permute_validation(lib):
 
 def test_grouped_gemm_validation(lib):
     def call(dtype=0, N=128, K=128, cap=256, A=FAKE, src=NULL, div=1, B=FAKE, B2=NULL, lay=0,
-             bg=FAKE, nr=FAKE, epi=0, D=FAKE, ws=NULL):
-        return lib.grouped_gemm(dtype, N, K, cap, A, src, div, B, B2, lay, bg, nr, epi, D, ws, 0, NULL)
+             bg=FAKE, nr=FAKE, epi=0, rp=NULL, pw=NULL, k=0, D=FAKE, ws=NULL):
+        return lib.grouped_gemm(dtype, N, K, cap, A, src, div, B, B2, lay, bg, nr, epi, rp, pw, k, D,
+                                ws, 0, NULL)
     assert call(A=NULL) == moe.MOE_ERR_INVALID
     assert call(A=MISALIGNED) == moe.MOE_ERR_INVALID
     assert call(N=96) == moe.MOE_ERR_UNSUPPORTED
@@ -112,7 +115,19 @@ def test_grouped_gemm_validation(lib):
     assert call(epi=7) == moe.MOE_ERR_UNSUPPORTED
     assert call(src=FAKE, div=0) == moe.MOE_ERR_INVALID
     assert call(ws=MISALIGNED) == moe.MOE_ERR_INVALID
+    # weighted scatter: needs the row -> pair map, the weights and k >= 1; [K][N] weights only
+    assert call(epi=2) == moe.MOE_ERR_INVALID
+    assert call(epi=2, rp=FAKE, pw=FAKE, k=0) == moe.MOE_ERR_INVALID
+    assert call(epi=2, rp=FAKE, pw=NULL, k=2) == moe.MOE_ERR_INVALID
+    assert call(epi=2, rp=FAKE, pw=FAKE, k=2, lay=1) == moe.MOE_ERR_UNSUPPORTED
+    assert call(epi=3) == moe.MOE_ERR_UNSUPPORTED
     assert lib.grouped_gemm_workspace_size() > 0
+
+
+def test_finalize_validation(lib):
+    assert lib.moe_finalize(NULL, 64, FAKE, NULL) == moe.MOE_ERR_INVALID
+    assert lib.moe_finalize(FAKE, 0, FAKE, NULL) == moe.MOE_ERR_INVALID
+    assert lib.moe_finalize(FAKE, 64, MISALIGNED, NULL) == moe.MOE_ERR_INVALID
 
 
 def test_combine_and_layer_validation(lib):
@@ -130,6 +145,14 @@ def test_combine_and_layer_validation(lib):
     assert call(I=80) == moe.MOE_ERR_UNSUPPORTED
     assert call(k=9) == moe.MOE_ERR_INVALID
     assert call(wsb=ws - 1) == moe.MOE_ERR_WORKSPACE
+
+    def call_ex(combine, wsb=ws, x=FAKE):
+        return lib.moe_layer_ex(x, FAKE, NULL, NULL, FAKE, FAKE, FAKE, T, H, E, k, I, FAKE, combine,
+                                FAKE, wsb, NULL)
+    assert call_ex(2) == moe.MOE_ERR_UNSUPPORTED
+    assert call_ex(-1) == moe.MOE_ERR_UNSUPPORTED
+    assert call_ex(1, x=NULL) == moe.MOE_ERR_INVALID
+    assert call_ex(1, wsb=ws - 1) == moe.MOE_ERR_WORKSPACE
 
 
 def test_valid_call_without_device_reports_device_error(lib):

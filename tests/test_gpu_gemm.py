@@ -223,3 +223,82 @@ def test_split_tail_random_values_and_repeatability(monkeypatch):
     rows = g.choice(cap, 48, replace=False).astype(np.int32)
     ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, rows=rows)
     assert_close(to_f64(D1)[rows], ref, "split random")
+
+
+def _scatter_case(T, k, E, K, N, seed, dtype="bf16"):
+    """A down-GEMM-shaped scatter case: routing by the oracle, integer
+    (ternary) A and B, power-of-two weights -- every fp32 partial sum is exact
+    in any order, so the atomically accumulated result is unique."""
+    g = np.random.default_rng(seed)
+    idx, _ = oracle.route(g.standard_normal((T, E)).astype(np.float32), k)
+    P = oracle.permute(idx, E)
+    cap = P["cap"]
+    A = syn.ternary_bits((cap, K), seed + 1, dtype)
+    B = syn.ternary_bits((E, K, N), seed + 2, dtype)
+    w = g.choice(np.array([0.25, 0.5, 1.0, 2.0, -1.0], np.float32), size=(T, k))
+    return P, A, B, w
+
+
+def _run_scatter(P, A, B, w, *, N, K, dtype="bf16", out=None):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    return moe.grouped_gemm(dev16(A, tdt), dev16(B, tdt), torch.from_numpy(P["block_expert"]).cuda(),
+                            torch.tensor([P["m_pad"]], dtype=torch.int32, device="cuda"), N=N, K=K,
+                            cap=P["cap"], epilogue="weighted_scatter",
+                            row_pair=torch.from_numpy(P["row_to_pair"]).cuda(),
+                            pair_w=torch.from_numpy(w).cuda(), out=out)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("T,k,E,K,N", [(150, 3, 4, 320, 256), (200, 1, 5, 64, 128), (90, 2, 3, 128, 192)])
+def test_weighted_scatter_integer_exact(dtype, T, k, E, K, N):
+    P, A, B, w = _scatter_case(T, k, E, K, N, seed=T + N, dtype=dtype)
+    say("scatter integer", dtype, T, k, E, K, N)
+    got = _run_scatter(P, A, B, w, N=N, K=K, dtype=dtype)
+    torch.cuda.synchronize()
+    Y = oracle.grouped_gemm(A, B, P["block_expert"], N=N, K=K, is_fp16=(dtype == "fp16"))
+    ref = oracle.weighted_scatter(Y, P["row_to_pair"], w, k, T)
+    assert np.array_equal(got.cpu().numpy().astype(np.float64), ref)
+
+
+def test_weighted_scatter_accumulates_and_split_tail(monkeypatch):
+    # `out` is accumulated into (the caller zeroes it); the split tail sums
+    # its partial tiles before scattering, so the exact result is unchanged
+    T, k, E, K, N = 260, 2, 6, 512, 256
+    P, A, B, w = _scatter_case(T, k, E, K, N, seed=5)
+    Y = oracle.grouped_gemm(A, B, P["block_expert"], N=N, K=K)
+    ref = oracle.weighted_scatter(Y, P["row_to_pair"], w, k, T)
+    for tile in ["256,3,1,0", "256,3,1,1", "128,4,2,1", "64,3,1,0,8"]:
+        monkeypatch.setenv("MOE_GG_TILE", tile)
+        say("scatter tile", tile)
+        base = torch.full((T, N), 3.0, dtype=torch.float32, device="cuda")
+        got = _run_scatter(P, A, B, w, N=N, K=K, out=base)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy().astype(np.float64), ref + 3.0), tile
+
+
+def test_weighted_scatter_random_values():
+    # bf16 random data, fp32 atomics: within the tolerances of the oracle's exact sum
+    T, k, E, K, N = 300, 4, 8, 256, 512
+    g = np.random.default_rng(21)
+    idx, w = oracle.route(g.standard_normal((T, E)).astype(np.float32), k)
+    P = oracle.permute(idx, E)
+    A = syn.bf16_bits(g.standard_normal((P["cap"], K)).astype(np.float32))
+    B = syn.bf16_bits((g.standard_normal((E, K, N)) / np.sqrt(K)).astype(np.float32))
+    say("scatter random")
+    got = _run_scatter(P, A, B, w, N=N, K=K)
+    torch.cuda.synchronize()
+    Y = oracle.grouped_gemm(A, B, P["block_expert"], N=N, K=K)
+    ref = oracle.weighted_scatter(Y, P["row_to_pair"], w, k, T)
+    assert_close(got.cpu().numpy().astype(np.float64), ref, "scatter random", max_frac=1e-4, rel_fro=1e-5)
+
+
+@pytest.mark.parametrize("n", [8, 1000003, 4096 * 2048])
+def test_finalize_rounds_to_nearest_even(n):
+    # against torch's CPU fp32 -> bf16 conversion (round to nearest even)
+    g = torch.Generator().manual_seed(n)
+    acc = torch.randn(n, generator=g) * 100
+    acc[: min(n, 4)] = torch.tensor([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -0.0, 65504.0])[: min(n, 4)]
+    say("finalize", n)
+    out = moe.finalize(acc.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu().view(torch.int16), acc.to(torch.bfloat16).view(torch.int16))

@@ -26,24 +26,24 @@ def _routing(d):
     return d["topk_idx"], d["topk_w"]
 
 
-def _run_layer(d, D):
+def _run_layer(d, D, combine="gather"):
     T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
     ws = moe.layer_workspace(T, H, E, k, I)
     if "logits" in d:
         out = moe.layer(D["x"], D["wg"], D["wu"], D["wd"], k, logits=torch.from_numpy(d["logits"]).cuda(),
-                        workspace=ws)
+                        workspace=ws, combine=combine)
     else:
         out = moe.layer(D["x"], D["wg"], D["wu"], D["wd"], k, topk_idx=torch.from_numpy(d["topk_idx"]).cuda(),
-                        topk_w=torch.from_numpy(d["topk_w"]).cuda(), workspace=ws)
+                        topk_w=torch.from_numpy(d["topk_w"]).cuda(), workspace=ws, combine=combine)
     torch.cuda.synchronize()
     return out, ws
 
 
-def _check_layer(d, tokens=None, what=""):
+def _check_layer(d, tokens=None, what="", combine="gather"):
     T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
-    say("layer", what, dict(T=T, H=H, E=E, k=k, I=I))
+    say("layer", what, combine, dict(T=T, H=H, E=E, k=k, I=I))
     D = _inputs_dev(d)
-    out, ws = _run_layer(d, D)
+    out, ws = _run_layer(d, D, combine)
     idx, w = _routing(d)
     # routing and permutation inside the layer: bit-exact
     view = lambda n: moe.workspace_view(ws, T, H, E, k, I, n).cpu().numpy()
@@ -127,3 +127,24 @@ def _sample(T, n, seed=0):
 def test_layer_full_size(name, n):
     d = syn.make_config(name)
     _check_layer(d, tokens=_sample(d["T"], min(n, d["T"] - 2)), what=name)
+
+
+# ---------------------------------------------------------------- weighted-scatter combine
+
+def test_layer_scatter_tiny_every_token():
+    out, _, _ = _check_layer(syn.make_config("tiny"), what="tiny", combine="scatter")
+
+
+def test_layer_scatter_small_shapes_and_gather_agree():
+    for (T, H, E, k, I, seed) in [(300, 128, 6, 2, 192, 1), (130, 64, 1, 1, 128, 3), (40, 512, 3, 3, 256, 4)]:
+        d = syn.make_moe(T, H, E, k, I, seed=seed)
+        out_s, _, D = _check_layer(d, what="scatter small T%d E%d k%d" % (T, E, k), combine="scatter")
+        out_g, _ = _run_layer(d, D, "gather")
+        # the two combines differ only in y's bf16 rounding and the fp32 sum order
+        assert_close(to_f64(out_s), to_f64(out_g), "scatter vs gather", max_frac=1e-2, rel_fro=4e-3)
+
+
+@pytest.mark.parametrize("name,n", [("tp_share", 96), ("ep_skew", 96), ("prefill", 24)])
+def test_layer_scatter_full_size(name, n):
+    d = syn.make_config(name)
+    _check_layer(d, tokens=_sample(d["T"], min(n, d["T"] - 2)), what=name, combine="scatter")
