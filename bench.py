@@ -214,7 +214,7 @@ def bench_dense(a):
     bg = torch.zeros(M // 128, dtype=torch.int32, device="cuda")
     nr = torch.tensor([M], dtype=torch.int32, device="cuda")
     D = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    ws = moe.gemm_workspace()
+    ws = moe.gemm_workspace(M)
 
     def step():
         moe.grouped_gemm(A, B, bg, nr, N=N, K=K, cap=M, b_layout="nk", out=D, workspace=ws)

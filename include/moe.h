@@ -137,15 +137,19 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, const void *x,
  *     a(r) = a_src_row[r] / a_src_div   otherwise (the gate/up GEMM passes
  *                                       row_to_pair and k: the row gather
  *                                       of the reorder-by-route prologue)
- * Rows with a_src_row[r] < 0 are padding: their outputs are unspecified.
+ * Rows with a_src_row[r] < 0 are padding: their outputs are unspecified
+ * (they are not written).
  *   dtype      MOE_BF16 or MOE_FP16 (A, B, B2 and D all of this type, except
  *              D of MOE_EPI_WEIGHTED_SCATTER, which is fp32)
  *   A          [*][K]   (rows addressed by a(r))
  *   B, B2      [G][K][N] (MOE_B_KN) or [G][N][K] (MOE_B_NK); B2 only for
  *              MOE_EPI_SILU_MUL (the up weights; B holds the gate weights)
  *   D          [cap][N] for MOE_EPI_STORE and MOE_EPI_SILU_MUL.
- *   epi_row_pair, pair_w, k   used by MOE_EPI_WEIGHTED_SCATTER only (pass
- *              NULL, NULL, 0 otherwise): the top-k weighted reduction of
+ *   epi_row_pair  optional for MOE_EPI_STORE / MOE_EPI_SILU_MUL: rows r with
+ *              epi_row_pair[r] < 0 are padding and are not written (the MoE
+ *              down GEMM passes row_to_pair).
+ *   epi_row_pair, pair_w, k   MOE_EPI_WEIGHTED_SCATTER (pair_w and k are
+ *              ignored otherwise; pass NULL, 0): the top-k weighted reduction of
  *              [P2 s.4] (MoE layer1 row) done by the epilogue.  Row r with
  *              p = epi_row_pair[r] >= 0 adds pair_w[p] * (A.B)[r] into
  *              D[p / k], an fp32 [T][N] buffer the caller has zeroed; rows
@@ -154,16 +158,17 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, const void *x,
  *              order, so results are reproducible only up to fp32 rounding
  *              order.  MOE_B_KN only.  For the MoE down GEMM:
  *              epi_row_pair = row_to_pair, pair_w = topk_w.
- * Accumulation is fp32 (MFMA); the store epilogues round to nearest even.
+ * Accumulation is fp32 (MFMA), over k in a fixed per-task order (each
+ * column block starts at its own k offset and wraps around); the store
+ * epilogues round to nearest even, so STORE and SILU_MUL results are
+ * deterministic.
+ * Consecutive blocks of one group are computed as 256-row tasks; the pairing
+ * is planned on the device, in the workspace, before the GEMM runs.
  * Requires N % 64 == 0, K % 64 == 0, cap % 128 == 0.
- * workspace (optional, may be NULL): scratch of at least
- * grouped_gemm_workspace_size() bytes, 256-byte aligned, contents need not be
- * initialized.  With it, the tasks of a last, partly filled round are split
- * along K over all workgroups (fp32 partial tiles, summed in K order, so the
- * result is deterministic); without it, every task runs whole.  Results are
- * the same up to the fp32 summation order of the split tasks.
+ * workspace: at least grouped_gemm_workspace_size(cap) bytes, 16-byte
+ * aligned, contents need not be initialized (MOE_ERR_WORKSPACE otherwise).
  * ---------------------------------------------------------------------- */
-size_t grouped_gemm_workspace_size(void);
+size_t grouped_gemm_workspace_size(int cap);
 int grouped_gemm(int dtype, int N, int K, int cap, const void *A,
                  const int32_t *a_src_row, int a_src_div, const void *B,
                  const void *B2, int b_layout, const int32_t *block_group,
@@ -212,7 +217,7 @@ size_t moe_layer_workspace_size(int T, int H, int E, int k, int I);
  *   4 pair_to_row [T*k] int32   5 row_to_pair [cap] int32
  *   6 block_expert [cap/128]    7 num_padded_rows [1] int32
  *   8 h [cap][I] bf16           9 y [cap][H] bf16
- *  10 permute scratch          11 grouped-GEMM scratch
+ *  10 permute scratch          11 grouped-GEMM row-task plan
  *  12 out_acc [T][H] fp32 (MOE_COMBINE_SCATTER only)
  *  13 total size
  * Returns MOE_OK or MOE_ERR_INVALID. */

@@ -66,7 +66,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "moe_route": ([P, I, I, I, P, P, P], I),
             "moe_permute_workspace_size": ([I, I, I], Z),
             "moe_permute": ([P, I, I, I, P, I, P, P, P, P, P, P, P, I, P, Z, P], I),
-            "grouped_gemm_workspace_size": ([], Z),
+            "grouped_gemm_workspace_size": ([I], Z),
             "grouped_gemm": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P, I, P, P, Z, P], I),
             "moe_combine": ([P, I, P, P, I, I, P, P], I),
             "moe_finalize": ([P, Z, P, P], I),
@@ -180,17 +180,21 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
                  B2: torch.Tensor | None = None, b_layout: str = "kn", epilogue: str = "store",
                  row_pair: torch.Tensor | None = None, pair_w: torch.Tensor | None = None,
                  T: int | None = None, out: torch.Tensor | None = None,
-                 workspace: torch.Tensor | None = None, split_tail: bool = True) -> torch.Tensor:
+                 workspace: torch.Tensor | None = None) -> torch.Tensor:
     """D[r] = A[a(r)] . B[block_group[r // 128]] for r < min(num_rows, cap),
     or SiLU(A.B) * (A.B2) with epilogue="silu_mul".  Returns D [cap, N].
+
+    With row_pair given and epilogue "store" or "silu_mul", rows r with
+    row_pair[r] < 0 are padding and are not written (nor are rows whose
+    a_src_row entry is negative).
 
     epilogue="weighted_scatter": row r with p = row_pair[r] >= 0 adds
     pair_w[p] * (A.B)[r] into the fp32 row p // k of D [T, N] (k = pair_w's
     second dimension); D is zero-filled here unless `out` is given, in which
     case it is accumulated into.
 
-    With split_tail, a scratch workspace lets the last partly filled round of
-    tasks be split along K (allocated here if not given)."""
+    `workspace` holds the device-built row-task plan (grouped_gemm_workspace_size(cap)
+    bytes; allocated here if not given)."""
     _need(A, "A", (torch.bfloat16, torch.float16))
     _need(B, "B", A.dtype)
     _need(block_group, "block_group", torch.int32)
@@ -200,6 +204,8 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
     if a_src_row is not None:
         _need(a_src_row, "a_src_row", torch.int32)
     k = 0
+    if row_pair is not None:
+        _need(row_pair, "row_pair", torch.int32)
     if epilogue == "weighted_scatter":
         _need(row_pair, "row_pair", torch.int32)
         _need(pair_w, "pair_w", torch.float32, 2)
@@ -217,10 +223,8 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
     else:
         _need(out, "out", A.dtype)
     lib = load_library()
-    if split_tail and workspace is None:
-        workspace = gemm_workspace(A.device)
-    if not split_tail:
-        workspace = None
+    if workspace is None:
+        workspace = gemm_workspace(cap, A.device)
     _check("grouped_gemm", lib.grouped_gemm(
         _DTYPES[A.dtype], N, K, cap, _ptr(A), _ptr(a_src_row), a_src_div, _ptr(B), _ptr(B2),
         _LAYOUTS[b_layout], _ptr(block_group), _ptr(num_rows), _EPIS[epilogue], _ptr(row_pair),
@@ -232,13 +236,16 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
 _gemm_ws = {}
 
 
-def gemm_workspace(device="cuda") -> torch.Tensor:
-    """A cached scratch buffer of grouped_gemm_workspace_size() bytes per device."""
+def gemm_workspace(cap: int, device="cuda") -> torch.Tensor:
+    """A scratch buffer of grouped_gemm_workspace_size(cap) bytes, cached per
+    device and grown on demand.  Calls on one stream may share it; calls that
+    may overlap on different streams need workspaces of their own."""
     dev = torch.device(device)
     key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    need = load_library().grouped_gemm_workspace_size(cap)
     ws = _gemm_ws.get(key)
-    if ws is None:
-        ws = torch.empty(load_library().grouped_gemm_workspace_size(), dtype=torch.uint8, device=dev)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         _gemm_ws[key] = ws
     return ws
 

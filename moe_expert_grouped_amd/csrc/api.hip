@@ -12,11 +12,11 @@ size_t permute_workspace_bytes(long R, int E);
 hipError_t launch_permute(const int32_t *, int, int, int, const uint16_t *, int, int32_t *,
                           int32_t *, int32_t *, int32_t *, int32_t *, int32_t *, uint16_t *, int,
                           void *, hipStream_t);
-hipError_t launch_grouped_gemm(int, int, int, int, const uint16_t *, const int32_t *, int,
-                               const uint16_t *, const uint16_t *, int, const int32_t *,
-                               const int32_t *, int, const int32_t *, const float *, int, void *,
-                               void *, size_t, int, hipStream_t);
-size_t gg_workspace_bytes(int grid);
+hipError_t launch_grouped_gemm(int, int, int, const uint16_t *, const int32_t *, int,
+                               const uint16_t *, const uint16_t *, int, const int32_t *, int,
+                               const int32_t *, const float *, int, void *, int, hipStream_t);
+hipError_t launch_gg_plan(const int32_t *, const int32_t *, int, int32_t *, hipStream_t);
+size_t gg_plan_bytes(int cap);
 hipError_t launch_combine(const uint16_t *, int, const int32_t *, const float *, int, int,
                           uint16_t *, hipStream_t);
 hipError_t launch_finalize(const float *, long, uint16_t *, hipStream_t);
@@ -120,9 +120,9 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, const void *x, int
       block_expert, num_padded_rows, (uint16_t *)x_perm, cap, workspace, (hipStream_t)stream));
 }
 
-size_t grouped_gemm_workspace_size(void) {
-  const int cus = device_cus();
-  return align256(moe::gg_workspace_bytes(cus > 0 ? cus : kDefaultCus));
+size_t grouped_gemm_workspace_size(int cap) {
+  if (cap <= 0) return 0;
+  return align256(moe::gg_plan_bytes(cap));
 }
 
 int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t *a_src_row,
@@ -148,12 +148,16 @@ int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t 
   if (N % 64 != 0 || K % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (cap % MOE_ROW_BLOCK != 0) return MOE_ERR_INVALID;
   if (workspace && !aligned16(workspace)) return MOE_ERR_INVALID;
+  if (!workspace || ws_bytes < grouped_gemm_workspace_size(cap)) return MOE_ERR_WORKSPACE;
   const int cus = device_cus();
   if (cus == 0) return MOE_ERR_DEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t *plan = (int32_t *)workspace;
+  if (moe::launch_gg_plan(block_group, num_rows, cap, plan, s) != hipSuccess)
+    return MOE_ERR_DEVICE;
   return launch_status(moe::launch_grouped_gemm(
-      dtype, N, K, cap, (const uint16_t *)A, a_src_row, a_src_div, (const uint16_t *)B,
-      (const uint16_t *)B2, b_layout, block_group, num_rows, epilogue, epi_row_pair, pair_w, k,
-      D, workspace, workspace ? ws_bytes : 0, cus, (hipStream_t)stream));
+      dtype, N, K, (const uint16_t *)A, a_src_row, a_src_div, (const uint16_t *)B,
+      (const uint16_t *)B2, b_layout, plan, epilogue, epi_row_pair, pair_w, k, D, cus, s));
 }
 
 int moe_combine(const void *y, int H, const int32_t *pair_to_row, const float *topk_w, int T,
@@ -196,7 +200,7 @@ int moe_layer_workspace_layout(int T, int H, int E, int k, int I, size_t off[14]
   take(8, (size_t)cap * I * 2);
   take(9, (size_t)cap * H * 2);
   take(10, moe::permute_workspace_bytes(R, E));
-  take(11, grouped_gemm_workspace_size());
+  take(11, grouped_gemm_workspace_size((int)cap));
   take(12, (size_t)T * H * 4);
   off[13] = o;
   return MOE_OK;
@@ -249,8 +253,7 @@ int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
   uint16_t *h = (uint16_t *)(ws + off[8]);
   uint16_t *y = (uint16_t *)(ws + off[9]);
   void *pws = ws + off[10];
-  void *gws = ws + off[11];
-  const size_t gws_bytes = off[12] - off[11];
+  int32_t *plan = (int32_t *)(ws + off[11]);
   float *oacc = (float *)(ws + off[12]);
   const int cap = (int)padded_cap(T, k, E);
 
@@ -266,23 +269,25 @@ int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
   e = moe::launch_permute(ridx, T, k, E, nullptr, 0, counts, offsets, p2r, r2p, bexp, mpad,
                           nullptr, cap, pws, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
-  e = moe::launch_grouped_gemm(MOE_BF16, I, H, cap, (const uint16_t *)x, r2p, k,
-                               (const uint16_t *)w_gate, (const uint16_t *)w_up, MOE_B_KN, bexp,
-                               mpad, MOE_EPI_SILU_MUL, nullptr, nullptr, 0, h, gws, gws_bytes,
-                               cus, s);
+  // one row-task plan serves both GEMMs (they share the block experts)
+  e = moe::launch_gg_plan(bexp, mpad, cap, plan, s);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  e = moe::launch_grouped_gemm(MOE_BF16, I, H, (const uint16_t *)x, r2p, k,
+                               (const uint16_t *)w_gate, (const uint16_t *)w_up, MOE_B_KN, plan,
+                               MOE_EPI_SILU_MUL, nullptr, nullptr, 0, h, cus, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   if (combine == MOE_COMBINE_SCATTER) {
     e = moe::launch_zero(oacc, (long)T * H, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
-    e = moe::launch_grouped_gemm(MOE_BF16, H, I, cap, h, nullptr, 1, (const uint16_t *)w_down,
-                                 nullptr, MOE_B_KN, bexp, mpad, MOE_EPI_WEIGHTED_SCATTER, r2p, rw,
-                                 k, oacc, gws, gws_bytes, cus, s);
+    e = moe::launch_grouped_gemm(MOE_BF16, H, I, h, nullptr, 1, (const uint16_t *)w_down,
+                                 nullptr, MOE_B_KN, plan, MOE_EPI_WEIGHTED_SCATTER, r2p, rw, k,
+                                 oacc, cus, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     return launch_status(moe::launch_finalize(oacc, (long)T * H, (uint16_t *)out, s));
   }
-  e = moe::launch_grouped_gemm(MOE_BF16, H, I, cap, h, nullptr, 1, (const uint16_t *)w_down,
-                               nullptr, MOE_B_KN, bexp, mpad, MOE_EPI_STORE, nullptr, nullptr, 0,
-                               y, gws, gws_bytes, cus, s);
+  // padding rows of y are never read: the down GEMM skips their stores
+  e = moe::launch_grouped_gemm(MOE_BF16, H, I, h, nullptr, 1, (const uint16_t *)w_down, nullptr,
+                               MOE_B_KN, plan, MOE_EPI_STORE, r2p, nullptr, 0, y, cus, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   e = moe::launch_combine(y, H, p2r, rw, T, k, (uint16_t *)out, s);
   return launch_status(e);

@@ -15,28 +15,41 @@
 // times its product into the fp32 row of its token.
 //
 // How (the pages' SM120 template -- TMA producer warp, mbarrier ring, 8
-// consumer warps -- is prior art; this is the CDNA4 form of the same ideas):
-//   * persistent grid of one 256-thread workgroup (4 wavefronts) per CU;
-//     tasks are (row block, column block) pairs, row-block-major, counted
-//     from the device-resident padded row count so the host never waits;
-//   * the task list is cut into 8 contiguous ranges, one per XCD (workgroup
-//     w runs on XCD w % 8), so the row blocks of one expert -- which share
-//     its weight tiles -- run side by side on one XCD and meet in its L2;
-//   * every workgroup streams its tasks' 64-deep K slices through an
-//     NSTAGE-deep ring of LDS stages with direct global->LDS DMA
-//     (global_load_lds_dwordx4): no registers are spent on staging and the
-//     ring keeps NSTAGE-1 slices in flight, across task boundaries too;
-//     completion is tracked per wavefront with s_waitcnt vmcnt and made
-//     visible to the workgroup with one s_barrier per slice (the roles of
-//     the pages' "arrived"/"finished" barriers);
+// consumer warps, 128-row tasks -- is prior art; this is the CDNA4 form):
+//   * a task is one or two 128-row blocks of the SAME group (a "row task",
+//     up to 256 rows) times one BN-column block: the weight tile is streamed
+//     once for up to 256 rows, halving weight traffic per row against
+//     128-row tasks.  A plan kernel pairs consecutive blocks of each group
+//     (gg_plan_kernel) so the task list is dense;
+//   * persistent grid of one 256-thread workgroup (4 wavefronts, one per
+//     SIMD) per CU; the task list is cut into 8 contiguous ranges, one per
+//     XCD (workgroup w runs on XCD w % 8), so the column tasks of one row
+//     task share its A rows in that XCD's L2;
+//   * 32-deep K slices stream through LDS rings with direct global->LDS DMA
+//     (global_load_lds_dwordx4), no registers spent on staging: a shallow
+//     ring for A tiles (mostly L2 hits) and a deeper one for the weight
+//     tiles (HBM, whose latency under load needs ~80 KiB in flight per CU),
+//     both running across task boundaries;
+//   * the kernel body issues no ordinary global load: the per-task plan
+//     entry, the A-row and epilogue index tables and the scatter weights are
+//     DMA'd into small LDS rings one or two tasks ahead, so every wait is an
+//     explicit s_waitcnt vmcnt(n) on DMA that completes in issue order, and
+//     no compiler-inserted vmcnt(0) ever drains the ring;
+//   * one s_barrier per slice publishes the slice to the workgroup and
+//     frees the oldest stage (the roles of the pages' arrived / finished
+//     barriers); fragment reads of the next k step are issued before the
+//     matrix instructions of the current one, across slice boundaries too;
 //   * LDS rows are XOR-swizzled in 16-byte granules by permuting the source
 //     address each lane fetches (the DMA writes lane-contiguously);
 //   * A tiles (and B tiles stored [N][K]) are read with ds_read_b128; weight
-//     tiles stored [K][N] are read with the gfx950 transpose read
-//     ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one
-//     column -- exactly the MFMA B-operand layout;
-//   * v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulators in registers; each
-//     wavefront owns a 64 x (BN/2) quarter of the 128 x BN tile.
+//     tiles stored [K][N] with the gfx950 transpose read ds_read_b64_tr_b16,
+//     which hands each lane 4 consecutive k of one column -- the MFMA B
+//     operand layout;
+//   * v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulators; wavefront (wm, wn)
+//     owns rows [128 wm, 128 wm + 128) and columns [BN/2 wn, BN/2 wn + BN/2)
+//     of each B matrix.  A one-block task loads its 128 rows twice; the
+//     second copy's products are not stored (they hide under the weight
+//     stream in the HBM-bound shapes, and keep one fixed register layout).
 #pragma once
 #include <stdio.h>
 #include <stdlib.h>
@@ -45,51 +58,60 @@
 
 namespace moe {
 
-constexpr int kBM = 128;
-constexpr int kBK = 64;
-
-// Wavefront layout of a workgroup: WAVES = 4 (one per SIMD, a 2 x 2 grid of
-// 64 x BN/2 wave tiles) or 8 (two per SIMD, so one wavefront's LDS and DMA
-// waits hide behind the other's MFMAs: a 2 x 4 grid of 64 x BN/4 wave tiles,
-// or 4 x 2 of 32 x BN/2 when BN = 64).
-template <int BN, int WAVES> struct WaveGrid {
-  static constexpr int kThreads = 64 * WAVES;
-  static constexpr int WMR = WAVES == 4 ? 2 : (BN >= 128 ? 2 : 4); // wave rows
-  static constexpr int WNC = WAVES / WMR;                          // wave columns
-  static constexpr int WR = kBM / WMR;                             // rows per wave
-  static constexpr int WC = BN / WNC;                              // columns per wave (per matrix)
-  static constexpr int MI = WR / 32;
-  static constexpr int NI = WC / 32;
-  static_assert(WC >= 32 && WR >= 32, "wave tile");
-};
-
-struct GGArgs {
-  const uint16_t *A;
-  const int32_t *a_src_row;
-  int a_src_div;
-  const uint16_t *B;
-  const uint16_t *B2;
-  const int32_t *block_group;
-  const int32_t *num_rows;
-  uint16_t *D;
-  int N, K, cap;
-  int group_rows;  // row blocks per super-block of the task order (>= 1)
-  float *partials; // partial tiles of a split tail (NULL: no split)
-  // weighted scatter only: row r adds pair_w[p] * product into Dacc[p / topk]
-  // (p = epi_row_pair[r], skipped when negative)
-  float *Dacc;
-  const int32_t *epi_row_pair;
-  const float *pair_w;
-  int topk;
-};
+constexpr int kBM = 128;     // rows per block: alignment unit and plan granule
+constexpr int kTM = 256;     // rows per task: one or two blocks of one group
+constexpr int kWaves = 4;    // wavefronts per workgroup, one per SIMD
+constexpr int kThreads = 64 * kWaves;
+// Ring slots of the per-task tables.  The tables of task i are fetched when
+// the B stream starts task i-1 and read until task i's epilogue; those of
+// task i+4 (same slot) are fetched when the B stream -- NBR-1 slices ahead
+// of the consumer -- starts task i+3, which it reaches after task i's
+// epilogue as long as 2 KT >= NBR - 1 (KT slices per task; the host only
+// picks ring depths that satisfy this).  Plan entries are fetched two tasks
+// ahead of the B stream into a ring of 8, and read at the start of each
+// task, before the slot can be refetched.
+constexpr int kTabSlots = 4;
+constexpr int kPlanSlots = 8;
 
 // Epilogues: plain store, SiLU(gate) * up of two B matrices, weighted scatter.
 enum { kEpiStore = 0, kEpiSiluMul = 1, kEpiScatter = 2 };
 
-// 16-byte-granule XOR swizzle of a tile stored with 128-byte rows (A tiles,
-// [N][K] B tiles).  Conflict-free ds_read_b128 of 16 consecutive rows at one
-// logical granule for both 32- and 64-bank LDS views.
+// Plan of row tasks, built on the device from block_group and the padded
+// row count: plan[0] = number of row tasks, plan[1] = number of blocks, then
+// per row task i:  plan[2 + 2 i] = first block | (blocks - 1) << 30,
+//                  plan[3 + 2 i] = group.
+constexpr int kPlanHead = 2;
+constexpr int kPlanTwo = 1 << 30;
+inline size_t plan_ints(int cap) { return kPlanHead + 2 * (size_t)(cap / kBM); }
+
+struct GGArgs {
+  const uint16_t *A;
+  const int32_t *a_src_row; // A row of output row r: a_src_row[r] / a_src_div (NULL: r)
+  int a_src_div;
+  const uint16_t *B;
+  const uint16_t *B2;
+  const int32_t *plan;
+  uint16_t *D;                 // STORE / SILU_MUL output [cap][N]
+  float *Dacc;                 // WEIGHTED_SCATTER output [T][N] (fp32, accumulated into)
+  const int32_t *epi_row_pair; // scatter: pair of each row; store: rows with p < 0 are skipped
+  const float *pair_w;         // scatter: weight of each pair
+  int topk;                    // scatter: token of pair p is p / topk
+  int N, K;
+  int group_rows; // row tasks per super-block of the task order (>= 1)
+};
+
+// 16-byte-granule XOR swizzles of tiles stored with 64- or 128-byte rows
+// (A tiles and [N][K] B tiles: BK = 32 or 64 k of one row).  Both make the
+// ds_read_b128 of 16 consecutive rows at one logical granule conflict-free,
+// for 64 banks (16 lanes per cycle) and for 32 banks (8 lanes per cycle).
+__device__ __forceinline__ int swz64(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
 __device__ __forceinline__ int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+template <int BK> __device__ __forceinline__ int swz_rows(int r) {
+  if constexpr (BK == 64)
+    return swz128(r);
+  else
+    return swz64(r);
+}
 
 // Swizzle of a [K][N] weight tile with BN columns (rows of 2*BN bytes), read
 // with ds_read_b64_tr_b16: one 16-lane group reads 4 consecutive k rows x 32
@@ -106,10 +128,17 @@ template <int BN> __device__ __forceinline__ int swz_kn(int k) {
 // them: lane i of the wavefront writes bytes [16 i, 16 i + 16) (or [4 i, 4 i
 // + 4) for the dword form) after the wave-uniform LDS byte address in M0
 // (one wait state between the M0 write and its use).  Completion is awaited
-// explicitly with wait_vmcnt.
+// explicitly with wait_vmcnt; loads complete in issue order.
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
                "s"(lds_addr)
+               : "memory", "m0");
+}
+// The same with a wave-uniform 64-bit base (SGPR pair) and a 32-bit per-lane
+// byte offset: the per-lane state is one register instead of a pointer.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void *sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(sbase), "s"(lds_addr)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void *g, uint32_t lds_addr) {
@@ -125,7 +154,10 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-
+// LDS wait through the builtin, so the compiler's own wait insertion knows
+// the reads issued before it have completed (encoding: vmcnt and expcnt at
+// their maximum, lgkmcnt 0)
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <bool FP16>
@@ -142,86 +174,43 @@ __device__ __forceinline__ f32x16 mfma32(const i16x4 a0, const i16x4 a1, const i
                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------------------
-// Work schedule, shared by the GEMM kernel and the fixup kernel.
-//
-// Tasks (row block, column block) are cut into nx contiguous ranges, one per
-// XCD (workgroup w runs on XCD w % nx); the S workgroups of an XCD take its
-// tasks round-robin.  When the last round would be mostly empty (the XCD
-// has rem = ntx mod S leftover tasks, rem <= 3/4 S) and a partial-tile buffer
-// is given, those rem tasks are not handed out whole: their rem * KT
-// k-slices are split evenly over the S workgroups (a stream-K tail).  A
-// workgroup then owns at most two tail segments; a segment that covers a
-// whole task is finished in place, the others store fp32 partial tiles that
-// the fixup kernel sums in k order.
-struct Sched {
-  int nx, xcd, slot, S, KT, ncol, nblk;
-  int tx0, full, rem; // first task of this XCD, tasks handed out whole, tail tasks
-  long U;             // tail k-slices
-
-  __device__ void init(const GGArgs &a, int bn, int grid, int block) {
-    KT = a.K / kBK;
-    const int mrows = max(0, min(a.num_rows[0], a.cap));
-    nblk = mrows / kBM;
-    ncol = a.N / bn;
-    const int ntask = nblk * ncol;
-    nx = (grid % 8 == 0) ? 8 : 1;
-    xcd = block % nx;
-    slot = block / nx;
-    S = grid / nx;
-    tx0 = (int)(((long)ntask * xcd) / nx);
-    const int ntx = (int)(((long)ntask * (xcd + 1)) / nx) - tx0;
-    full = ntx / S * S;
-    rem = ntx - full;
-    if (!a.partials || rem == 0 || rem * 4 > S * 3) {
-      full = ntx;
-      rem = 0;
-    }
-    U = (long)rem * KT;
-  }
-  __device__ int bound(int s) const { return (int)(U * s / S); }
-  // tasks this workgroup receives whole
-  __device__ int n_full() const { return full > slot ? (full - slot + S - 1) / S : 0; }
-  // tail segments of slot s: [bound(s), bound(s+1)) in tail k-slices
-  __device__ int n_tail(int s) const {
-    const int r0 = bound(s), r1 = bound(s + 1);
-    return r1 > r0 ? (r1 - 1) / KT - r0 / KT + 1 : 0;
-  }
-  // item i of this workgroup: task, k-slice range [ka, kb), tail task index or -1
-  __device__ void item(int i, int &task, int &ka, int &kb, int &tt) const {
-    const int nf = n_full();
-    if (i < nf) {
-      task = tx0 + slot + i * S;
-      ka = 0;
-      kb = KT;
-      tt = -1;
-    } else {
-      const int r0 = bound(slot), r1 = bound(slot + 1);
-      tt = r0 / KT + (i - nf);
-      task = tx0 + full + tt;
-      ka = max(r0, tt * KT) - tt * KT;
-      kb = min(r1, (tt + 1) * KT) - tt * KT;
-    }
-  }
-};
-
-// Partial tile of one tail segment: ACC floats per thread, stored as
-// [ACC/4][threads][4] so each store and load is one coalesced 16-byte access
-// per lane.  Buffer (xcd, slot, j) holds the j-th tail segment (j < 2) of
-// that workgroup.
-__device__ __forceinline__ float *partial_tile(float *base, const Sched &sc, int s, int j,
-                                               int acc_per_thread, int threads) {
-  return base + ((size_t)(sc.xcd * sc.S + s) * 2 + j) * (size_t)acc_per_thread * threads;
+// Reads one accumulator out of its AGPR where the epilogue needs it.  Plain
+// C++ uses make the compiler copy every accumulator into VGPRs at once after
+// the k loop (hundreds of registers at the register peak); an asm operand
+// constrained to an AGPR keeps them there until each piece is stored.
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
 }
 
-// Epilogue of one 128 x BN output tile: every 32x32 accumulator tile goes,
-// 16 rows at a time, through a per-wavefront LDS tile so that each lane
-// writes one 16-byte row piece (the MFMA layout gives each lane one column
-// of 4-row groups; registers 0-7 hold rows 0-15, registers 8-15 rows 16-31).
+// Task order: super-blocks of `GR` row tasks; inside one, the column block
+// varies slowest, so the row tasks of a super-block (mostly one group) read
+// each weight tile at about the same time and share it in L2, while with
+// GR = 1 the column tasks of one row task run side by side and share its A
+// rows.
+__device__ __forceinline__ void task_coords(int task, int GR, int ncol, int nrt, int bn, int &rt,
+                                            int &n0) {
+  const int span = GR * ncol;
+  const int sb = task / span;
+  const int r = task - sb * span;
+  const int rows = min(GR, nrt - sb * GR);
+  const int n = r / rows;
+  rt = sb * GR + (r - n * rows);
+  n0 = n * bn;
+}
+
+// Epilogue of one wavefront's share of a tile for STORE and SILU_MUL: every
+// 32 x 32 accumulator tile goes, 16 rows at a time, through a per-wavefront
+// LDS tile so that each lane writes one 16-byte row piece (the MFMA layout
+// gives each lane one column of 4-row groups; registers 0-7 hold rows 0-15,
+// registers 8-15 rows 16-31).  Rows whose entry in `skip` (the task's pair
+// table, if any) is negative are padding and are not written.
 constexpr int kEpiLd = 40; // row pitch (elements) of the staging tile
 template <int NB, bool FP16, int MI, int NI>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint16_t *Dt, int N,
-                                           MOE_LDS uint16_t *stg, int lane, int row0,
+                                           MOE_LDS uint16_t *stg,
+                                           const MOE_LDS int32_t *skip, int lane, int row0,
                                            int col0) {
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -232,445 +221,484 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint
 #pragma unroll
         for (int r = 8 * h; r < 8 * h + 8; ++r) {
           const int row = 8 * ((r >> 2) & 1) + 4 * (lane >> 5) + (r & 3);
-          float v = acc[0][i][j][r];
+          float v = acc_read(acc[0][i][j][r]);
           if constexpr (NB == 2) {
-            const float u = acc[1][i][j][r];
+            const float u = acc_read(acc[1][i][j][r]);
             v = v / (1.0f + __expf(-v)) * u;
           }
           stg[row * kEpiLd + (lane & 31)] = FP16 ? f32_to_f16(v) : f32_to_bf16(v);
         }
         const int row = lane >> 2;
         const int col = (lane & 3) * 8;
+        const int trow = row0 + i * 32 + 16 * h + row; // row inside the task
         const u32x4 q = *(const MOE_LDS u32x4 *)(stg + row * kEpiLd + col);
-        uint16_t *dst = Dt + (size_t)(row0 + i * 32 + 16 * h + row) * N + col0 + j * 32 + col;
-        *reinterpret_cast<u32x4 *>(dst) = q;
+        // byte offset inside the task's tile (< 2^32): the address is the
+        // wave-uniform tile base plus one 32-bit register
+        const uint32_t off = (uint32_t)((trow * N + col0 + j * 32 + col) * 2);
+        if (!skip || skip[trow] >= 0)
+          *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(Dt) + off) = q;
+        // one 16-row piece at a time: unrolled freely, the scheduler would
+        // overlap all of them and hold ~100 registers of temporaries
+        __builtin_amdgcn_sched_barrier(0);
       }
 }
 
-// Weighted-scatter epilogue of one wavefront's share of a tile: row r adds
-// w_p * acc into the fp32 token row p / k of Dacc, p = row_pair[r] (padding
-// rows, p < 0, add nothing).  Lane l fetches the pair of wavefront row l
-// once; each accumulator register then takes its row's destination and
-// weight from that lane (ds_bpermute).  The adds are fp32 atomics at device
-// scope, so the sum over a token's k rows is order-free (not bit-stable).
+// Weighted-scatter epilogue of one wavefront's share of a tile: task row r
+// adds w_r * acc into the fp32 token row p_r / k of Dacc, with the pair p_r
+// and its weight w_r taken from the task's LDS tables (padding rows, p < 0,
+// add nothing).  fp32 device-scope atomics: the k contributions of a token
+// meet in no fixed order.
 template <int MI, int NI>
 __device__ __forceinline__ void scatter_tile(const f32x16 (&acc)[1][MI][NI], float *Dacc, int N,
-                                             const int32_t *row_pair, const float *pair_w,
-                                             int k, int lane, int col) {
-  int dst = -1;
-  float wt = 0.0f;
-  if (lane < MI * 32) {
-    const int p = row_pair[lane];
-    if (p >= 0) {
-      dst = p / k;
-      wt = pair_w[p];
-    }
-  }
+                                             const MOE_LDS int32_t *ptab,
+                                             const MOE_LDS float *wtab, int k, int lane, int row0,
+                                             int col) {
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int rl = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const int d = __shfl(dst, rl);
-      const float w = __shfl(wt, rl);
-      if (d >= 0) {
-        float *o = Dacc + (size_t)d * N + col + (lane & 31);
+      const int tr = row0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int p = ptab[tr];
+      if (p >= 0) {
+        const float w = wtab[tr];
+        float *o = Dacc + (size_t)(p / k) * N + col + (lane & 31);
 #pragma unroll
-        for (int j = 0; j < NI; ++j) unsafeAtomicAdd(o + j * 32, w * acc[0][i][j][r]);
+        for (int j = 0; j < NI; ++j) unsafeAtomicAdd(o + j * 32, w * acc_read(acc[0][i][j][r]));
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// Task order inside the whole-task phase: super-blocks of `group_rows` row
-// blocks; inside one, the column block varies slowest, so the row blocks of
-// a super-block (mostly one expert) read each weight tile at about the same
-// time and share it in L2, while a row block's A tile is reused by its
-// column tasks.
-__device__ __forceinline__ void task_coords(int task, int GR, int ncol, int nblk, int bn, int &b,
-                                            int &n0) {
-  const int span = GR * ncol;
-  const int sb = task / span;
-  const int r = task - sb * span;
-  const int rows = min(GR, nblk - sb * GR);
-  const int n = r / rows;
-  b = sb * GR + (r - n * rows);
-  n0 = n * bn;
-}
-
-// BN: output columns per task (per B matrix); EPI: kEpiStore, kEpiSiluMul
-// (two B matrices) or kEpiScatter; KN: B stored [K][N] (else [N][K]);
-// NSTAGE: LDS ring depth; WAVES: 4 or 8.
-template <int BN, int EPI, bool KN, bool FP16, int NSTAGE, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 1) void grouped_gemm_kernel(GGArgs args) {
+// BN: output columns per task (per B matrix); BK: k per slice (32 or 64:
+// A rows of 64 or 128 bytes per slice); EPI: kEpiStore, kEpiSiluMul (two B
+// matrices) or kEpiScatter; KN: B stored [K][N] (else [N][K]); NA, NBR:
+// depths of the A ring and of the B ring.
+//
+// Two rings: the B (weight) ring is deeper than the A ring.  Weights stream
+// from HBM, whose latency under full load is several microseconds, so each
+// CU needs most of its in-flight bytes to be weights; A tiles mostly hit in
+// L2 and need a shorter lead.  At consumer slice c the wavefront issues A
+// slice c + NA - 1 and then B slice c + NBR - 1 (each into the slot its
+// ring freed at the previous barrier), so the B stream runs NBR - NA
+// slices further ahead and may already be on a later task than the A
+// stream; each stream keeps its own task cursor.
+template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) {
   constexpr int NB = EPI == kEpiSiluMul ? 2 : 1; // B matrices
-  using WG = WaveGrid<BN, WAVES>;
-  constexpr int NT = WG::kThreads;
-  constexpr int A_BYTES = kBM * kBK * 2;
-  constexpr int B_BYTES = kBK * BN * 2;
-  constexpr int STAGE_BYTES = A_BYTES + NB * B_BYTES;
-  constexpr int MI = WG::MI;       // 32-high MFMA tiles per wavefront
-  constexpr int NI = WG::NI;       // 32-wide MFMA tiles per wavefront per matrix
-  constexpr int A_INSTR = 16 / WAVES;         // DMA instructions per wavefront per A slice
-  constexpr int B_INSTR = BN / (8 * WAVES);   // per wavefront per B matrix per slice
-  constexpr int LOADS = A_INSTR + NB * B_INSTR; // DMA ops per wavefront per slice
-  constexpr int ROWS_PW = 8 * A_INSTR;        // A rows each wavefront loads
-  constexpr int IDX_SLOTS = 4;     // per-wavefront ring of task index tables
-  constexpr int IDX_WORDS = 40;    // words per table: source rows, the group at word 32
-  constexpr int ACC = NB * MI * NI * 16; // accumulator floats per thread
-  static_assert(B_INSTR >= 1 && ROWS_PW <= 32, "DMA split");
-  static_assert(LOADS * (NSTAGE - 2) < 64, "vmcnt range");
-  static_assert(NSTAGE >= 2 && NSTAGE <= IDX_SLOTS, "ring depth");
+  constexpr int ARP = BK * 2;                    // bytes per A row (and [N][K] B row) per slice
+  constexpr int A_BYTES = kTM * ARP;             // one A stage
+  constexpr int B_BYTES = BK * BN * 2;           // one B matrix of one B stage
+  constexpr int BS_BYTES = NB * B_BYTES;         // one B stage
+  constexpr int A_INSTR = A_BYTES / 1024 / kWaves;    // DMA instructions per wavefront per A slice
+  constexpr int B_INSTR = B_BYTES / 1024 / kWaves;    // per B matrix per B slice
+  constexpr int A_LOADS = A_INSTR;
+  constexpr int B_LOADS = NB * B_INSTR;
+  constexpr int LA = NA - 1;                          // A issue lead (slices)
+  constexpr int LB = NBR - 1;                         // B issue lead (slices)
+  // DMA instructions issued, by the end of slice c, after the later of A
+  // slice c+1 and B slice c+1.  A slice c+1 is issued at step c+1-LA,
+  // followed in that step by B slice c+1-LA+LB; with LB > LA, B slice c+1
+  // came in an earlier step, so A slice c+1 is the later one and the B
+  // slice of its step plus LA-1 whole steps follow it; with LB == LA, B
+  // slice c+1 itself is the later one and only the LA-1 whole steps follow.
+  constexpr int AFTER = (LB > LA ? B_LOADS : 0) + (LA - 1) * (A_LOADS + B_LOADS);
+  constexpr int A_RPI = 1024 / ARP;                   // A rows per DMA instruction
+  constexpr int A_GPR = ARP / 16;                     // 16-byte granules per A row
+  constexpr int WC = BN / 2;                          // columns per wavefront per matrix
+  constexpr int NI = WC / 32;
+  constexpr int KSTEPS = BK / 16;
+  constexpr bool SCAT = EPI == kEpiScatter;
+  static_assert(BK == 32 || BK == 64, "slice depth");
+  static_assert(B_INSTR >= 1 && A_INSTR * A_RPI * kWaves == kTM, "DMA split");
+  static_assert(NA >= 2 && NBR >= NA, "ring depths");
+  static_assert(LA * A_LOADS + LB * B_LOADS < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) int32_t idx_lds[WAVES][IDX_SLOTS][IDX_WORDS];
-  __shared__ __attribute__((aligned(16))) uint16_t epi_lds[WAVES][16 * kEpiLd];
+  __shared__ __attribute__((aligned(1024))) unsigned char aring[NA * A_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char bring[NBR * BS_BYTES];
+  // tab: the task's pair per row -- the A source pairs if A rows are
+  // gathered, else the epilogue pairs; etab: scatter only, the epilogue pairs
+  // when they differ from the A source pairs; wtab: scatter only, the weights
+  __shared__ __attribute__((aligned(16))) int32_t tab[kTabSlots][kTM];
+  __shared__ __attribute__((aligned(16))) int32_t etab[SCAT ? kTabSlots : 1][SCAT ? kTM : 1];
+  __shared__ __attribute__((aligned(16))) float wtab[SCAT ? kTabSlots : 1][SCAT ? kTM : 1];
+  __shared__ __attribute__((aligned(16))) int32_t ptab[kWaves][kPlanSlots][2]; // plan entries
+  __shared__ __attribute__((aligned(16))) uint16_t epi_lds[SCAT ? 1 : kWaves][SCAT ? 1 : 16 * kEpiLd];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WG::WNC;
-  const int wn = wave % WG::WNC;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
   const int N = args.N, K = args.K;
+  const int KT = K / BK;
+  const bool has_a = args.a_src_row != nullptr;
+  // the pair table `tab` holds a_src_row if given, else epi_row_pair; the
+  // scatter's own epilogue table is needed only when both differ
+  const int32_t *tab_src = has_a ? args.a_src_row : args.epi_row_pair;
+  const bool has_tab = tab_src != nullptr;
+  const bool own_e = SCAT && has_a && args.epi_row_pair != args.a_src_row;
 
-  Sched sc;
-  sc.init(args, BN, gridDim.x, blockIdx.x);
-  const int KT = sc.KT, ncol = sc.ncol, nblk = sc.nblk;
-  const int n_items = sc.n_full() + sc.n_tail(sc.slot);
-  auto coords = [&](int task, int &b, int &n0) {
-    task_coords(task, args.group_rows, ncol, nblk, BN, b, n0);
+  // ---------------- schedule ----------------
+  const int nrt = args.plan[0]; // read before any DMA is in flight
+  const int ncol = N / BN;
+  const int ntask = nrt * ncol;
+  const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
+  const int xcd = blockIdx.x % nx;
+  const int S = gridDim.x / nx;
+  const int slot = blockIdx.x / nx;
+  const int tx0 = (int)(((long)ntask * xcd) / nx);
+  const int tx1 = (int)(((long)ntask * (xcd + 1)) / nx);
+  const int n_items = tx1 - tx0 > slot ? (tx1 - tx0 - slot + S - 1) / S : 0;
+  if (n_items == 0) return;
+  const int total = n_items * KT; // slices of this workgroup
+  auto coords = [&](int i, int &rt, int &n0) {
+    task_coords(tx0 + slot + i * S, args.group_rows, ncol, nrt, BN, rt, n0);
   };
 
-  const uint32_t smem_addr = lds_addr_of(smem);
-  MOE_LDS int32_t(*my_idx)[IDX_WORDS] = (MOE_LDS int32_t(*)[IDX_WORDS])idx_lds[wave];
-
-  // DMA the index table of `task` (the 32 source rows this wavefront loads
-  // and the block's group) into ring slot `seq`.
-  auto fetch_index = [&](int task, int seq) {
-    int b, n0;
-    coords(task, b, n0);
-    const uint32_t dst = (uint32_t)(uintptr_t)&my_idx[seq % IDX_SLOTS][0];
-    if (args.a_src_row) {
-      if (lane < ROWS_PW)
-        dma4(args.a_src_row + (size_t)b * kBM + wave * ROWS_PW + lane, dst);
-      else if (lane == 32)
-        dma4(args.block_group + b, dst); // lane 32 lands at word 32
-    } else if (lane == 32) {
-      dma4(args.block_group + b, dst);
+  // ---------------- per-task tables (DMA'd into small LDS rings) ----------------
+  // DMA the plan entry of item i into this wavefront's slot (lanes 0, 1).
+  auto fetch_plan = [&](int i) {
+    int rt, n0;
+    coords(i, rt, n0);
+    if (lane < 2)
+      dma4(args.plan + kPlanHead + 2 * rt + lane, lds_addr_of(&ptab[wave][i % kPlanSlots][0]));
+  };
+  auto plan_of = [&](int i, int &b, int &nb, int &g) {
+    const int e = __builtin_amdgcn_readfirstlane(ptab[wave][i % kPlanSlots][0]);
+    g = __builtin_amdgcn_readfirstlane(ptab[wave][i % kPlanSlots][1]);
+    b = e & (kPlanTwo - 1);
+    nb = (e & kPlanTwo) ? 2 : 1;
+  };
+  // DMA this wavefront's 64 rows of the pair tables of item i (its plan
+  // entry has landed).  Rows of the missing second block of a one-block
+  // task repeat the first block's rows.
+  auto fetch_tables = [&](int i) {
+    if (!has_tab) return;
+    int b, nb, g;
+    plan_of(i, b, nb, g);
+    const int r = 64 * wave + lane;
+    const size_t src = (size_t)b * kBM + (nb == 2 ? r : (r & (kBM - 1)));
+    const int s = i % kTabSlots;
+    dma4(tab_src + src, lds_addr_of(&tab[s][64 * wave]));
+    if constexpr (SCAT)
+      if (own_e) dma4(args.epi_row_pair + src, lds_addr_of(&etab[s][64 * wave]));
+  };
+  // the epilogue's pair per row
+  auto pair_table = [&](int s) -> const MOE_LDS int32_t * {
+    if constexpr (SCAT)
+      if (own_e) return (const MOE_LDS int32_t *)etab[s];
+    return (const MOE_LDS int32_t *)tab[s];
+  };
+  // DMA the routing weights of this wavefront's 64 rows of item i (its pair
+  // table has landed).
+  auto fetch_weights = [&](int i) {
+    if constexpr (SCAT) {
+      const int s = i % kTabSlots;
+      const int p = pair_table(s)[64 * wave + lane];
+      dma4(args.pair_w + (p < 0 ? 0 : p), lds_addr_of(&wtab[s][64 * wave]));
     }
   };
+  // The column tasks of one row task run side by side on neighbouring CUs;
+  // each starts at its own k-slice, spread evenly by column block, and wraps
+  // around (the sum over k is the same; its fp32 rounding order is fixed per
+  // task).
+  auto k_rotation = [&](int n0) {
+    return __builtin_amdgcn_readfirstlane((int)(((long)(n0 / BN) * KT) / ncol));
+  };
 
-  // ---------------- issue (producer) state ----------------
-  int it_i = 0;   // item being issued
-  int it_k = 0;   // next k-slice of it
-  int it_kb = 0;  // end of its k-slice range
-  int it_len = 0; // its length
+  // ---------------- A stream ----------------
+  int a_i = 0, a_k = KT, a_rot = 0; // item being issued, slices of it issued, its rotation
   const unsigned char *a_src[A_INSTR];
-  const unsigned char *b_src[NB][B_INSTR];
-
-  // Point the per-lane DMA sources at `task`, whose index table sits in
-  // ring slot `seq` and has landed.
-  auto setup_issue = [&](int task, int seq) {
-    int b, n0;
-    coords(task, b, n0);
-    const MOE_LDS int32_t *tab = my_idx[seq % IDX_SLOTS];
-    const int g = tab[32];
+  // Point the A sources at item i (its plan entry and tables have landed).
+  // A one-block task loads its 128 rows twice (rows 128-255 repeat them,
+  // served by the caches) so every slice has the same DMA count.
+  auto a_begin = [&](int i) {
+    // item i's tables were fetched when the B stream began item i-1, which
+    // the consumer's waits have covered unless the A lead is long against
+    // the task length; then wait for everything
+    if (i > 0 && KT + LB <= 2 * LA) wait_vmcnt<0>();
+    int rt, n0, b, nb, g;
+    coords(i, rt, n0);
+    plan_of(i, b, nb, g);
+    a_rot = k_rotation(n0);
+    const MOE_LDS int32_t *ptbl = (const MOE_LDS int32_t *)tab[i % kTabSlots];
 #pragma unroll
-    for (int i = 0; i < A_INSTR; ++i) {
-      // instruction i covers tile rows (wave*A_INSTR+i)*8 .. +8, lane row lane/8
-      const int row = (wave * A_INSTR + i) * 8 + (lane >> 3);
-      int src = b * kBM + row;
-      if (args.a_src_row) {
-        const int p = tab[i * 8 + (lane >> 3)];
+    for (int q = 0; q < A_INSTR; ++q) {
+      // instruction q covers task rows (wave*A_INSTR+q)*A_RPI .. +A_RPI
+      const int row = (wave * A_INSTR + q) * A_RPI + lane / A_GPR;
+      long src = (long)b * kBM + (nb == 2 ? row : (row & (kBM - 1)));
+      if (has_a) {
+        const int p = ptbl[row];
         src = p < 0 ? 0 : p / args.a_src_div; // padding rows read a valid row
       }
-      const int c = (lane & 7) ^ swz128(row);
-      a_src[i] = reinterpret_cast<const unsigned char *>(args.A) + ((size_t)src * K + c * 8) * 2;
+      const int c = (lane % A_GPR) ^ swz_rows<BK>(row);
+      a_src[q] = reinterpret_cast<const unsigned char *>(args.A) + ((size_t)src * K + c * 8) * 2;
     }
+    fetch_weights(i);
+    a_i = i;
+    a_k = 0;
+  };
+  int a_issued = 0; // A slices issued
+  auto a_issue = [&]() {
+    if (a_issued >= total) return;
+    if (a_k == KT) a_begin(a_i + 1);
+    const int ks = __builtin_amdgcn_readfirstlane(a_k + a_rot < KT ? a_k + a_rot : a_k + a_rot - KT);
+    const uint32_t stage = lds_addr_of(aring) + (a_issued % NA) * A_BYTES;
+#pragma unroll
+    for (int q = 0; q < A_INSTR; ++q)
+      dma16(a_src[q] + (size_t)ks * BK * 2, stage + (wave * A_INSTR + q) * 1024);
+    ++a_k;
+    ++a_issued;
+  };
+
+  // ---------------- B stream ----------------
+  constexpr int RPI = KN ? 512 / BN : A_RPI; // k rows ([K][N]) or n rows ([N][K]) per instruction
+  // the swizzle depends on k mod 4 ([K][N]) or n mod 16 ([N][K]): distinct
+  // per-lane offset patterns among the instructions
+  constexpr int QV = KN ? (RPI < 4 ? 4 / RPI : 1) : (RPI < 16 ? 16 / RPI : 1);
+  uint32_t b_off[QV];
+#pragma unroll
+  for (int v = 0; v < QV; ++v) {
+    if constexpr (KN) {
+      constexpr int GPR = BN / 8; // 16-byte granules per k row
+      const int k = v * RPI + lane / GPR;
+      b_off[v] = (uint32_t)(((lane / GPR) * N + (((lane % GPR) ^ swz_kn<BN>(k)) * 8)) * 2);
+    } else {
+      const int n = v * RPI + lane / A_GPR;
+      b_off[v] =
+          (uint32_t)(((lane / A_GPR) * K + (((lane % A_GPR) ^ swz_rows<BK>(n)) * 8)) * 2);
+    }
+  }
+  int b_i = 0, b_k = KT, b_rot = 0;
+  const unsigned char *b_base[NB];
+  // Start the B stream on item i: fetch the plan entry of item i+2 and the
+  // tables of item i+1, then point the B bases at item i (its plan entry
+  // has landed).
+  auto b_begin = [&](int i) {
+    // the plan entry of item i+1 (read by fetch_tables) was fetched when
+    // item i-1 began, which the consumer's waits have covered once a task
+    // has more than NA - 1 slices; below that, wait for everything
+    if (i > 0 && KT < NA) wait_vmcnt<0>();
+    if (i + 2 < n_items) fetch_plan(i + 2);
+    if (i + 1 < n_items) fetch_tables(i + 1);
+    int rt, n0, b, nb, g;
+    coords(i, rt, n0);
+    plan_of(i, b, nb, g);
+    b_rot = k_rotation(n0);
     const int gg = g < 0 ? 0 : g;
 #pragma unroll
     for (int m = 0; m < NB; ++m) {
-      const uint16_t *Bm = (m == 0 ? args.B : args.B2) + (size_t)gg * K * N;
-#pragma unroll
-      for (int i = 0; i < B_INSTR; ++i) {
-        if constexpr (KN) {
-          constexpr int GPR = BN / 8;   // granules per k row
-          constexpr int RPI = 64 / GPR; // k rows per instruction
-          const int k = (wave * B_INSTR + i) * RPI + lane / GPR;
-          const int c = (lane % GPR) ^ swz_kn<BN>(k);
-          b_src[m][i] =
-              reinterpret_cast<const unsigned char *>(Bm) + ((size_t)k * N + n0 + c * 8) * 2;
-        } else {
-          const int n = (wave * B_INSTR + i) * 8 + (lane >> 3);
-          const int c = (lane & 7) ^ swz128(n);
-          b_src[m][i] =
-              reinterpret_cast<const unsigned char *>(Bm) + ((size_t)(n0 + n) * K + c * 8) * 2;
-        }
-      }
+      const unsigned char *Bm =
+          reinterpret_cast<const unsigned char *>(m == 0 ? args.B : args.B2) + (size_t)gg * K * N * 2;
+      // this wavefront's first k row (or n row) of every slice
+      b_base[m] = KN ? Bm + ((size_t)(wave * B_INSTR * RPI) * N + n0) * 2
+                     : Bm + (size_t)(n0 + wave * B_INSTR * RPI) * K * 2;
     }
+    b_i = i;
+    b_k = 0;
   };
-
-  auto begin_issue_item = [&](int i) {
-    int task, ka, kb, tt;
-    sc.item(i, task, ka, kb, tt);
-    if (i + 1 < n_items) {
-      int t2, a2, b2, tt2;
-      sc.item(i + 1, t2, a2, b2, tt2);
-      fetch_index(t2, i + 1);
-    }
-    setup_issue(task, i);
-    it_k = ka;
-    it_kb = kb;
-    it_len = kb - ka;
-  };
-
-  int n_issued = 0;
-  // DMA instruction q (0 <= q < LOADS) of the slice being issued: A first,
-  // then each B matrix.
-  auto issue_dma = [&](int q) {
-    const uint32_t stage = smem_addr + (n_issued % NSTAGE) * STAGE_BYTES;
-    if (q < A_INSTR) {
-      dma16(a_src[q] + (size_t)it_k * kBK * 2, stage + (wave * A_INSTR + q) * 1024);
-    } else {
-      const int m = (q - A_INSTR) / B_INSTR;
-      const int i = (q - A_INSTR) - m * B_INSTR;
-      const size_t b_off = KN ? (size_t)it_k * kBK * N * 2 : (size_t)it_k * kBK * 2;
-      dma16(b_src[m][i] + b_off,
-            stage + A_BYTES + m * B_BYTES + (wave * B_INSTR + i) * 1024);
-    }
-  };
-  // bookkeeping once every instruction of the slice is out
-  auto issue_done = [&]() {
-    ++n_issued;
-    if (++it_k == it_kb) {
-      ++it_i;
-      if (it_i < n_items) {
-        // the table of item it_i was fetched right before the first slice of
-        // the previous item; once NSTAGE of that item's slices were issued
-        // it has been awaited (DMA completes in order)
-        if (it_len < NSTAGE) wait_vmcnt<0>();
-        begin_issue_item(it_i);
-      }
-    }
-  };
-  auto issue_next = [&]() {
-    if (it_i >= n_items) return;
-#pragma unroll
-    for (int q = 0; q < LOADS; ++q) issue_dma(q);
-    issue_done();
-  };
-
-  if (n_items > 0) {
-    int task, ka, kb, tt;
-    sc.item(0, task, ka, kb, tt);
-    fetch_index(task, 0);
-    wait_vmcnt<0>();
-    begin_issue_item(0);
-  }
-#pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s) issue_next();
-
-  // ---------------- compute (consumer) ----------------
-  int n_consumed = 0;
-  for (int i = 0; i < n_items; ++i) {
-    int task, ka, kb, tt;
-    sc.item(i, task, ka, kb, tt);
-    f32x16 acc[NB][MI][NI];
+  int b_issued = 0;
+  auto b_issue = [&]() {
+    if (b_issued >= total) return;
+    if (b_k == KT) b_begin(b_i + 1);
+    const int ks = __builtin_amdgcn_readfirstlane(b_k + b_rot < KT ? b_k + b_rot : b_k + b_rot - KT);
+    const uint32_t stage = lds_addr_of(bring) + (b_issued % NBR) * BS_BYTES;
 #pragma unroll
     for (int m = 0; m < NB; ++m)
 #pragma unroll
-      for (int a = 0; a < MI; ++a)
+      for (int q = 0; q < B_INSTR; ++q) {
+        const size_t off = KN ? ((size_t)ks * BK + q * RPI) * N * 2
+                              : (size_t)ks * BK * 2 + (size_t)q * RPI * K * 2;
+        dma16s(b_off[q % QV], b_base[m] + off,
+               stage + m * B_BYTES + (wave * B_INSTR + q) * 1024);
+      }
+    ++b_k;
+    ++b_issued;
+  };
+
+  // prologue: the plan entries of items 0-3 and the tables of items 0-2 --
+  // all the prologue's streams can reach (the B stream at most item 1, as
+  // 2 KT >= NBR - 1) and what their task starts fetch for later ones; then
+  // the B stream and the A stream start on item 0 and issue the first LB B
+  // slices and LA A slices, A slice s right before B slice s + LB - LA, the
+  // order of the main loop
+  for (int j = 0; j < 4 && j < n_items; ++j) fetch_plan(j);
+  wait_vmcnt<0>();
+  for (int j = 0; j < 3 && j < n_items; ++j) fetch_tables(j);
+  wait_vmcnt<0>();
+  b_begin(0);
+  a_begin(0);
+  for (int s = 0; s < LB - LA; ++s) b_issue();
+  for (int s = 0; s < LA; ++s) {
+    a_issue();
+    b_issue();
+  }
+
+  // ---------------- compute (consumer) ----------------
+  // Fragments of one 16-deep k step, double-buffered in registers.
+  i16x4 fa[2][4][2];
+  i16x4 fb[2][NB][NI][2];
+  auto load_frags = [&](int c, int kk, i16x4(&a)[4][2], i16x4(&b)[NB][NI][2]) {
+    const MOE_LDS unsigned char *sA =
+        (const MOE_LDS unsigned char *)(aring + (c % NA) * A_BYTES);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int row = wm * 128 + mi * 32 + (lane & 31);
+      const int c16 = (kk * 2 + (lane >> 5)) ^ swz_rows<BK>(row);
+      const u32x4 v = *(const MOE_LDS u32x4 *)(sA + row * ARP + c16 * 16);
+      a[mi][0] = __builtin_bit_cast(i16x4, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
+      a[mi][1] = __builtin_bit_cast(i16x4, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
+    }
+    const MOE_LDS unsigned char *sBs =
+        (const MOE_LDS unsigned char *)(bring + (c % NBR) * BS_BYTES);
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+      const MOE_LDS unsigned char *sB = sBs + m * B_BYTES;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        if constexpr (KN) {
+          // lane group G = lane/16 reads columns n0 + 16*(G&1) .. +16 at
+          // k = 8*(G>>1) + 4*r + (lane%16)/4; each lane points at 4
+          // consecutive columns, the transpose read returns 4 k of one column
+          const int G = lane >> 4;
+          const int q = lane & 15;
+          const int n = wn * WC + j * 32 + 16 * (G & 1) + 4 * (q & 3);
+          const int k0 = kk * 16 + 8 * (G >> 1) + (q >> 2);
+          const int k1 = k0 + 4;
+          const int o0 = k0 * (BN * 2) + (((n >> 3) ^ swz_kn<BN>(k0)) << 4) + ((n & 7) << 1);
+          const int o1 = k1 * (BN * 2) + (((n >> 3) ^ swz_kn<BN>(k1)) << 4) + ((n & 7) << 1);
+          b[m][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4 *)(sB + o0));
+          b[m][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4 *)(sB + o1));
+        } else {
+          const int n = wn * WC + j * 32 + (lane & 31);
+          const int c16 = (kk * 2 + (lane >> 5)) ^ swz_rows<BK>(n);
+          const u32x4 v = *(const MOE_LDS u32x4 *)(sB + n * ARP + c16 * 16);
+          b[m][j][0] = __builtin_bit_cast(i16x4, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
+          b[m][j][1] = __builtin_bit_cast(i16x4, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
+        }
+      }
+    }
+  };
+
+  // Slice c+1 (A and B) has landed for this wavefront once at most AFTER
+  // DMA instructions are still in flight (DMA completes in issue order);
+  // near the end of the stream fewer were issued after it, so wait for all.
+  auto wait_slice = [&](int c1) {
+    if (b_issued >= c1 + LB && a_issued >= c1 + LA)
+      wait_vmcnt<AFTER>();
+    else
+      wait_vmcnt<0>();
+  };
+  wait_slice(0);
+  block_barrier();
+  load_frags(0, 0, fa[0], fb[0]);
+
+  // The accumulators are carried across items and cleared right after each
+  // epilogue has read them, so one register set serves every item.
+  f32x16 acc[NB][4][NI];
+  auto clear_acc = [&]() {
+    // an opaque zero: a constant zero vector would be hoisted out of the
+    // item loop and kept in 16 * NB * 4 * NI spare registers
+    float z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int j = 0; j < NI; ++j)
-          for (int r = 0; r < 16; ++r) acc[m][a][j][r] = 0.0f;
-    int group = 0;
-
-    for (int kt = ka; kt < kb; ++kt) {
-      // this wavefront's DMA for slice n_consumed has landed ...
-      if (n_issued - n_consumed - 1 >= NSTAGE - 2)
-        wait_vmcnt<LOADS * (NSTAGE - 2)>();
-      else
-        wait_vmcnt<0>();
-      // ... and so has every other wavefront's; everyone is done with the
-      // stage the next issue overwrites
-      block_barrier();
-      if (kt == ka) group = __builtin_amdgcn_readfirstlane(my_idx[i % IDX_SLOTS][32]);
-      // the next slice's DMA is spread over the k steps of this one, so the
-      // address unit drains it in the background of the MFMAs
-      const bool issuing = it_i < n_items;
-      constexpr int PER = (LOADS + 3) / 4;
-
-      const MOE_LDS unsigned char *sA =
-          (const MOE_LDS unsigned char *)(smem + (n_consumed % NSTAGE) * STAGE_BYTES);
-      // Fragments of one 16-deep k step, double-buffered in registers: the
-      // LDS reads of step kk+1 are issued before the MFMAs of step kk, so
-      // their latency hides behind matrix work (one wavefront per SIMD
-      // leaves nothing else to hide it).
-      i16x4 fa[2][MI][2];
-      i16x4 fb[2][NB][NI][2];
-      auto load_frags = [&](int kk, i16x4 (&a)[MI][2], i16x4 (&b)[NB][NI][2]) {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-          const int row = wm * WG::WR + mi * 32 + (lane & 31);
-          const int c = (kk * 2 + (lane >> 5)) ^ swz128(row);
-          const u32x4 v = *(const MOE_LDS u32x4 *)(sA + row * 128 + c * 16);
-          a[mi][0] = __builtin_bit_cast(i16x4, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
-          a[mi][1] = __builtin_bit_cast(i16x4, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
-        }
+          for (int r = 0; r < 16; ++r) acc[m][a][j][r] = z;
+  };
+  clear_acc();
+  int c = 0; // slice being consumed (global count)
+  for (int i = 0; i < n_items; ++i) {
+    // this item's coordinates, read before later fetches may reuse its slot
+    int rt, n0, b, nb, g;
+    coords(i, rt, n0);
+    plan_of(i, b, nb, g);
+    for (int kt = 0; kt < KT; ++kt, ++c) {
+      const bool has_next = c + 1 < total;
 #pragma unroll
-        for (int m = 0; m < NB; ++m) {
-          const MOE_LDS unsigned char *sB = sA + A_BYTES + m * B_BYTES;
-#pragma unroll
-          for (int j = 0; j < NI; ++j) {
-            if constexpr (KN) {
-              // lane group G = lane/16 reads columns n0 + 16*(G&1) .. +16 at
-              // k = 8*(G>>1) + 4*r + (lane%16)/4; each lane points at 4
-              // consecutive columns, the transpose read returns 4 k of one column
-              const int G = lane >> 4;
-              const int q = lane & 15;
-              const int n = wn * WG::WC + j * 32 + 16 * (G & 1) + 4 * (q & 3);
-              const int k0 = kk * 16 + 8 * (G >> 1) + (q >> 2);
-              const int k1 = k0 + 4;
-              const int o0 = k0 * (BN * 2) + (((n >> 3) ^ swz_kn<BN>(k0)) << 4) + ((n & 7) << 1);
-              const int o1 = k1 * (BN * 2) + (((n >> 3) ^ swz_kn<BN>(k1)) << 4) + ((n & 7) << 1);
-              b[m][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4 *)(sB + o0));
-              b[m][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4 *)(sB + o1));
-            } else {
-              const int n = wn * WG::WC + j * 32 + (lane & 31);
-              const int c = (kk * 2 + (lane >> 5)) ^ swz128(n);
-              const u32x4 v = *(const MOE_LDS u32x4 *)(sB + n * 128 + c * 16);
-              b[m][j][0] = __builtin_bit_cast(i16x4, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
-              b[m][j][1] = __builtin_bit_cast(i16x4, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
-            }
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const int cur = kk & 1;
+        if (kk + 1 < KSTEPS) {
+          // this step's fragments (read during the previous MFMAs) are in:
+          // said explicitly, so no LDS wait lands among the MFMAs below
+          wait_lgkm0();
+          // next k step of this slice; then this wavefront's share of the
+          // next slices' DMA, into the stages every wavefront has released
+          load_frags(c, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+          if (kk == 0) {
+            a_issue();
+            b_issue();
+          }
+        } else {
+          // this wavefront is done reading stage c (on every path, so the
+          // compiler sees this step's fragments complete and puts no LDS
+          // wait among the MFMAs below)
+          wait_lgkm0();
+          if (has_next) {
+            // slice c+1 has landed for this wavefront ...
+            wait_slice(c + 1);
+            // ... and for every wavefront; and every wavefront is done
+            // reading stage c, which the next issues overwrite
+            block_barrier();
+            load_frags(c + 1, 0, fa[cur ^ 1], fb[cur ^ 1]);
           }
         }
-      };
-      load_frags(0, fa[0], fb[0]);
-#pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        const int cur = kk & 1;
-        if (kk + 1 < kBK / 16) load_frags(kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
-        if (issuing) {
-#pragma unroll
-          for (int q = kk * PER; q < (kk + 1) * PER && q < LOADS; ++q) issue_dma(q);
-        }
-        // keep the next step's reads and this DMA share ahead of the MFMAs
+        // keep the fragment reads and the DMA issue ahead of the MFMAs
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < NB; ++m)
 #pragma unroll
           for (int j = 0; j < NI; ++j)
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
+            for (int mi = 0; mi < 4; ++mi)
               acc[m][mi][j] = mfma32<FP16>(fa[cur][mi][0], fa[cur][mi][1], fb[cur][m][j][0],
                                            fb[cur][m][j][1], acc[m][mi][j]);
       }
-      if (issuing) issue_done();
-      ++n_consumed;
     }
 
-    if (group < 0) continue; // block without a group: no output
-    if (ka == 0 && kb == KT) {
-      int b, n0;
-      coords(task, b, n0);
-      if constexpr (EPI == kEpiScatter)
-        scatter_tile<MI, NI>(acc, args.Dacc, N, args.epi_row_pair + (size_t)b * kBM + wm * WG::WR,
-                             args.pair_w, args.topk, lane, n0 + wn * WG::WC);
-      else
-        store_tile<NB, FP16, MI, NI>(acc, args.D + (size_t)b * kBM * N + n0, N,
-                                     (MOE_LDS uint16_t *)epi_lds[wave], lane, wm * WG::WR,
-                                     wn * WG::WC);
-    } else {
-      // a piece of a split tail task: store the fp32 partial tile
-      float *pt = partial_tile(args.partials, sc, sc.slot, tt - sc.bound(sc.slot) / KT, ACC, NT);
-      const float *flat = reinterpret_cast<const float *>(&acc[0][0][0]);
-#pragma unroll
-      for (int q = 0; q < ACC / 4; ++q) {
-        f32x4 v = {flat[4 * q], flat[4 * q + 1], flat[4 * q + 2], flat[4 * q + 3]};
-        *reinterpret_cast<f32x4 *>(pt + ((size_t)q * NT + tid) * 4) = v;
+    // no group: no output; a one-block task has no rows 128-255
+    if (g >= 0 && (nb == 2 || wm == 0)) {
+      const int s = i % kTabSlots;
+      if constexpr (SCAT) {
+        scatter_tile<4, NI>(acc, args.Dacc, N, pair_table(s), (const MOE_LDS float *)wtab[s],
+                            args.topk, lane, wm * 128, n0 + wn * WC);
+      } else {
+        store_tile<NB, FP16, 4, NI>(acc, args.D + (size_t)b * kBM * N + n0, N,
+                                    (MOE_LDS uint16_t *)epi_lds[wave],
+                                    has_tab ? pair_table(s) : nullptr, lane, wm * 128, wn * WC);
       }
     }
+    clear_acc();
   }
   // drain any DMA still in flight before the workgroup retires its LDS
   wait_vmcnt<0>();
 }
 
-// Sums the partial tiles of every split tail task in k order (deterministic)
-// and runs the epilogue.  One workgroup per (XCD, tail task); launched with
-// the same grid size as the GEMM so the schedule is recomputed identically.
-template <int BN, int EPI, bool FP16, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void grouped_gemm_fixup(GGArgs args, int gemm_grid) {
-  constexpr int NB = EPI == kEpiSiluMul ? 2 : 1;
-  using WG = WaveGrid<BN, WAVES>;
-  constexpr int NT = WG::kThreads;
-  constexpr int MI = WG::MI;
-  constexpr int NI = WG::NI;
-  constexpr int ACC = NB * MI * NI * 16;
-  __shared__ __attribute__((aligned(16))) uint16_t epi_lds[WAVES][16 * kEpiLd];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  Sched sc;
-  // blockIdx.x = xcd + nx * tail task index: reuse the XCD / slot fields
-  sc.init(args, BN, gemm_grid, blockIdx.x % (gemm_grid % 8 == 0 ? 8 : 1));
-  const int tt = blockIdx.x / sc.nx;
-  if (tt >= sc.rem) return;
-  const int KT = sc.KT;
-  // segments of tail task tt, in k order
-  int nseg = 0;
-  for (int s = 0; s < sc.S; ++s)
-    if (max(sc.bound(s), tt * KT) < min(sc.bound(s + 1), (tt + 1) * KT)) ++nseg;
-  if (nseg < 2) return; // finished in place by the GEMM kernel
-  const int task = sc.tx0 + sc.full + tt;
-  int b, n0;
-  task_coords(task, args.group_rows, sc.ncol, sc.nblk, BN, b, n0);
-  if (args.block_group[b] < 0) return;
-
-  f32x16 acc[NB][MI][NI];
-  float *flat = reinterpret_cast<float *>(&acc[0][0][0]);
-  bool first = true;
-  for (int s = 0; s < sc.S; ++s) {
-    if (!(max(sc.bound(s), tt * KT) < min(sc.bound(s + 1), (tt + 1) * KT))) continue;
-    const float *pt = partial_tile(args.partials, sc, s, tt - sc.bound(s) / KT, ACC, NT);
-#pragma unroll
-    for (int q = 0; q < ACC / 4; ++q) {
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(pt + ((size_t)q * NT + tid) * 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) flat[4 * q + e] = first ? v[e] : flat[4 * q + e] + v[e];
-    }
-    first = false;
-  }
-  const int wm = wave / WG::WNC, wn = wave % WG::WNC;
-  if constexpr (EPI == kEpiScatter)
-    scatter_tile<MI, NI>(acc, args.Dacc, args.N, args.epi_row_pair + (size_t)b * kBM + wm * WG::WR,
-                         args.pair_w, args.topk, lane, n0 + wn * WG::WC);
-  else
-    store_tile<NB, FP16, MI, NI>(acc, args.D + (size_t)b * kBM * args.N + n0, args.N,
-                                 (MOE_LDS uint16_t *)epi_lds[wave], lane, wm * WG::WR,
-                                 wn * WG::WC);
-}
-
-template <int BN, int EPI, bool KN, bool FP16, int NSTAGE, int WAVES>
+template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR>
 static hipError_t launch_one(const GGArgs &a, int grid, hipStream_t stream) {
-  grouped_gemm_kernel<BN, EPI, KN, FP16, NSTAGE, WAVES><<<grid, 64 * WAVES, 0, stream>>>(a);
-  if (a.partials)
-    grouped_gemm_fixup<BN, EPI, FP16, WAVES><<<grid, 64 * WAVES, 0, stream>>>(a, grid);
+  grouped_gemm_kernel<BN, BK, EPI, KN, FP16, NA, NBR><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-// Tile configuration of one launch: BN (columns per matrix), LDS ring depth,
-// super-block rows of the task order, split tail on/off, wavefronts (4 or 8).
+// Tile configuration of one launch: BN (columns per matrix), BK (k per
+// slice), A and B ring depths, row tasks per super-block of the task order.
 struct TileCfg {
-  int bn, stages, group, split, waves;
+  int bn, bk, na, nb, group;
 };
 
-// instantiated (BN, stages) per B-matrix count; LDS: ring + 4 KiB index
-// tables + 10 KiB epilogue tiles <= 160 KiB
-inline bool tile_supported(int nb, int bn, int stages) {
-  if (stages < 2 || stages > 4) return false;
-  if (bn == 64) return true;
-  if (bn == 128) return nb == 1 || stages <= 3;
-  if (bn == 256) return nb == 1 && stages <= 3;
-  return false;
+// The instantiated (BN, BK, NA, NBR) per B-matrix count; the rings stay
+// within 144 KiB so the tables and staging tiles fit in the 160 KiB of LDS.
+// Every BN has the 4/4 rings, safe for any K (2 KT >= 3).
+inline bool tile_supported(int nbm, int bn, int bk, int na, int nb) {
+  if (bk != 32) return false;
+  if (na == 4 && nb == 4) return bn == 64 || bn == 128 || (bn == 256 && nbm == 1);
+  if (nbm == 2) return (bn == 128 && na == 3 && nb == 6) || (bn == 64 && na == 3 && nb == 10);
+  return (bn == 256 && na == 3 && nb == 6) || (bn == 128 && na == 3 && nb == 10) ||
+         (bn == 64 && na == 4 && nb == 8);
 }
 
 // Launch of one (epilogue, B layout, dtype) combination with the tile shape
@@ -678,16 +706,14 @@ inline bool tile_supported(int nb, int bn, int stages) {
 // the dispatcher declares those instantiations extern.
 template <int EPI, bool KN, bool FP16>
 hipError_t launch_bn(const GGArgs &a, const TileCfg &c, int grid, hipStream_t s) {
-  constexpr int NB = EPI == kEpiSiluMul ? 2 : 1;
-#define MOE_GG_CASE(BNV, NSV)                                                                 \
-  if (c.bn == BNV && c.stages == NSV)                                                         \
-    return c.waves == 8 ? launch_one<BNV, EPI, KN, FP16, NSV, 8>(a, grid, s)                  \
-                        : launch_one<BNV, EPI, KN, FP16, NSV, 4>(a, grid, s);
-  MOE_GG_CASE(64, 2) MOE_GG_CASE(64, 3) MOE_GG_CASE(64, 4)
-  MOE_GG_CASE(128, 2) MOE_GG_CASE(128, 3)
-  if constexpr (NB == 1) {
-    MOE_GG_CASE(128, 4)
-    MOE_GG_CASE(256, 2) MOE_GG_CASE(256, 3)
+#define MOE_GG_CASE(BNV, NAV, NBV)                                                            \
+  if (c.bn == BNV && c.bk == 32 && c.na == NAV && c.nb == NBV)                                \
+    return launch_one<BNV, 32, EPI, KN, FP16, NAV, NBV>(a, grid, s);
+  if constexpr (EPI == kEpiSiluMul) {
+    MOE_GG_CASE(128, 3, 6) MOE_GG_CASE(128, 4, 4) MOE_GG_CASE(64, 3, 10) MOE_GG_CASE(64, 4, 4)
+  } else {
+    MOE_GG_CASE(256, 3, 6) MOE_GG_CASE(256, 4, 4) MOE_GG_CASE(128, 3, 10) MOE_GG_CASE(128, 4, 4)
+    MOE_GG_CASE(64, 4, 8) MOE_GG_CASE(64, 4, 4)
   }
 #undef MOE_GG_CASE
   return hipErrorInvalidValue;

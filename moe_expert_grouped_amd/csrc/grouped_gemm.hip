@@ -21,47 +21,120 @@ MOE_GG_EXTERN(kEpiScatter, true, false)
 MOE_GG_EXTERN(kEpiScatter, true, true)
 #undef MOE_GG_EXTERN
 
-// Tile configurations.  Defaults (measured on the MI355X at the shapes of
-// the MoE layer share): gate/up 128 gate + 128 up columns with a 3-deep
-// ring, down / dense 256 columns with a 3-deep ring; the split tail is off
-// (its fp32 partial-tile round trip cost more than the balance it bought).
-// Each can be overridden for tuning sweeps with
-// MOE_GG_TILE="<bn>,<stages>,<group rows>[,<split>[,<waves>]]" (e.g. "128,3,4,1").
-static TileCfg tile_config(int epilogue, int N) {
-  TileCfg c = epilogue == kEpiSiluMul
-                  ? TileCfg{N % 128 == 0 ? 128 : 64, N % 128 == 0 ? 3 : 4, 1, 0, 4}
-                  : TileCfg{N % 256 == 0 ? 256 : (N % 128 == 0 ? 128 : 64), N % 256 == 0 ? 3 : 4,
-                            1, 0, 4};
-  if (const char *env = getenv("MOE_GG_TILE")) {
-    TileCfg e{0, 0, 0, 0, 4};
-    const int n =
-        sscanf(env, "%d,%d,%d,%d,%d", &e.bn, &e.stages, &e.group, &e.split, &e.waves);
-    if (n >= 3 && e.group >= 1 && N % e.bn == 0 && (e.waves == 4 || e.waves == 8) &&
-        tile_supported(epilogue == kEpiSiluMul ? 2 : 1, e.bn, e.stages))
-      c = e;
+// Tile configurations: (BN, BK, A ring depth, B ring depth, super-block row
+// tasks).  Defaults: gate/up 128 gate + 128 up columns, down / dense 256
+// columns (128 when N is not a multiple of 256, 64 below that), 32-deep
+// slices, a 3-deep A ring and a 6-deep B ring (weights are most of the
+// bytes in flight).  Each can be overridden for tuning sweeps with
+// MOE_GG_TILE="<bn>,<bk>,<na>,<nb>[,<group rows>]" (MOE_GG_TILE_GU, if set,
+// for the SiLU*up epilogue only).  A configuration is used
+// only if it is instantiated, divides N, and its B ring keeps the per-task
+// tables safe for this K (2 * K / BK >= nb - 1); otherwise the 4-deep rings,
+// instantiated for every BN.
+static bool tile_usable(const TileCfg &c, int epilogue, int N, int K) {
+  return c.group >= 1 && c.bn > 0 && c.bk > 0 && N % c.bn == 0 && K % c.bk == 0 &&
+         2 * (K / c.bk) >= c.nb - 1 &&
+         tile_supported(epilogue == kEpiSiluMul ? 2 : 1, c.bn, c.bk, c.na, c.nb);
+}
+
+static TileCfg tile_config(int epilogue, int N, int K) {
+  TileCfg c;
+  if (epilogue == kEpiSiluMul)
+    c = N % 128 == 0 ? TileCfg{128, 32, 3, 6, 1} : TileCfg{64, 32, 3, 10, 1};
+  else
+    c = N % 256 == 0 ? TileCfg{256, 32, 3, 6, 1}
+                     : (N % 128 == 0 ? TileCfg{128, 32, 3, 10, 1} : TileCfg{64, 32, 4, 8, 1});
+  if (!tile_usable(c, epilogue, N, K)) c.na = c.nb = 4; // short K: shallower rings
+  const char *env = epilogue == kEpiSiluMul ? getenv("MOE_GG_TILE_GU") : nullptr;
+  if (!env) env = getenv("MOE_GG_TILE");
+  if (env) {
+    TileCfg e{0, 0, 0, 0, 1};
+    const int n = sscanf(env, "%d,%d,%d,%d,%d", &e.bn, &e.bk, &e.na, &e.nb, &e.group);
+    if (n >= 4 && tile_usable(e, epilogue, N, K)) c = e;
   }
   return c;
 }
 
-// Workspace for the split tail: two fp32 partial tiles per workgroup of the
-// largest tile shape (128 accumulator floats per thread).
-size_t gg_workspace_bytes(int grid) { return (size_t)grid * 2 * 128 * 256 * sizeof(float); }
+// Plan of row tasks (one workgroup of 1024 threads): inside each maximal run
+// of blocks with the same non-negative group, blocks are paired from the
+// run's first block; a run of odd length ends in a one-block task.  Blocks
+// with a negative group get no task.  Chunks of 1024 blocks carry the open
+// run's first block and the task count.
+__global__ __launch_bounds__(1024) void gg_plan_kernel(const int32_t *__restrict__ block_group,
+                                                       const int32_t *__restrict__ num_rows,
+                                                       int cap, int32_t *__restrict__ plan) {
+  __shared__ int s_a[1024];
+  __shared__ int s_b[1024];
+  const int t = threadIdx.x;
+  const int nblk = max(0, min(num_rows[0], cap)) / kBM;
+  int carry_start = -1, carry_count = 0;
+  for (int base = 0; base < nblk; base += 1024) {
+    const int b = base + t;
+    const int g = b < nblk ? block_group[b] : -1;
+    const int gp = (b > 0 && b < nblk) ? block_group[b - 1] : -1;
+    const int gn = (b + 1 < nblk) ? block_group[b + 1] : -1;
+    const bool start = g >= 0 && (b == 0 || gp != g);
+    // inclusive max-scan of run starts
+    s_a[t] = start ? b : -1;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int v = t >= off ? s_a[t - off] : -1;
+      __syncthreads();
+      s_a[t] = max(s_a[t], v);
+      __syncthreads();
+    }
+    const int rs = max(s_a[t], carry_start);
+    const bool head = g >= 0 && ((b - rs) & 1) == 0;
+    // inclusive sum-scan of heads
+    s_b[t] = head ? 1 : 0;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int v = t >= off ? s_b[t - off] : 0;
+      __syncthreads();
+      s_b[t] += v;
+      __syncthreads();
+    }
+    if (head) {
+      const int idx = carry_count + s_b[t] - 1;
+      plan[kPlanHead + 2 * idx] = b | (gn == g ? kPlanTwo : 0);
+      plan[kPlanHead + 2 * idx + 1] = g;
+    }
+    const int last_rs = max(s_a[1023], carry_start);
+    const int total = s_b[1023];
+    __syncthreads();
+    carry_start = last_rs;
+    carry_count += total;
+  }
+  if (t == 0) {
+    plan[0] = carry_count;
+    plan[1] = nblk;
+  }
+}
+
+size_t gg_plan_bytes(int cap) { return plan_ints(cap) * sizeof(int32_t); }
+
+// Builds the row-task plan of block_group / num_rows into `plan`.
+hipError_t launch_gg_plan(const int32_t *block_group, const int32_t *num_rows, int cap,
+                          int32_t *plan, hipStream_t stream) {
+  gg_plan_kernel<<<1, 1024, 0, stream>>>(block_group, num_rows, cap, plan);
+  return hipGetLastError();
+}
 
 // dtype 0 bf16 / 1 fp16; layout 0 KN / 1 NK; epilogue 0 STORE / 1 SILU_MUL /
 // 2 WEIGHTED_SCATTER (KN only; D is then the fp32 token-row accumulator).
-hipError_t launch_grouped_gemm(int dtype, int N, int K, int cap, const uint16_t *A,
+// `plan` holds the row-task plan of block_group (launch_gg_plan), built
+// earlier on the same stream.
+hipError_t launch_grouped_gemm(int dtype, int N, int K, const uint16_t *A,
                                const int32_t *a_src_row, int a_src_div, const uint16_t *B,
-                               const uint16_t *B2, int layout, const int32_t *block_group,
-                               const int32_t *num_rows, int epilogue, const int32_t *epi_row_pair,
-                               const float *pair_w, int topk, void *D, void *ws,
-                               size_t ws_bytes, int num_cus, hipStream_t stream) {
-  const TileCfg c = tile_config(epilogue, N);
+                               const uint16_t *B2, int layout, const int32_t *plan, int epilogue,
+                               const int32_t *epi_row_pair, const float *pair_w, int topk,
+                               void *D, int num_cus, hipStream_t stream) {
+  const TileCfg c = tile_config(epilogue, N, K);
   const int grid = num_cus; // one workgroup per CU (LDS-limited)
-  float *partials = (c.split && ws && ws_bytes >= gg_workspace_bytes(grid)) ? (float *)ws : nullptr;
   const bool scat = epilogue == kEpiScatter;
-  GGArgs a{A, a_src_row, a_src_div, B, B2, block_group, num_rows,
-           scat ? nullptr : (uint16_t *)D, N, K, cap, c.group, partials,
-           scat ? (float *)D : nullptr, epi_row_pair, pair_w, topk};
+  GGArgs a{A, a_src_row, a_src_div, B, B2, plan,
+           scat ? nullptr : (uint16_t *)D, scat ? (float *)D : nullptr,
+           epi_row_pair, pair_w, topk, N, K, c.group};
   const bool fp16 = dtype == 1;
   const bool kn = layout == 0;
   if (scat) {

@@ -101,9 +101,9 @@ def test_permute_validation(lib):
 
 def test_grouped_gemm_validation(lib):
     def call(dtype=0, N=128, K=128, cap=256, A=FAKE, src=NULL, div=1, B=FAKE, B2=NULL, lay=0,
-             bg=FAKE, nr=FAKE, epi=0, rp=NULL, pw=NULL, k=0, D=FAKE, ws=NULL):
+             bg=FAKE, nr=FAKE, epi=0, rp=NULL, pw=NULL, k=0, D=FAKE, ws=FAKE, wsb=1 << 20):
         return lib.grouped_gemm(dtype, N, K, cap, A, src, div, B, B2, lay, bg, nr, epi, rp, pw, k, D,
-                                ws, 0, NULL)
+                                ws, wsb, NULL)
     assert call(A=NULL) == moe.MOE_ERR_INVALID
     assert call(A=MISALIGNED) == moe.MOE_ERR_INVALID
     assert call(N=96) == moe.MOE_ERR_UNSUPPORTED
@@ -115,13 +115,16 @@ def test_grouped_gemm_validation(lib):
     assert call(epi=7) == moe.MOE_ERR_UNSUPPORTED
     assert call(src=FAKE, div=0) == moe.MOE_ERR_INVALID
     assert call(ws=MISALIGNED) == moe.MOE_ERR_INVALID
+    assert call(wsb=8) == moe.MOE_ERR_WORKSPACE
     # weighted scatter: needs the row -> pair map, the weights and k >= 1; [K][N] weights only
     assert call(epi=2) == moe.MOE_ERR_INVALID
     assert call(epi=2, rp=FAKE, pw=FAKE, k=0) == moe.MOE_ERR_INVALID
     assert call(epi=2, rp=FAKE, pw=NULL, k=2) == moe.MOE_ERR_INVALID
     assert call(epi=2, rp=FAKE, pw=FAKE, k=2, lay=1) == moe.MOE_ERR_UNSUPPORTED
     assert call(epi=3) == moe.MOE_ERR_UNSUPPORTED
-    assert lib.grouped_gemm_workspace_size() > 0
+    assert call(ws=NULL) == moe.MOE_ERR_WORKSPACE
+    assert lib.grouped_gemm_workspace_size(256) > 0
+    assert lib.grouped_gemm_workspace_size(0) == 0
 
 
 def test_finalize_validation(lib):

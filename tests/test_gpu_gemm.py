@@ -133,24 +133,24 @@ def test_dense_fp16_degenerate_case_sampled():
     assert_close(to_f64(D), lib.double().cpu().numpy(), "dense vs library")
 
 
-# bn, ring stages, super-block rows[, split tail, wavefronts]
-TILES = [("store", "64,2,1"), ("store", "64,3,2"), ("store", "128,2,3"), ("store", "128,3,4"),
-         ("store", "128,4,1"), ("store", "256,2,4"), ("store", "256,3,2"),
-         ("silu_mul", "64,2,2"), ("silu_mul", "64,3,1"), ("silu_mul", "64,4,4"),
-         ("silu_mul", "128,2,4"), ("silu_mul", "128,3,3"),
-         ("store", "64,3,1,0,8"), ("store", "128,4,2,0,8"), ("store", "256,3,1,0,8"),
-         ("store", "256,3,1,1,8"), ("silu_mul", "64,4,1,0,8"), ("silu_mul", "128,3,1,0,8"),
-         ("silu_mul", "128,3,2,1,8")]
+# bn, bk, A ring depth, B ring depth[, super-block row tasks]
+TILES = [("store", "256,32,3,6"), ("store", "256,32,4,4,2"), ("store", "128,32,3,10"),
+         ("store", "64,32,4,8,3"), ("store", "256,32,3,6,4"),
+         ("silu_mul", "128,32,3,6"), ("silu_mul", "128,32,4,4,2"), ("silu_mul", "64,32,3,10"),
+         ("silu_mul", "128,32,3,6,3")]
 
 
 @pytest.mark.parametrize("epi,tile", TILES, ids=["%s-%s" % t for t in TILES])
 def test_tile_configurations_integer_exact(epi, tile, monkeypatch):
-    # every instantiated tile shape / ring depth / task order gives the exact result
+    # every instantiated tile shape / ring depths / task order gives the
+    # exact result; K = 64 and 128 have fewer slices than the B ring has
+    # stages (a configuration whose table ring is unsafe for them falls back
+    # to shallower rings)
     monkeypatch.setenv("MOE_GG_TILE", tile)
     G, N = 4, 512
     cap = 11 * 128
     bg = _groups(cap // 128, G, 17)
-    for K in (128, 320):
+    for K in (64, 128, 320, 640):
         A = syn.ternary_bits((cap, K), 8)
         B = syn.ternary_bits((G, K, N), 9)
         B2 = syn.ternary_bits((G, K, N), 10) if epi == "silu_mul" else None
@@ -167,62 +167,71 @@ def test_tile_configurations_integer_exact(epi, tile, monkeypatch):
         assert np.all(np.isnan(got[m_rows:]))
 
 
-@pytest.mark.parametrize("epi,tile,K", [("store", "256,3,1", 320), ("store", "128,4,2", 128),
-                                        ("store", "64,3,4", 576), ("silu_mul", "128,3,1", 320),
-                                        ("silu_mul", "64,4,2", 192)])
-@pytest.mark.parametrize("waves", [4, 8])
-def test_split_tail_matches_whole_tasks(epi, tile, K, waves, monkeypatch):
-    # a task count that leaves a partly filled last round on every XCD, so the
-    # tail is split along K (several segments per task) and finished by the
-    # fixup kernel; integer-exact inputs make both paths bit-identical
-    G, N = 5, 512
-    bn = int(tile.split(",")[0])
-    ncol = N // bn
-    nblk = (8 * 42 + ncol - 1) // ncol          # ~42 tasks per XCD: 32 whole + 10 split
+# block-group patterns for the pairing of blocks into 256-row tasks: runs of
+# odd and even length, a group that comes back after another, blocks without
+# a group inside and at the ends, one-block runs, a single run
+PAIRINGS = [[0, 0, 0, 1, 1, 2, 2, 2, 2, 3],
+            [-1, 5, 5, 5, -1, 5, 5, 2, -1, -1],
+            [1, 0, 1, 0, 1, 1, 1, 0, 0, 0, 2],
+            [3] * 13,
+            [2, -1, -1, 4, 4, -1, 0],
+            [4, 3, 2, 1, 0]]
+
+
+@pytest.mark.parametrize("pattern", range(len(PAIRINGS)))
+@pytest.mark.parametrize("epi", ["store", "silu_mul"])
+def test_block_pairing_integer_exact(pattern, epi):
+    bg = np.array(PAIRINGS[pattern], np.int32)
+    G, K = 6, 192
+    N = 256 if epi == "store" else 128
+    nblk = len(bg)
     cap = (nblk + 1) * 128
-    bg = _groups(cap // 128, G, 23)
-    A = syn.ternary_bits((cap, K), 11)
-    B = syn.ternary_bits((G, K, N), 12)
-    B2 = syn.ternary_bits((G, K, N), 13) if epi == "silu_mul" else None
+    bgc = np.concatenate([bg, [-1]]).astype(np.int32)
+    A = syn.ternary_bits((cap, K), 40 + pattern)
+    B = syn.ternary_bits((G, K, N), 50 + pattern)
+    B2 = syn.ternary_bits((G, K, N), 60 + pattern) if epi == "silu_mul" else None
     m_rows = nblk * 128
-    say("gemm split tail", epi, tile, "K", K, "blocks", nblk)
-    monkeypatch.setenv("MOE_GG_TILE", tile + ",1,%d" % waves)
-    D1 = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16", B2_bits=B2, epi=epi)
-    monkeypatch.setenv("MOE_GG_TILE", tile + ",0,%d" % waves)
-    D0 = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16", B2_bits=B2, epi=epi)
-    assert torch.equal(D1[:m_rows].view(torch.int16), D0[:m_rows].view(torch.int16))
-    rows = np.random.default_rng(0).choice(m_rows, 64, replace=False).astype(np.int32)
-    ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, B2_bits=B2, epilogue=epi, rows=rows)
-    got = to_f64(D1)[rows]
+    say("gemm pairing", epi, PAIRINGS[pattern])
+    D = _run(A, B, bgc, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16", B2_bits=B2, epi=epi)
+    ref = oracle.grouped_gemm(A, B, bgc, N=N, K=K, B2_bits=B2, epilogue=epi,
+                              rows=np.arange(m_rows, dtype=np.int32))
+    got = to_f64(D)
+    real = np.repeat(bg, 128) >= 0
     if epi == "store":
-        assert np.array_equal(got, ref)
+        assert np.array_equal(got[:m_rows][real], ref[real])
     else:
-        assert_close(got, ref, "split " + tile, max_frac=8e-3, rel_fro=4e-3)
-    assert np.all(np.isnan(to_f64(D1)[m_rows:]))
+        assert_close(got[:m_rows][real], ref[real], "pairing", max_frac=8e-3, rel_fro=4e-3)
+    assert np.all(np.isnan(got[:m_rows][~real]))  # blocks without a group: not written
+    assert np.all(np.isnan(got[m_rows:]))          # rows past num_rows: not written
 
 
-def test_split_tail_random_values_and_repeatability(monkeypatch):
-    # random bf16 values: split and whole paths agree to fp32 summation order,
-    # and the split path is bitwise repeatable
-    G, N, K = 4, 1024, 704
-    nblk = 8 * 40 // 4
-    cap = nblk * 128
-    bg = _groups(nblk, G, 31)
-    g = np.random.default_rng(3)
-    A = syn.bf16_bits(g.standard_normal((cap, K)).astype(np.float32))
-    B = syn.bf16_bits((g.standard_normal((G, K, N)) / np.sqrt(K)).astype(np.float32))
-    say("gemm split random")
-    monkeypatch.setenv("MOE_GG_TILE", "256,3,1,1")
-    D1 = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=cap, dtype="bf16")
-    D1b = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=cap, dtype="bf16")
-    monkeypatch.setenv("MOE_GG_TILE", "256,3,1,0")
-    D0 = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=cap, dtype="bf16")
-    assert torch.equal(D1.view(torch.int16), D1b.view(torch.int16))
-    diff = (D1.float() - D0.float()).abs().max().item()
-    assert diff <= 2 ** -6 * D0.float().abs().max().item()
-    rows = g.choice(cap, 48, replace=False).astype(np.int32)
-    ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, rows=rows)
-    assert_close(to_f64(D1)[rows], ref, "split random")
+def test_padding_rows_not_written():
+    # rows whose source (or epilogue pair) is negative are padding: left untouched
+    K, N, G, T = 128, 256, 3, 200
+    cap = 5 * 128
+    bg = np.array([0, 0, 1, 2, 2], np.int32)
+    g = np.random.default_rng(4)
+    src = g.integers(0, T, size=cap).astype(np.int32)
+    src[g.random(cap) < 0.3] = -1
+    A = syn.ternary_bits((T, K), 70)
+    B = syn.ternary_bits((G, K, N), 71)
+    say("gemm padding rows")
+    D = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=cap, dtype="bf16", src=src, div=1)
+    got = to_f64(D)
+    ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, a_src_row=src, a_src_div=1)
+    assert np.array_equal(got[src >= 0], ref[src >= 0])
+    assert np.all(np.isnan(got[src < 0]))
+    # identity A rows, padding named by the epilogue pair map instead
+    A2 = syn.ternary_bits((cap, K), 72)
+    out = torch.full((cap, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    D2 = moe.grouped_gemm(dev16(A2), dev16(B), torch.from_numpy(bg).cuda(),
+                          torch.tensor([cap], dtype=torch.int32, device="cuda"), N=N, K=K, cap=cap,
+                          row_pair=torch.from_numpy(src).cuda(), out=out)
+    torch.cuda.synchronize()
+    got2 = to_f64(D2)
+    ref2 = oracle.grouped_gemm(A2, B, bg, N=N, K=K)
+    assert np.array_equal(got2[src >= 0], ref2[src >= 0])
+    assert np.all(np.isnan(got2[src < 0]))
 
 
 def _scatter_case(T, k, E, K, N, seed, dtype="bf16"):
@@ -260,14 +269,14 @@ def test_weighted_scatter_integer_exact(dtype, T, k, E, K, N):
     assert np.array_equal(got.cpu().numpy().astype(np.float64), ref)
 
 
-def test_weighted_scatter_accumulates_and_split_tail(monkeypatch):
-    # `out` is accumulated into (the caller zeroes it); the split tail sums
-    # its partial tiles before scattering, so the exact result is unchanged
+def test_weighted_scatter_accumulates_and_tiles(monkeypatch):
+    # `out` is accumulated into (the caller zeroes it); every tile shape gives
+    # the exact result
     T, k, E, K, N = 260, 2, 6, 512, 256
     P, A, B, w = _scatter_case(T, k, E, K, N, seed=5)
     Y = oracle.grouped_gemm(A, B, P["block_expert"], N=N, K=K)
     ref = oracle.weighted_scatter(Y, P["row_to_pair"], w, k, T)
-    for tile in ["256,3,1,0", "256,3,1,1", "128,4,2,1", "64,3,1,0,8"]:
+    for tile in ["256,32,3,6", "256,32,4,4,2", "128,32,3,10", "64,32,4,8"]:
         monkeypatch.setenv("MOE_GG_TILE", tile)
         say("scatter tile", tile)
         base = torch.full((T, N), 3.0, dtype=torch.float32, device="cuda")
