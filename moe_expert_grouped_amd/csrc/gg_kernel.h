@@ -54,9 +54,22 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <utility>
+
 #include "common.h"
 
 namespace moe {
+
+// Compile-time loops: f(I_<0>{}), ..., f(I_<N-1>{}), so register arrays are
+// indexed with constants.
+template <int V> using I_ = std::integral_constant<int, V>;
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_seq(F &&f, std::integer_sequence<int, Is...>) {
+  (f(I_<Is>{}), ...);
+}
+template <int N, class F> __device__ __forceinline__ void static_for(F &&f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 constexpr int kBM = 128;     // rows per block: alignment unit and plan granule
 constexpr int kTM = 256;     // rows per task: one or two blocks of one group
@@ -306,9 +319,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   constexpr int A_GPR = ARP / 16;                     // 16-byte granules per A row
   constexpr int WC = BN / 2;                          // columns per wavefront per matrix
   constexpr int NI = WC / 32;
-  constexpr int KSTEPS = BK / 16;
   constexpr bool SCAT = EPI == kEpiScatter;
-  static_assert(BK == 32 || BK == 64, "slice depth");
+  static_assert(BK == 32, "two 16-deep k steps per slice");
   static_assert(B_INSTR >= 1 && A_INSTR * A_RPI * kWaves == kTM, "DMA split");
   static_assert(NA >= 2 && NBR >= NA, "ring depths");
   static_assert(LA * A_LOADS + LB * B_LOADS < 64, "vmcnt range");
@@ -438,17 +450,31 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
     a_i = i;
     a_k = 0;
   };
+  // The DMA of one A slice: a_prep does the bookkeeping (task switch, k
+  // offset, stage), a_emit(q) issues instruction q, so the consumer can
+  // spread the instructions among its matrix instructions.  Past the end of
+  // the stream the slices still go out, re-reading the last slice into the
+  // stage they would use: that stage was released and is never read again
+  // (the consumer ends first), and every slice keeps the same instruction
+  // count, so the waits are exact and the issue sequence has no branches.
   int a_issued = 0; // A slices issued
-  auto a_issue = [&]() {
-    if (a_issued >= total) return;
-    if (a_k == KT) a_begin(a_i + 1);
-    const int ks = __builtin_amdgcn_readfirstlane(a_k + a_rot < KT ? a_k + a_rot : a_k + a_rot - KT);
-    const uint32_t stage = lds_addr_of(aring) + (a_issued % NA) * A_BYTES;
-#pragma unroll
-    for (int q = 0; q < A_INSTR; ++q)
-      dma16(a_src[q] + (size_t)ks * BK * 2, stage + (wave * A_INSTR + q) * 1024);
-    ++a_k;
+  uint32_t a_koff = 0, a_stage = 0;
+  auto a_prep = [&]() {
+    if (a_issued < total) {
+      if (a_k == KT) a_begin(a_i + 1);
+      const int ks =
+          __builtin_amdgcn_readfirstlane(a_k + a_rot < KT ? a_k + a_rot : a_k + a_rot - KT);
+      a_koff = (uint32_t)(ks * BK * 2);
+      ++a_k;
+    }
+    a_stage = lds_addr_of(aring) + (a_issued % NA) * A_BYTES + wave * A_INSTR * 1024;
     ++a_issued;
+  };
+  auto a_emit = [&](int q) { dma16(a_src[q] + a_koff, a_stage + q * 1024); };
+  auto a_issue = [&]() {
+    a_prep();
+#pragma unroll
+    for (int q = 0; q < A_INSTR; ++q) a_emit(q);
   };
 
   // ---------------- B stream ----------------
@@ -497,23 +523,31 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
     b_i = i;
     b_k = 0;
   };
+  // the B slice's DMA in the same two parts (instruction e: matrix e /
+  // B_INSTR, piece e % B_INSTR), past the end of the stream likewise
   int b_issued = 0;
-  auto b_issue = [&]() {
-    if (b_issued >= total) return;
-    if (b_k == KT) b_begin(b_i + 1);
-    const int ks = __builtin_amdgcn_readfirstlane(b_k + b_rot < KT ? b_k + b_rot : b_k + b_rot - KT);
-    const uint32_t stage = lds_addr_of(bring) + (b_issued % NBR) * BS_BYTES;
-#pragma unroll
-    for (int m = 0; m < NB; ++m)
-#pragma unroll
-      for (int q = 0; q < B_INSTR; ++q) {
-        const size_t off = KN ? ((size_t)ks * BK + q * RPI) * N * 2
-                              : (size_t)ks * BK * 2 + (size_t)q * RPI * K * 2;
-        dma16s(b_off[q % QV], b_base[m] + off,
-               stage + m * B_BYTES + (wave * B_INSTR + q) * 1024);
-      }
-    ++b_k;
+  size_t b_koff = 0;
+  uint32_t b_stage = 0;
+  auto b_prep = [&]() {
+    if (b_issued < total) {
+      if (b_k == KT) b_begin(b_i + 1);
+      const int ks =
+          __builtin_amdgcn_readfirstlane(b_k + b_rot < KT ? b_k + b_rot : b_k + b_rot - KT);
+      b_koff = KN ? (size_t)ks * BK * N * 2 : (size_t)ks * BK * 2;
+      ++b_k;
+    }
+    b_stage = lds_addr_of(bring) + (b_issued % NBR) * BS_BYTES + wave * B_INSTR * 1024;
     ++b_issued;
+  };
+  auto b_emit = [&](int e) {
+    const int m = e / B_INSTR, q = e % B_INSTR;
+    const size_t qoff = KN ? (size_t)q * RPI * N * 2 : (size_t)q * RPI * K * 2;
+    dma16s(b_off[q % QV], b_base[m] + b_koff + qoff, b_stage + m * B_BYTES + q * 1024);
+  };
+  auto b_issue = [&]() {
+    b_prep();
+#pragma unroll
+    for (int e = 0; e < B_LOADS; ++e) b_emit(e);
   };
 
   // prologue: the plan entries of items 0-3 and the tables of items 0-2 --
@@ -535,64 +569,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   }
 
   // ---------------- compute (consumer) ----------------
-  // Fragments of one 16-deep k step, double-buffered in registers.
-  i16x4 fa[2][4][2];
-  i16x4 fb[2][NB][NI][2];
-  auto load_frags = [&](int c, int kk, i16x4(&a)[4][2], i16x4(&b)[NB][NI][2]) {
-    const MOE_LDS unsigned char *sA =
-        (const MOE_LDS unsigned char *)(aring + (c % NA) * A_BYTES);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int row = wm * 128 + mi * 32 + (lane & 31);
-      const int c16 = (kk * 2 + (lane >> 5)) ^ swz_rows<BK>(row);
-      const u32x4 v = *(const MOE_LDS u32x4 *)(sA + row * ARP + c16 * 16);
-      a[mi][0] = __builtin_bit_cast(i16x4, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
-      a[mi][1] = __builtin_bit_cast(i16x4, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
-    }
-    const MOE_LDS unsigned char *sBs =
-        (const MOE_LDS unsigned char *)(bring + (c % NBR) * BS_BYTES);
-#pragma unroll
-    for (int m = 0; m < NB; ++m) {
-      const MOE_LDS unsigned char *sB = sBs + m * B_BYTES;
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        if constexpr (KN) {
-          // lane group G = lane/16 reads columns n0 + 16*(G&1) .. +16 at
-          // k = 8*(G>>1) + 4*r + (lane%16)/4; each lane points at 4
-          // consecutive columns, the transpose read returns 4 k of one column
-          const int G = lane >> 4;
-          const int q = lane & 15;
-          const int n = wn * WC + j * 32 + 16 * (G & 1) + 4 * (q & 3);
-          const int k0 = kk * 16 + 8 * (G >> 1) + (q >> 2);
-          const int k1 = k0 + 4;
-          const int o0 = k0 * (BN * 2) + (((n >> 3) ^ swz_kn<BN>(k0)) << 4) + ((n & 7) << 1);
-          const int o1 = k1 * (BN * 2) + (((n >> 3) ^ swz_kn<BN>(k1)) << 4) + ((n & 7) << 1);
-          b[m][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4 *)(sB + o0));
-          b[m][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4 *)(sB + o1));
-        } else {
-          const int n = wn * WC + j * 32 + (lane & 31);
-          const int c16 = (kk * 2 + (lane >> 5)) ^ swz_rows<BK>(n);
-          const u32x4 v = *(const MOE_LDS u32x4 *)(sB + n * ARP + c16 * 16);
-          b[m][j][0] = __builtin_bit_cast(i16x4, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
-          b[m][j][1] = __builtin_bit_cast(i16x4, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
-        }
-      }
-    }
-  };
-
-  // Slice c+1 (A and B) has landed for this wavefront once at most AFTER
-  // DMA instructions are still in flight (DMA completes in issue order);
-  // near the end of the stream fewer were issued after it, so wait for all.
-  auto wait_slice = [&](int c1) {
-    if (b_issued >= c1 + LB && a_issued >= c1 + LA)
-      wait_vmcnt<AFTER>();
-    else
-      wait_vmcnt<0>();
-  };
-  wait_slice(0);
-  block_barrier();
-  load_frags(0, 0, fa[0], fb[0]);
-
   // The accumulators are carried across items and cleared right after each
   // epilogue has read them, so one register set serves every item.
   f32x16 acc[NB][4][NI];
@@ -610,7 +586,89 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[m][a][j][r] = z;
   };
+
+  // Fragments of one 16-deep k step, double-buffered in registers.
+  i16x4 fa[2][4][2];
+  i16x4 fb[2][NB][NI][2];
+  // LDS read d of the fragments of k step kk of slice c into buffer BUF:
+  // d < 4 the A rows of 32-row group d; then the B columns, two transpose
+  // reads per 32-column group and matrix ([K][N]) or one 16-byte read
+  // ([N][K]).
+  constexpr int ND = 4 + NB * NI * (KN ? 2 : 1); // LDS reads per k step
+  auto frag = [&](auto D, auto BUF, int c, int kk) {
+    constexpr int d = decltype(D)::value;
+    constexpr int buf = decltype(BUF)::value;
+    if constexpr (d < 4) {
+      const MOE_LDS unsigned char *sA =
+          (const MOE_LDS unsigned char *)(aring + (c % NA) * A_BYTES);
+      const int row = wm * 128 + d * 32 + (lane & 31);
+      const int c16 = (kk * 2 + (lane >> 5)) ^ swz_rows<BK>(row);
+      const u32x4 v = *(const MOE_LDS u32x4 *)(sA + row * ARP + c16 * 16);
+      fa[buf][d][0] = __builtin_bit_cast(i16x4, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
+      fa[buf][d][1] = __builtin_bit_cast(i16x4, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
+    } else if constexpr (KN) {
+      constexpr int e = d - 4, m = e / (2 * NI), j = (e / 2) % NI, h = e % 2;
+      const MOE_LDS unsigned char *sB =
+          (const MOE_LDS unsigned char *)(bring + (c % NBR) * BS_BYTES + m * B_BYTES);
+      // lane group G = lane/16 reads columns n0 + 16*(G&1) .. +16 at
+      // k = 8*(G>>1) + 4*h + (lane%16)/4; each lane points at 4
+      // consecutive columns, the transpose read returns 4 k of one column
+      const int G = lane >> 4;
+      const int q = lane & 15;
+      const int n = wn * WC + j * 32 + 16 * (G & 1) + 4 * (q & 3);
+      const int k = kk * 16 + 8 * (G >> 1) + (q >> 2) + 4 * h;
+      const int o = k * (BN * 2) + (((n >> 3) ^ swz_kn<BN>(k)) << 4) + ((n & 7) << 1);
+      fb[buf][m][j][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4 *)(sB + o));
+    } else {
+      constexpr int e = d - 4, m = e / NI, j = e % NI;
+      const MOE_LDS unsigned char *sB =
+          (const MOE_LDS unsigned char *)(bring + (c % NBR) * BS_BYTES + m * B_BYTES);
+      const int n = wn * WC + j * 32 + (lane & 31);
+      const int c16 = (kk * 2 + (lane >> 5)) ^ swz_rows<BK>(n);
+      const u32x4 v = *(const MOE_LDS u32x4 *)(sB + n * ARP + c16 * 16);
+      fb[buf][m][j][0] = __builtin_bit_cast(i16x4, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
+      fb[buf][m][j][1] = __builtin_bit_cast(i16x4, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
+    }
+  };
+  // matrix instruction t of a k step on buffer BUF (row group fastest)
+  constexpr int NM = NB * NI * 4;
+  auto mma = [&](auto T, auto BUF) {
+    constexpr int t = decltype(T)::value;
+    constexpr int buf = decltype(BUF)::value;
+    constexpr int m = t / (4 * NI), j = (t / 4) % NI, mi = t % 4;
+    acc[m][mi][j] = mfma32<FP16>(fa[buf][mi][0], fa[buf][mi][1], fb[buf][m][j][0],
+                                 fb[buf][m][j][1], acc[m][mi][j]);
+  };
+  // DMA instruction q of this slice's share (A first, then B)
+  constexpr int NQ = A_LOADS + B_LOADS;
+  auto dma = [&](auto Q) {
+    constexpr int q = decltype(Q)::value;
+    if constexpr (q < A_LOADS)
+      a_emit(q);
+    else
+      b_emit(q - A_LOADS);
+  };
+  // Interleave: after matrix instruction t come the fragment reads
+  // FPS*t .. FPS*t+FPS-1 and, from slot Q0 on, DPS DMA instructions per
+  // slot; a scheduling fence after every group keeps the order, so the
+  // matrix pipe always has the next instruction queued while the wavefront
+  // issues the others.  The barrier of the last k step comes after BAR
+  // matrix instructions, its fragment reads (of the next slice) after it.
+  constexpr int FPS = 2;
+  constexpr int FSLOTS = (ND + FPS - 1) / FPS;
+  constexpr int Q0 = FSLOTS < NM ? FSLOTS : NM - 1;
+  constexpr int DPS = (NQ + (NM - Q0) - 1) / (NM - Q0);
+  constexpr int BAR = NM >= 8 ? NM / 4 : 0;
+  static_assert(BAR + FSLOTS <= NM, "fragment reads fit the last k step");
+
+  // Slice c+1 (A and B) has landed for this wavefront once at most AFTER
+  // DMA instructions are still in flight (DMA completes in issue order;
+  // every slice, past the end of the stream too, has the same count).
+  wait_vmcnt<AFTER>();
+  block_barrier();
+  static_for<ND>([&](auto D) { frag(D, I_<0>{}, 0, 0); });
   clear_acc();
+
   int c = 0; // slice being consumed (global count)
   for (int i = 0; i < n_items; ++i) {
     // this item's coordinates, read before later fetches may reuse its slot
@@ -618,46 +676,54 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
     coords(i, rt, n0);
     plan_of(i, b, nb, g);
     for (int kt = 0; kt < KT; ++kt, ++c) {
-      const bool has_next = c + 1 < total;
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const int cur = kk & 1;
-        if (kk + 1 < KSTEPS) {
-          // this step's fragments (read during the previous MFMAs) are in:
-          // said explicitly, so no LDS wait lands among the MFMAs below
-          wait_lgkm0();
-          // next k step of this slice; then this wavefront's share of the
-          // next slices' DMA, into the stages every wavefront has released
-          load_frags(c, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
-          if (kk == 0) {
-            a_issue();
-            b_issue();
-          }
-        } else {
-          // this wavefront is done reading stage c (on every path, so the
-          // compiler sees this step's fragments complete and puts no LDS
-          // wait among the MFMAs below)
-          wait_lgkm0();
-          if (has_next) {
-            // slice c+1 has landed for this wavefront ...
-            wait_slice(c + 1);
-            // ... and for every wavefront; and every wavefront is done
-            // reading stage c, which the next issues overwrite
-            block_barrier();
-            load_frags(c + 1, 0, fa[cur ^ 1], fb[cur ^ 1]);
-          }
-        }
-        // keep the fragment reads and the DMA issue ahead of the MFMAs
+      // k step 0 on buffer 0: its fragments (read during the previous
+      // matrix instructions) are in -- said explicitly, so no LDS wait lands
+      // among the matrix instructions; among them, the fragment reads of k
+      // step 1 and this wavefront's share of the next slices' DMA, into the
+      // stages every wavefront released at the last barrier
+      wait_lgkm0();
+      static_for<NM>([&](auto T) {
+        constexpr int t = decltype(T)::value;
+        mma(T, I_<0>{});
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < NB; ++m)
-#pragma unroll
-          for (int j = 0; j < NI; ++j)
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-              acc[m][mi][j] = mfma32<FP16>(fa[cur][mi][0], fa[cur][mi][1], fb[cur][m][j][0],
-                                           fb[cur][m][j][1], acc[m][mi][j]);
-      }
+        static_for<FPS>([&](auto F) {
+          constexpr int d = FPS * t + decltype(F)::value;
+          if constexpr (d < ND) frag(I_<d>{}, I_<1>{}, c, 1);
+        });
+        if constexpr (t == 0) {
+          a_prep();
+          b_prep();
+        }
+        if constexpr (t >= Q0)
+          static_for<DPS>([&](auto P) {
+            constexpr int q = (t - Q0) * DPS + decltype(P)::value;
+            if constexpr (q < NQ) dma(I_<q>{});
+          });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // k step 1 on buffer 1 (its fragments are in: this wavefront is done
+      // reading stage c).  After the last slice the same sequence waits for
+      // and reads the slice past the end of the stream, which was issued like
+      // any other: one branch-free sequence for every slice.
+      wait_lgkm0();
+      static_for<NM>([&](auto T) {
+        constexpr int t = decltype(T)::value;
+        if constexpr (t == BAR) {
+          // slice c+1 has landed for this wavefront ... and for every
+          // wavefront; and every wavefront is done reading stage c, which
+          // the next issues overwrite
+          wait_vmcnt<AFTER>();
+          block_barrier();
+        }
+        mma(T, I_<1>{});
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (t >= BAR)
+          static_for<FPS>([&](auto F) {
+            constexpr int d = FPS * (t - BAR) + decltype(F)::value;
+            if constexpr (d < ND) frag(I_<d>{}, I_<0>{}, c + 1, 0);
+          });
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
 
     // no group: no output; a one-block task has no rows 128-255
