@@ -308,13 +308,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   constexpr int B_LOADS = NB * B_INSTR;
   constexpr int LA = NA - 1;                          // A issue lead (slices)
   constexpr int LB = NBR - 1;                         // B issue lead (slices)
-  // DMA instructions issued, by the end of slice c, after the later of A
-  // slice c+1 and B slice c+1.  A slice c+1 is issued at step c+1-LA,
-  // followed in that step by B slice c+1-LA+LB; with LB > LA, B slice c+1
-  // came in an earlier step, so A slice c+1 is the later one and the B
-  // slice of its step plus LA-1 whole steps follow it; with LB == LA, B
-  // slice c+1 itself is the later one and only the LA-1 whole steps follow.
-  constexpr int AFTER = (LB > LA ? B_LOADS : 0) + (LA - 1) * (A_LOADS + B_LOADS);
+  // DMA instructions issued after the later of A slice 1 and B slice 1 by
+  // the end of the prologue: A slice s is issued with B slice s + LB - LA,
+  // so with LB > LA, A slice 1 is the later one and the B slice issued with
+  // it plus LA - 2 whole pairs follow it; with LB == LA, B slice 1 is the
+  // later one and LA - 2 pairs follow.  (The same count, with LA - 1 pairs,
+  // holds for slice 0, the first wait.)
+  constexpr int NQ = A_LOADS + B_LOADS; // DMA instructions per slice
+  constexpr int AFTER0 = (LB > LA ? B_LOADS : 0) + (LA - 1) * NQ;
+  static_assert(LA >= 2, "the A stream leads by at least two slices");
   constexpr int A_RPI = 1024 / ARP;                   // A rows per DMA instruction
   constexpr int A_GPR = ARP / 16;                     // 16-byte granules per A row
   constexpr int WC = BN / 2;                          // columns per wavefront per matrix
@@ -323,7 +325,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   static_assert(BK == 32, "two 16-deep k steps per slice");
   static_assert(B_INSTR >= 1 && A_INSTR * A_RPI * kWaves == kTM, "DMA split");
   static_assert(NA >= 2 && NBR >= NA, "ring depths");
-  static_assert(LA * A_LOADS + LB * B_LOADS < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) unsigned char aring[NA * A_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char bring[NBR * BS_BYTES];
@@ -640,7 +641,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
                                  fb[buf][m][j][1], acc[m][mi][j]);
   };
   // DMA instruction q of this slice's share (A first, then B)
-  constexpr int NQ = A_LOADS + B_LOADS;
   auto dma = [&](auto Q) {
     constexpr int q = decltype(Q)::value;
     if constexpr (q < A_LOADS)
@@ -648,23 +648,44 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
     else
       b_emit(q - A_LOADS);
   };
-  // Interleave: after matrix instruction t come the fragment reads
-  // FPS*t .. FPS*t+FPS-1 and, from slot Q0 on, DPS DMA instructions per
-  // slot; a scheduling fence after every group keeps the order, so the
-  // matrix pipe always has the next instruction queued while the wavefront
-  // issues the others.  The barrier of the last k step comes after BAR
-  // matrix instructions, its fragment reads (of the next slice) after it.
+  // Interleave: after matrix instruction t of a k step come the fragment
+  // reads FPS*t .. FPS*t+FPS-1 (of the next k step; in the last k step,
+  // from matrix instruction BAR on, of the next slice, after the barrier);
+  // the slice's DMA instructions are spread evenly over both k steps, DMA
+  // q after matrix instruction dslot(q) of the slice's 2 NM.  A wavefront
+  // whose DMA queue is full stalls at its next DMA instruction, so the
+  // issue is kept steady: a burst would stall the matrix pipe and then
+  // leave the memory pipeline idle for the rest of the slice.  A
+  // scheduling fence after every group keeps the order.
   constexpr int FPS = 2;
   constexpr int FSLOTS = (ND + FPS - 1) / FPS;
-  constexpr int Q0 = FSLOTS < NM ? FSLOTS : NM - 1;
-  constexpr int DPS = (NQ + (NM - Q0) - 1) / (NM - Q0);
   constexpr int BAR = NM >= 8 ? NM / 4 : 0;
   static_assert(BAR + FSLOTS <= NM, "fragment reads fit the last k step");
+  constexpr auto dslot = [](int q) { return (2 * NM * q) / NQ + NM / NQ; };
+  // DMA instructions of a slice issued before the wait of its last k step
+  constexpr int D_PRE = [&] {
+    int n = 0;
+    for (int q = 0; q < NQ; ++q) n += dslot(q) < NM + BAR;
+    return n;
+  }();
+  // The wait of slice c's last k step is for slice c+1: A slice c+1 came
+  // with the DMA of slice c+1-LA, B slice c+1 earlier (LB > LA) or with it;
+  // after the later of them come the rest of that slice's DMA (B_LOADS if
+  // A was the later one), LA - 2 whole slices and the D_PRE instructions
+  // of slice c issued so far.
+  constexpr int AFTER = (LB > LA ? B_LOADS : 0) + (LA - 2) * NQ + D_PRE;
+  static_assert(AFTER >= 0 && AFTER < 64 && AFTER0 < 64, "vmcnt range");
+  auto dma_at = [&](auto S) {
+    constexpr int slot = decltype(S)::value;
+    static_for<NQ>([&](auto Q) {
+      if constexpr (dslot(decltype(Q)::value) == slot) dma(Q);
+    });
+  };
 
-  // Slice c+1 (A and B) has landed for this wavefront once at most AFTER
+  // Slice 0 (A and B) has landed for this wavefront once at most AFTER0
   // DMA instructions are still in flight (DMA completes in issue order;
   // every slice, past the end of the stream too, has the same count).
-  wait_vmcnt<AFTER>();
+  wait_vmcnt<AFTER0>();
   block_barrier();
   static_for<ND>([&](auto D) { frag(D, I_<0>{}, 0, 0); });
   clear_acc();
@@ -694,11 +715,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
           a_prep();
           b_prep();
         }
-        if constexpr (t >= Q0)
-          static_for<DPS>([&](auto P) {
-            constexpr int q = (t - Q0) * DPS + decltype(P)::value;
-            if constexpr (q < NQ) dma(I_<q>{});
-          });
+        dma_at(T);
         __builtin_amdgcn_sched_barrier(0);
       });
       // k step 1 on buffer 1 (its fragments are in: this wavefront is done
@@ -722,6 +739,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
             constexpr int d = FPS * (t - BAR) + decltype(F)::value;
             if constexpr (d < ND) frag(I_<d>{}, I_<0>{}, c + 1, 0);
           });
+        dma_at(I_<NM + t>{});
         __builtin_amdgcn_sched_barrier(0);
       });
     }
