@@ -8,6 +8,9 @@
 
 namespace moe {
 hipError_t launch_route(const float *, int, int, int, int32_t *, float *, hipStream_t);
+bool permute_plan_fits(int T, int E, int k);
+hipError_t launch_permute_plan(const int32_t *, int, int, int, int, int32_t *, int32_t *,
+                               int32_t *, int32_t *, int32_t *, int32_t *, int32_t *, hipStream_t);
 size_t permute_workspace_bytes(long R, int E);
 hipError_t launch_permute(const int32_t *, int, int, int, const uint16_t *, int, int32_t *,
                           int32_t *, int32_t *, int32_t *, int32_t *, int32_t *, uint16_t *, int,
@@ -266,12 +269,19 @@ int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
     ridx = idx;
     rw = w;
   }
-  e = moe::launch_permute(ridx, T, k, E, nullptr, 0, counts, offsets, p2r, r2p, bexp, mpad,
-                          nullptr, cap, pws, s);
-  if (e != hipSuccess) return MOE_ERR_DEVICE;
-  // one row-task plan serves both GEMMs (they share the block experts)
-  e = moe::launch_gg_plan(bexp, mpad, cap, plan, s);
-  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  if (moe::permute_plan_fits(T, E, k)) {
+    // permutation and the row-task plan in one launch
+    e = moe::launch_permute_plan(ridx, T, E, k, cap, counts, offsets, p2r, r2p, bexp, mpad, plan,
+                                 s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+  } else {
+    e = moe::launch_permute(ridx, T, k, E, nullptr, 0, counts, offsets, p2r, r2p, bexp, mpad,
+                            nullptr, cap, pws, s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    // one row-task plan serves both GEMMs (they share the block experts)
+    e = moe::launch_gg_plan(bexp, mpad, cap, plan, s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+  }
   e = moe::launch_grouped_gemm(MOE_BF16, I, H, (const uint16_t *)x, r2p, k,
                                (const uint16_t *)w_gate, (const uint16_t *)w_up, MOE_B_KN, plan,
                                MOE_EPI_SILU_MUL, nullptr, nullptr, 0, h, cus, s);

@@ -30,9 +30,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     if (j < k) {
+      // a pair without a row (routed to no valid expert) adds nothing
       const int row = pair_to_row[(size_t)t * k + j];
-      wt[j] = w[(size_t)t * k + j];
-      q[j] = *reinterpret_cast<const u32x4 *>(y + (size_t)row * H + col);
+      wt[j] = row >= 0 ? w[(size_t)t * k + j] : 0.0f;
+      q[j] = row >= 0 ? *reinterpret_cast<const u32x4 *>(y + (size_t)row * H + col)
+                      : u32x4{0u, 0u, 0u, 0u};
     }
   }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};

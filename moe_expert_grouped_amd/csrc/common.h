@@ -38,4 +38,28 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Inclusive prefix sum across the 64 lanes of a wavefront, with DPP lane
+// moves (no LDS permutes): shifts right by 1, 2, 4, 8 inside each row of 16
+// lanes (lanes shifted in from outside the row add 0), then row r adds the
+// last lane of row r - 1 (rows 1 and 3) and rows 2 and 3 add lane 31.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false); // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false); // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false); // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false); // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false); // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false); // row_bcast:31
+  return v;
+}
+
+// Row-task plan of the grouped GEMM, built on the device from the block
+// groups and the padded row count: plan[0] = number of row tasks, plan[1] =
+// number of blocks, then per row task i (one or two consecutive 128-row
+// blocks of one group, paired from the first block of each run of equal
+// groups):  plan[2 + 2 i] = first block | (blocks - 1) << 30,
+//           plan[3 + 2 i] = group.
+constexpr int kPlanHead = 2;
+constexpr int kPlanTwo = 1 << 30;
+inline size_t plan_ints(int cap) { return kPlanHead + 2 * (size_t)(cap / kRowBlock); }
+
 } // namespace moe

@@ -89,14 +89,6 @@ constexpr int kPlanSlots = 8;
 // Epilogues: plain store, SiLU(gate) * up of two B matrices, weighted scatter.
 enum { kEpiStore = 0, kEpiSiluMul = 1, kEpiScatter = 2 };
 
-// Plan of row tasks, built on the device from block_group and the padded
-// row count: plan[0] = number of row tasks, plan[1] = number of blocks, then
-// per row task i:  plan[2 + 2 i] = first block | (blocks - 1) << 30,
-//                  plan[3 + 2 i] = group.
-constexpr int kPlanHead = 2;
-constexpr int kPlanTwo = 1 << 30;
-inline size_t plan_ints(int cap) { return kPlanHead + 2 * (size_t)(cap / kBM); }
-
 struct GGArgs {
   const uint16_t *A;
   const int32_t *a_src_row; // A row of output row r: a_src_row[r] / a_src_div (NULL: r)

@@ -21,8 +21,8 @@
 //                            the same grid marks padding rows with -1
 //   pass 4  permute_gather   optional: x_perm[row] = x[token of row], zero
 //                            rows for padding (16-byte vector copies)
-// Routings of at most 16384 pairs run passes 1-3 as one workgroup
-// (permute_small) in a single launch.
+// Routings of at most 16384 pairs take passes 1-3 in a single launch
+// instead (permute_plan.hip).
 #include "common.h"
 
 namespace moe {
@@ -43,17 +43,6 @@ __global__ __launch_bounds__(kPermThreads) void permute_hist(const int32_t *__re
   for (long p = p0 + threadIdx.x; p < p1; p += blockDim.x) atomicAdd(&cnt[idx[p]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)e * nchunks + c] = cnt[e];
-}
-
-// inclusive prefix sum across the 64 lanes of a wavefront
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
-  return v;
 }
 
 __global__ __launch_bounds__(1024) void permute_scan(
@@ -226,143 +215,11 @@ __global__ __launch_bounds__(256) void permute_gather(const uint16_t *__restrict
   }
 }
 
-// Small routings (R <= kSmallPairs): the same counting sort in one
-// 1024-thread workgroup and one launch -- counts, padded offsets, M_pad,
-// stable ranks (batches of 1024 pairs: ballot match inside each wavefront,
-// per-wavefront counts in LDS across the 16 wavefronts), row maps, block
-// experts and padding marks.
-constexpr int kSmallPairs = 16384;
-constexpr int kSmallThreads = 1024;
-constexpr int kSmallMaxE = 512;
-// row capacity bound of the small path: ceil128(16384 + 512 * 127) / 128
-constexpr int kSmallMaxBlocks = (kSmallPairs + kSmallMaxE * 127 + 127) / 128;
-
-__global__ __launch_bounds__(kSmallThreads) void permute_small(
-    const int32_t *__restrict__ idx, int R, int E, int cap, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ pair_to_row,
-    int32_t *__restrict__ row_to_pair, int32_t *__restrict__ block_expert,
-    int32_t *__restrict__ num_padded_rows) {
-  constexpr int kWaves = kSmallThreads / 64;
-  __shared__ int cnt[kMaxExperts];
-  __shared__ int off[kMaxExperts + 1];
-  __shared__ int wave_tot[kWaves];
-  __shared__ int bexp[kSmallMaxBlocks];
-  extern __shared__ int wcount_dyn[]; // [kWaves][E]
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-
-  // every key this thread will rank, loaded once (one memory latency, not
-  // one per batch)
-  constexpr int kKeys = kSmallPairs / kSmallThreads;
-  int keys[kKeys];
-#pragma unroll
-  for (int j = 0; j < kKeys; ++j) {
-    const int p = j * kSmallThreads + tid;
-    keys[j] = p < R ? idx[p] : E;
-  }
-  for (int e = tid; e < E; e += kSmallThreads) {
-    cnt[e] = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) wcount_dyn[w * E + e] = 0;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kKeys; ++j)
-    if (keys[j] < E) atomicAdd(&cnt[keys[j]], 1);
-  __syncthreads();
-
-  // exclusive scan of padded counts (one thread per expert)
-  const int padded = tid < E ? (cnt[tid] + kRowBlock - 1) / kRowBlock * kRowBlock : 0;
-  const int incl = wave_incl_scan(padded);
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wave_tot[w];
-  if (tid < E) {
-    off[tid] = before + incl - padded;
-    counts[tid] = cnt[tid];
-    offsets[tid] = before + incl - padded;
-  }
-  if (tid == E - 1) {
-    off[E] = before + incl;
-    offsets[E] = before + incl;
-    num_padded_rows[0] = before + incl;
-  }
-  __syncthreads();
-  const int m_pad = off[E];
-  // cnt[] becomes the next free row of each expert
-  for (int e = tid; e < E; e += kSmallThreads) cnt[e] = off[e];
-  int nbits = 1;
-  while ((1 << nbits) <= E) ++nbits;
-  __syncthreads();
-
-  const unsigned long long lt_mask = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int j = 0; j < kKeys; ++j) {
-    if (j * kSmallThreads >= R) break; // uniform
-    const int p = j * kSmallThreads + tid;
-    const bool valid = p < R;
-    const int key = keys[j];
-    unsigned long long same = ~0ull;
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (key >> b) & 1;
-      const unsigned long long bal = __ballot(bit);
-      same &= bit ? bal : ~bal;
-    }
-    const int rank = __popcll(same & lt_mask);
-    const bool leader = rank == 0;
-    const bool last = (same >> lane) == 1ull;
-    if (valid && leader) wcount_dyn[wave * E + key] = __popcll(same);
-    __syncthreads();
-    int row = 0;
-    bool last_overall = false;
-    if (valid) {
-      int bef = 0, aft = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const int n = wcount_dyn[w * E + key];
-        if (w < wave) bef += n;
-        if (w > wave) aft += n;
-      }
-      row = cnt[key] + bef + rank;
-      last_overall = last && aft == 0;
-      pair_to_row[p] = row;
-      row_to_pair[row] = p;
-    }
-    __syncthreads();
-    if (valid && last_overall) cnt[key] = row + 1;
-    if (valid && leader) wcount_dyn[wave * E + key] = 0;
-    __syncthreads();
-  }
-
-  // block experts (kept in LDS), then -1 on padding rows and rows beyond M_pad:
-  // after the ranking loop cnt[e] = off[e] + counts[e], and rows of expert e
-  // at or past it are padding
-  const int nblk = cap / kRowBlock;
-  for (int b = tid; b < nblk; b += kSmallThreads) {
-    const int r = b * kRowBlock;
-    int ex = -1;
-    if (r < m_pad) {
-      int lo = 0, hi = E - 1; // largest e with off[e] <= r
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= r)
-          lo = mid;
-        else
-          hi = mid - 1;
-      }
-      ex = lo;
-    }
-    block_expert[b] = ex;
-    bexp[b] = ex;
-  }
-  __syncthreads();
-  for (int r = tid; r < cap; r += kSmallThreads) {
-    const int ex = bexp[r / kRowBlock];
-    if (ex < 0 || r >= cnt[ex]) row_to_pair[r] = -1;
-  }
-}
+bool permute_plan_fits(int T, int E, int k);
+hipError_t launch_permute_plan(const int32_t *idx, int T, int E, int k, int cap, int32_t *counts,
+                               int32_t *offsets, int32_t *pair_to_row, int32_t *row_to_pair,
+                               int32_t *block_expert, int32_t *num_padded_rows, int32_t *plan,
+                               hipStream_t stream);
 
 size_t permute_workspace_bytes(long R, int E) {
   const long nchunks = (R + kPermChunk - 1) / kPermChunk;
@@ -374,14 +231,14 @@ hipError_t launch_permute(const int32_t *idx, int T, int k, int E, const uint16_
                           int32_t *row_to_pair, int32_t *block_expert,
                           int32_t *num_padded_rows, uint16_t *x_perm, int cap, void *ws,
                           hipStream_t stream) {
-  const long R = (long)T * k;
-  if (R <= kSmallPairs && E <= kSmallMaxE && cap / kRowBlock <= kSmallMaxBlocks) {
-    // dynamic LDS: 16 * E * 4 bytes <= 32 KiB
-    const size_t dyn = (size_t)(kSmallThreads / 64) * E * sizeof(int32_t);
-    permute_small<<<1, kSmallThreads, dyn, stream>>>(idx, (int)R, E, cap, counts, offsets,
-                                                     pair_to_row, row_to_pair, block_expert,
-                                                     num_padded_rows);
+  if (permute_plan_fits(T, E, k)) {
+    // up to 16384 pairs: one launch (permute_plan.hip)
+    const hipError_t e = launch_permute_plan(idx, T, E, k, cap, counts, offsets, pair_to_row,
+                                             row_to_pair, block_expert, num_padded_rows, nullptr,
+                                             stream);
+    if (e != hipSuccess) return e;
   } else {
+    const long R = (long)T * k;
     const int nchunks = (int)((R + kPermChunk - 1) / kPermChunk);
     int32_t *hist = reinterpret_cast<int32_t *>(ws);
     int32_t *base = hist + (size_t)E * nchunks;

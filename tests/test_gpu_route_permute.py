@@ -93,3 +93,88 @@ def test_permute_repeatable():
     b = moe.permute(idx, 64)
     torch.cuda.synchronize()
     assert torch.equal(a.pair_to_row, b.pair_to_row) and torch.equal(a.row_to_pair, b.row_to_pair)
+
+
+def _small_layer_inputs(T, H, E, k, I, seed):
+    g = np.random.default_rng(seed)
+    logits = g.standard_normal((T, E)).astype(np.float32)
+    bits = lambda shape: syn.bf16_bits((g.standard_normal(shape) * 0.05).astype(np.float32))
+    return (logits, dev16(bits((T, H))), dev16(bits((E, H, I))), dev16(bits((E, H, I))),
+            dev16(bits((E, I, H))))
+
+
+# shapes of every variant of the one-launch routing + permutation + plan
+# (tokens per thread 1, 2, 4 x top-k list of 4, 8, 16) and one shape that
+# takes the separate kernels instead (E not a multiple of 4)
+@pytest.mark.parametrize("T,E,k", [(256, 8, 2), (1000, 64, 8), (64, 1024, 16), (2048, 64, 4),
+                                   (2000, 16, 7), (4096, 32, 4), (77, 5, 5)])
+def test_layer_routing_permutation_and_plan(T, E, k):
+    H = I = 64
+    logits, x, wg, wu, wd = _small_layer_inputs(T, H, E, k, I, T + E + k)
+    lg = torch.from_numpy(logits).cuda()
+    say("layer routing + permutation + plan", "T", T, "E", E, "k", k)
+    ws = moe.layer_workspace(T, H, E, k, I)
+    moe.layer(x, wg, wu, wd, k, logits=lg, workspace=ws)
+    idx, w = moe.route(lg, k)
+    torch.cuda.synchronize()
+    view = lambda n: moe.workspace_view(ws, T, H, E, k, I, n).cpu().numpy()
+    # the layer's routing: the same bits as the routing entry point
+    assert np.array_equal(view("topk_idx"), idx.cpu().numpy())
+    assert np.array_equal(view("topk_w").view(np.uint32), w.cpu().numpy().view(np.uint32))
+    assert np.array_equal(idx.cpu().numpy(), oracle.route(logits, k)[0])
+    ref = oracle.permute(idx.cpu().numpy(), E)
+    for name, key in (("expert_counts", "counts"), ("expert_offsets", "offsets"),
+                      ("pair_to_row", "pair_to_row"), ("row_to_pair", "row_to_pair"),
+                      ("block_expert", "block_expert")):
+        assert np.array_equal(view(name), ref[key]), name
+    assert int(view("num_padded_rows")[0]) == ref["m_pad"]
+    # the layer's row-task plan: the same as the grouped GEMM's own plan kernel
+    P = moe.permute(idx, E)
+    cap = P.cap
+    gws = torch.zeros(moe.gemm_workspace(cap).numel(), dtype=torch.uint8, device="cuda")
+    say("plan reference", "cap", cap)
+    moe.grouped_gemm(x, wg, P.block_expert, P.num_padded_rows, N=I, K=H, cap=cap,
+                     a_src_row=P.row_to_pair, a_src_div=k, B2=wu, epilogue="silu_mul",
+                     workspace=gws)
+    torch.cuda.synchronize()
+    lay = moe.layer_workspace_layout(T, H, E, k, I)
+    n = 2 + 2 * (cap // 128)
+    plan = ws[lay["gemm_scratch"]:lay["gemm_scratch"] + 4 * n].view(torch.int32).cpu().numpy()
+    plan_ref = gws[:4 * n].view(torch.int32).cpu().numpy()
+    used = 2 + 2 * int(plan_ref[0])
+    assert np.array_equal(plan[:used], plan_ref[:used])
+
+
+def test_permute_skips_invalid_ids():
+    # expert ids outside [0, E) get no row; the valid pairs are still a stable
+    # counting sort (checked by its defining properties)
+    g = np.random.default_rng(21)
+    T, k, E = 700, 3, 8
+    idx = g.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[::7, 0] = -3
+    idx[::11, 2] = E
+    idx[5, 1] = 1 << 20
+    say("permute invalid ids")
+    P = moe.permute(torch.from_numpy(idx).cuda(), E)
+    torch.cuda.synchronize()
+    flat = idx.ravel()
+    valid = (flat >= 0) & (flat < E)
+    p2r = P.pair_to_row.cpu().numpy()
+    r2p = P.row_to_pair.cpu().numpy()
+    bexp = P.block_expert.cpu().numpy()
+    counts = np.bincount(flat[valid], minlength=E)
+    assert np.array_equal(P.counts.cpu().numpy(), counts)
+    padded = (counts + 127) // 128 * 128
+    offs = np.concatenate([[0], np.cumsum(padded)])
+    assert np.array_equal(P.offsets.cpu().numpy(), offs)
+    assert np.all(p2r[~valid] == -1)
+    pv = np.nonzero(valid)[0]
+    rows = p2r[pv]
+    assert np.array_equal(r2p[rows], pv)
+    for e in range(E):
+        re = rows[flat[pv] == e]
+        assert np.array_equal(re, np.arange(offs[e], offs[e] + counts[e]))
+        assert np.all(bexp[offs[e] // 128:offs[e + 1] // 128] == e)
+    real = np.zeros(P.cap, bool)
+    real[rows] = True
+    assert np.all(r2p[~real] == -1)
