@@ -205,47 +205,54 @@ __device__ __forceinline__ void task_coords(int task, int GR, int ncol, int nrt,
   n0 = n * bn;
 }
 
-// Epilogue of one wavefront's share of a tile for STORE and SILU_MUL: every
-// 32 x 32 accumulator tile goes, 16 rows at a time, through a per-wavefront
-// LDS tile so that each lane writes one 16-byte row piece (the MFMA layout
-// gives each lane one column of 4-row groups; registers 0-7 hold rows 0-15,
-// registers 8-15 rows 16-31).  Rows whose entry in `skip` (the task's pair
-// table, if any) is negative are padding and are not written.
-constexpr int kEpiLd = 40; // row pitch (elements) of the staging tile
+// Epilogue of one wavefront's share of a tile for STORE and SILU_MUL.  These
+// epilogues run the matrix instructions with the operands swapped (weights
+// as the first operand), so each 32 x 32 accumulator tile is the transpose:
+// register 4 q + e of lane l holds row l % 32, column 8 q + 4 (l / 32) + e.
+// A lane thus owns 4 consecutive columns of one row and stores them as one
+// 8-byte piece straight from its registers (lanes l and l + 32 together
+// write 16 contiguous bytes of the row), with no LDS staging.  Rows whose
+// entry in `skip` (the task's pair table, if any) is negative are padding and
+// are not written.
 template <int NB, bool FP16, int MI, int NI>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint16_t *Dt, int N,
-                                           MOE_LDS uint16_t *stg,
                                            const MOE_LDS int32_t *skip, int lane, int row0,
                                            int col0) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < MI; ++i) {
+    const int trow = row0 + i * 32 + (lane & 31); // row inside the task
+    const bool keep = !skip || skip[trow] >= 0;
+    // byte offset inside the task's tile (< 2^32): the address is the
+    // wave-uniform tile base plus one 32-bit register
+    const uint32_t rowoff = (uint32_t)((trow * N + col0 + 4 * (lane >> 5)) * 2);
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
+    for (int j = 0; j < NI; ++j) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int q = 0; q < 4; ++q) {
+        uint32_t pk[2];
 #pragma unroll
-        for (int r = 8 * h; r < 8 * h + 8; ++r) {
-          const int row = 8 * ((r >> 2) & 1) + 4 * (lane >> 5) + (r & 3);
-          float v = acc_read(acc[0][i][j][r]);
-          if constexpr (NB == 2) {
-            const float u = acc_read(acc[1][i][j][r]);
-            v = v / (1.0f + __expf(-v)) * u;
+        for (int h = 0; h < 2; ++h) {
+          uint16_t o[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            float v = acc_read(acc[0][i][j][4 * q + 2 * h + e]);
+            if constexpr (NB == 2) {
+              const float u = acc_read(acc[1][i][j][4 * q + 2 * h + e]);
+              v = v / (1.0f + __expf(-v)) * u;
+            }
+            o[e] = FP16 ? f32_to_f16(v) : f32_to_bf16(v);
           }
-          stg[row * kEpiLd + (lane & 31)] = FP16 ? f32_to_f16(v) : f32_to_bf16(v);
+          pk[h] = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
         }
-        const int row = lane >> 2;
-        const int col = (lane & 3) * 8;
-        const int trow = row0 + i * 32 + 16 * h + row; // row inside the task
-        const u32x4 q = *(const MOE_LDS u32x4 *)(stg + row * kEpiLd + col);
-        // byte offset inside the task's tile (< 2^32): the address is the
-        // wave-uniform tile base plus one 32-bit register
-        const uint32_t off = (uint32_t)((trow * N + col0 + j * 32 + col) * 2);
-        if (!skip || skip[trow] >= 0)
-          *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(Dt) + off) = q;
-        // one 16-row piece at a time: unrolled freely, the scheduler would
-        // overlap all of them and hold ~100 registers of temporaries
-        __builtin_amdgcn_sched_barrier(0);
+        if (keep)
+          *reinterpret_cast<uint2 *>(reinterpret_cast<unsigned char *>(Dt) + rowoff +
+                                     (j * 32 + 8 * q) * 2) = uint2{pk[0], pk[1]};
       }
+      // one 32 x 32 tile at a time: unrolled freely, the scheduler would
+      // convert every tile at once and hold ~100 registers of temporaries
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
 }
 
 // Weighted-scatter epilogue of one wavefront's share of a tile: task row r
@@ -327,7 +334,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   __shared__ __attribute__((aligned(16))) int32_t etab[SCAT ? kTabSlots : 1][SCAT ? kTM : 1];
   __shared__ __attribute__((aligned(16))) float wtab[SCAT ? kTabSlots : 1][SCAT ? kTM : 1];
   __shared__ __attribute__((aligned(16))) int32_t ptab[kWaves][kPlanSlots][2]; // plan entries
-  __shared__ __attribute__((aligned(16))) uint16_t epi_lds[SCAT ? 1 : kWaves][SCAT ? 1 : 16 * kEpiLd];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -629,8 +635,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
     constexpr int t = decltype(T)::value;
     constexpr int buf = decltype(BUF)::value;
     constexpr int m = t / (4 * NI), j = (t / 4) % NI, mi = t % 4;
-    acc[m][mi][j] = mfma32<FP16>(fa[buf][mi][0], fa[buf][mi][1], fb[buf][m][j][0],
-                                 fb[buf][m][j][1], acc[m][mi][j]);
+    // the weighted scatter keeps the row-major accumulator layout (its fp32
+    // atomics then cover 32 contiguous columns per row); the stores take the
+    // transposed one (weights as the first operand)
+    if constexpr (SCAT)
+      acc[m][mi][j] = mfma32<FP16>(fa[buf][mi][0], fa[buf][mi][1], fb[buf][m][j][0],
+                                   fb[buf][m][j][1], acc[m][mi][j]);
+    else
+      acc[m][mi][j] = mfma32<FP16>(fb[buf][m][j][0], fb[buf][m][j][1], fa[buf][mi][0],
+                                   fa[buf][mi][1], acc[m][mi][j]);
   };
   // DMA instruction q of this slice's share (A first, then B)
   auto dma = [&](auto Q) {
@@ -744,7 +757,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
                             args.topk, lane, wm * 128, n0 + wn * WC);
       } else {
         store_tile<NB, FP16, 4, NI>(acc, args.D + (size_t)b * kBM * N + n0, N,
-                                    (MOE_LDS uint16_t *)epi_lds[wave],
                                     has_tab ? pair_table(s) : nullptr, lane, wm * 128, wn * WC);
       }
     }
