@@ -130,7 +130,10 @@ def main():
         if it >= a.warmup:
             timed.append(e)
     torch.cuda.synchronize()
-    dur = {n: float(np.mean([es[i].elapsed_time(es[i + 1]) for es in timed])) for i, n in enumerate(names)}
+    # medians: a stalled host iteration (the GPU idles waiting for a launch)
+    # would otherwise move the mean
+    dur = {n: float(np.median([es[i].elapsed_time(es[i + 1]) for es in timed]))
+           for i, n in enumerate(names)}
     # the weighted-scatter down GEMM and its finalize, same inputs
     acc = torch.empty((T, H), dtype=torch.float32, device="cuda")
     sc = []
@@ -147,7 +150,7 @@ def main():
         if it >= a.warmup:
             sc.append(e)
     torch.cuda.synchronize()
-    dur_sc = {n: float(np.mean([es[i].elapsed_time(es[i + 1]) for es in sc]))
+    dur_sc = {n: float(np.median([es[i].elapsed_time(es[i + 1]) for es in sc]))
               for i, n in enumerate(["zero", "down_scatter", "finalize"])}
     m_pad = int(P.num_padded_rows.item())
     counts = P.counts.cpu().numpy()
