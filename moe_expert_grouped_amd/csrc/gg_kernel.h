@@ -551,17 +551,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
 
   // prologue: the plan entries of items 0-3 and the tables of items 0-2 --
   // all the prologue's streams can reach (the B stream at most item 1, as
-  // 2 KT >= NBR - 1) and what their task starts fetch for later ones; then
-  // the B stream and the A stream start on item 0 and issue the first LB B
-  // slices and LA A slices, A slice s right before B slice s + LB - LA, the
-  // order of the main loop
+  // 2 KT >= NBR - 1) and what their task starts fetch for later ones.  The B
+  // stream needs only plan entries, so it starts while the tables are in
+  // flight: its first LB - LA slices go out, then the A stream (whose row
+  // addresses come from the tables) joins, A slice s right before B slice
+  // s + LB - LA, the order of the main loop.  The tables were issued before
+  // at least (LB - LA) B_LOADS DMA instructions (task starts may add more,
+  // which only makes the wait stricter).
   for (int j = 0; j < 4 && j < n_items; ++j) fetch_plan(j);
   wait_vmcnt<0>();
   for (int j = 0; j < 3 && j < n_items; ++j) fetch_tables(j);
-  wait_vmcnt<0>();
   b_begin(0);
-  a_begin(0);
   for (int s = 0; s < LB - LA; ++s) b_issue();
+  wait_vmcnt<(LB - LA) * B_LOADS>();
+  a_begin(0);
   for (int s = 0; s < LA; ++s) {
     a_issue();
     b_issue();
