@@ -83,9 +83,17 @@ def main():
     tw = torch.from_numpy(d["topk_w"]).cuda() if given else None
     ws = moe.layer_workspace(T, H, E, k, I)
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    # gate and up weights interleaved in 128-column blocks, once, before any
+    # timing (a weight-load transform: the gate/up GEMM then streams each k row
+    # of a weight tile as one 512-byte piece); the plain layout is timed too
+    packed = I % 128 == 0
+    wgu = moe.pack_gate_up(wg, wu) if packed else wg
+    wu_arg = None if packed else wu
+    torch.cuda.synchronize()
 
     def step():
-        moe.layer(x, wg, wu, wd, k, logits=logits, topk_idx=tidx, topk_w=tw, workspace=ws, out=out)
+        moe.layer(x, wgu, wu_arg, wd, k, logits=logits, topk_idx=tidx, topk_w=tw, workspace=ws,
+                  out=out)
 
     for _ in range(a.warmup):
         step()
@@ -99,12 +107,19 @@ def main():
     stats = step_stats(step, a.steps)
 
     def step_scatter():
-        moe.layer(x, wg, wu, wd, k, logits=logits, topk_idx=tidx, topk_w=tw, workspace=ws, out=out,
-                  combine="scatter")
+        moe.layer(x, wgu, wu_arg, wd, k, logits=logits, topk_idx=tidx, topk_w=tw, workspace=ws,
+                  out=out, combine="scatter")
 
     for _ in range(a.warmup):
         step_scatter()
     stats_scatter = step_stats(step_scatter, a.steps, cold=False)
+
+    def step_unpacked():
+        moe.layer(x, wg, wu, wd, k, logits=logits, topk_idx=tidx, topk_w=tw, workspace=ws, out=out)
+
+    for _ in range(a.warmup):
+        step_unpacked()
+    stats_unpacked = step_stats(step_unpacked, a.steps, cold=False)
 
     # ---- per-kernel durations: HIP events on the launch stream, same path step by step
     stream = torch.cuda.current_stream()
@@ -120,8 +135,9 @@ def main():
         e[1].record(stream)
         P = moe.permute(idx_t, E)
         e[2].record(stream)
-        h = moe.grouped_gemm(x, wg, P.block_expert, P.num_padded_rows, N=I, K=H, cap=P.cap,
-                             a_src_row=P.row_to_pair, a_src_div=k, B2=wu, epilogue="silu_mul")
+        h = moe.grouped_gemm(x, wgu, P.block_expert, P.num_padded_rows, N=I, K=H, cap=P.cap,
+                             a_src_row=P.row_to_pair, a_src_div=k, B2=wu_arg, epilogue="silu_mul",
+                             b_layout="kn_gate_up" if packed else "kn")
         e[3].record(stream)
         y = moe.grouped_gemm(h, wd, P.block_expert, P.num_padded_rows, N=H, K=I, cap=P.cap)
         e[4].record(stream)
@@ -181,12 +197,15 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "%s MoE layer share" % a.config, "T": T, "H": H, "E": E, "top_k": k,
-                   "I": I, "routing": cfg.get("routing"), "m_pad": m_pad, "active_experts": e_act},
+                   "I": I, "routing": cfg.get("routing"), "m_pad": m_pad, "active_experts": e_act,
+                   "gate_up_weights": ("interleaved in 128-column blocks (moe_pack_gate_up, once "
+                                       "before timing)") if packed else "separate [E][H][I]"},
         "layer_us": round(ms * 1e3, 2),
         "gemm_tflops": round(gemm_flops / gemm_s / 1e12, 2),
         "gemm_mfma_peak_frac": round(gemm_flops / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernel_us": {n: round(v * 1e3, 2) for n, v in dur.items()},
         "layer_us_per_step": stats,
+        "unpacked_gate_up_weights": {"layer_us_per_step": stats_unpacked},
         "scatter_combine": {"layer_us_per_step": stats_scatter,
                             "kernel_us": {n: round(v * 1e3, 2) for n, v in dur_sc.items()}},
         "measured_peaks": measured_peaks(),

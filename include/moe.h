@@ -65,6 +65,12 @@ extern "C" {
 /* Layout of the per-group B operand of grouped_gemm. */
 #define MOE_B_KN 0 /* B[g] is [K][N], N contiguous (expert weights [E,H,I] / [E,I,H]) */
 #define MOE_B_NK 1 /* B[g] is [N][K], K contiguous (the dense D = A * B^T case)      */
+/* B[g] is [K][2N] with the gate and up weights of MOE_EPI_SILU_MUL interleaved
+ * in 128-column blocks: row k holds, for each block b of 128 output columns,
+ * gate columns 128b .. 128b+127 then up columns 128b .. 128b+127
+ * (moe_pack_gate_up builds it).  Each k row of a task's weight tile is then
+ * one contiguous 512-byte piece instead of two 256-byte ones. */
+#define MOE_B_KN_GATE_UP 2
 
 /* Epilogues of grouped_gemm. */
 #define MOE_EPI_STORE 0    /* D[r][n] = round(acc)                              */
@@ -143,7 +149,10 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, const void *x,
  *              D of MOE_EPI_WEIGHTED_SCATTER, which is fp32)
  *   A          [*][K]   (rows addressed by a(r))
  *   B, B2      [G][K][N] (MOE_B_KN) or [G][N][K] (MOE_B_NK); B2 only for
- *              MOE_EPI_SILU_MUL (the up weights; B holds the gate weights)
+ *              MOE_EPI_SILU_MUL (the up weights; B holds the gate weights).
+ *              MOE_B_KN_GATE_UP: B is [G][K][2N], gate and up interleaved
+ *              (see the define), B2 must be NULL, the epilogue must be
+ *              MOE_EPI_SILU_MUL and N % 128 == 0.
  *   D          [cap][N] for MOE_EPI_STORE and MOE_EPI_SILU_MUL.
  *   epi_row_pair  optional for MOE_EPI_STORE / MOE_EPI_SILU_MUL: rows r with
  *              epi_row_pair[r] < 0 are padding and are not written (the MoE
@@ -169,6 +178,20 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, const void *x,
  * aligned, contents need not be initialized (MOE_ERR_WORKSPACE otherwise).
  * ---------------------------------------------------------------------- */
 size_t grouped_gemm_workspace_size(int cap);
+
+/* ------------------------------------------------------------------------
+ * moe_pack_gate_up -- the MOE_B_KN_GATE_UP weight layout from separate gate
+ * and up weights (a one-time weight transform, like loading a checkpoint
+ * into the layout the GEMM streams best; no arithmetic).
+ *   w_gate, w_up  [E][K][N] 16-bit (bf16 or fp16; the bits are copied)
+ *   out           [E][K][2N]: out[e][k][256 b + c]       = w_gate[e][k][128 b + c],
+ *                             out[e][k][256 b + 128 + c] = w_up[e][k][128 b + c]
+ *                 for c < 128.
+ * Requires N % 128 == 0; all pointers 16-byte aligned device pointers,
+ * out not overlapping the inputs.
+ * ---------------------------------------------------------------------- */
+int moe_pack_gate_up(const void *w_gate, const void *w_up, int E, int K, int N, void *out,
+                     void *stream);
 int grouped_gemm(int dtype, int N, int K, int cap, const void *A,
                  const int32_t *a_src_row, int a_src_div, const void *B,
                  const void *B2, int b_layout, const int32_t *block_group,
@@ -202,6 +225,9 @@ int moe_finalize(const float *acc, size_t n, void *out, void *stream);
  * topk_idx_in / topk_w_in give it.
  *   x [T][H] bf16; w_gate, w_up [E][H][I] bf16; w_down [E][I][H] bf16;
  *   out [T][H] bf16.
+ *   w_up == NULL: w_gate is the packed [E][H][2I] tensor of
+ *   moe_pack_gate_up (MOE_B_KN_GATE_UP; requires I % 128 == 0), which the
+ *   gate/up GEMM streams as contiguous 512-byte row pieces.
  * Intermediates: h = SiLU(gate)*up stored as bf16 [M_pad][I], expert outputs
  * y stored as bf16 [M_pad][H]; both live in the workspace.  The combine is
  * MOE_COMBINE_GATHER (deterministic: same input, same bits).

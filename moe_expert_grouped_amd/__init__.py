@@ -36,7 +36,7 @@ ROW_BLOCK = 128
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 _DTYPES = {torch.bfloat16: 0, torch.float16: 1}
-_LAYOUTS = {"kn": 0, "nk": 1}
+_LAYOUTS = {"kn": 0, "nk": 1, "kn_gate_up": 2}
 _EPIS = {"store": 0, "silu_mul": 1, "weighted_scatter": 2}
 _COMBINES = {"gather": 0, "scatter": 1}
 
@@ -70,6 +70,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "grouped_gemm": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P, I, P, P, Z, P], I),
             "moe_combine": ([P, I, P, P, I, I, P, P], I),
             "moe_finalize": ([P, Z, P, P], I),
+            "moe_pack_gate_up": ([P, P, I, I, I, P, P], I),
             "moe_layer_workspace_size": ([I, I, I, I, I], Z),
             "moe_layer_workspace_layout": ([I, I, I, I, I, ctypes.POINTER(Z)], I),
             "moe_layer": ([P, P, P, P, P, P, P, I, I, I, I, I, P, P, Z, P], I),
@@ -267,6 +268,27 @@ def combine(y: torch.Tensor, pair_to_row: torch.Tensor, topk_w: torch.Tensor,
     return out
 
 
+def pack_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """The interleaved gate/up weight layout (b_layout="kn_gate_up"): [E][K][2N]
+    with, per block of 128 output columns, the 128 gate columns then the 128
+    up columns.  A copy on the device."""
+    _need(w_gate, "w_gate", (torch.bfloat16, torch.float16), 3)
+    _need(w_up, "w_up", w_gate.dtype, 3)
+    if w_up.shape != w_gate.shape:
+        raise ValueError("w_gate and w_up must have the same shape")
+    E, K, N = w_gate.shape
+    if out is None:
+        out = torch.empty((E, K, 2 * N), dtype=w_gate.dtype, device=w_gate.device)
+    else:
+        _need(out, "out", w_gate.dtype, 3)
+        if tuple(out.shape) != (E, K, 2 * N):
+            raise ValueError("out must be [E, K, 2N]")
+    _check("moe_pack_gate_up", load_library().moe_pack_gate_up(
+        _ptr(w_gate), _ptr(w_up), E, K, N, _ptr(out), _stream()))
+    return out
+
+
 def finalize(acc: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """out = bf16(acc), round to nearest even (the weighted-scatter combine's last step)."""
     _need(acc, "acc", torch.float32)
@@ -306,14 +328,18 @@ def layer(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: tor
           out: torch.Tensor | None = None, combine: str = "gather") -> torch.Tensor:
     """The MoE layer share: route (or the given routing) -> permute -> gate/up
     grouped GEMM with SiLU*up -> down grouped GEMM -> top-k weighted combine.
+    w_up=None: w_gate is the interleaved [E][H][2I] tensor of pack_gate_up.
     combine="gather" (deterministic) stores y and runs the combine kernel;
     "scatter" folds the weighted sum into the down GEMM's epilogue."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w_gate, "w_gate", torch.bfloat16, 3)
-    _need(w_up, "w_up", torch.bfloat16, 3)
+    if w_up is not None:
+        _need(w_up, "w_up", torch.bfloat16, 3)
     _need(w_down, "w_down", torch.bfloat16, 3)
     T, H = x.shape
     E, _, I = w_gate.shape
+    if w_up is None:  # w_gate is pack_gate_up(gate, up): [E][H][2I]
+        I //= 2
     if logits is not None:
         _need(logits, "logits", torch.float32, 2)
     else:

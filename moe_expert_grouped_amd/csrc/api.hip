@@ -8,6 +8,8 @@
 
 namespace moe {
 hipError_t launch_route(const float *, int, int, int, int32_t *, float *, hipStream_t);
+hipError_t launch_pack_gate_up(const uint16_t *, const uint16_t *, int, int, int, uint16_t *,
+                               hipStream_t);
 bool permute_plan_fits(int T, int E, int k);
 hipError_t launch_permute_plan(const int32_t *, int, int, int, int, int32_t *, int32_t *,
                                int32_t *, int32_t *, int32_t *, int32_t *, int32_t *, hipStream_t);
@@ -138,11 +140,18 @@ int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t 
     return MOE_ERR_INVALID;
   if (N <= 0 || K <= 0 || cap <= 0) return MOE_ERR_INVALID;
   if (dtype != MOE_BF16 && dtype != MOE_FP16) return MOE_ERR_UNSUPPORTED;
-  if (b_layout != MOE_B_KN && b_layout != MOE_B_NK) return MOE_ERR_UNSUPPORTED;
+  if (b_layout != MOE_B_KN && b_layout != MOE_B_NK && b_layout != MOE_B_KN_GATE_UP)
+    return MOE_ERR_UNSUPPORTED;
   if (epilogue != MOE_EPI_STORE && epilogue != MOE_EPI_SILU_MUL &&
       epilogue != MOE_EPI_WEIGHTED_SCATTER)
     return MOE_ERR_UNSUPPORTED;
-  if (epilogue == MOE_EPI_SILU_MUL && !B2) return MOE_ERR_INVALID;
+  if (b_layout == MOE_B_KN_GATE_UP) {
+    // gate and up interleaved in B: the SiLU*up epilogue only, no B2
+    if (epilogue != MOE_EPI_SILU_MUL || B2) return MOE_ERR_INVALID;
+    if (N % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  } else if (epilogue == MOE_EPI_SILU_MUL && !B2) {
+    return MOE_ERR_INVALID;
+  }
   if (epilogue == MOE_EPI_WEIGHTED_SCATTER) {
     if (!epi_row_pair || !pair_w || k <= 0) return MOE_ERR_INVALID;
     if (b_layout != MOE_B_KN) return MOE_ERR_UNSUPPORTED;
@@ -161,6 +170,18 @@ int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t 
   return launch_status(moe::launch_grouped_gemm(
       dtype, N, K, (const uint16_t *)A, a_src_row, a_src_div, (const uint16_t *)B,
       (const uint16_t *)B2, b_layout, plan, epilogue, epi_row_pair, pair_w, k, D, cus, s));
+}
+
+int moe_pack_gate_up(const void *w_gate, const void *w_up, int E, int K, int N, void *out,
+                     void *stream) {
+  if (!w_gate || !w_up || !out) return MOE_ERR_INVALID;
+  if (E <= 0 || K <= 0 || N <= 0) return MOE_ERR_INVALID;
+  if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(out)) return MOE_ERR_INVALID;
+  if (N % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((long)E * K > (1L << 40) / N) return MOE_ERR_UNSUPPORTED;
+  if (device_cus() == 0) return MOE_ERR_DEVICE;
+  return launch_status(moe::launch_pack_gate_up((const uint16_t *)w_gate, (const uint16_t *)w_up, E,
+                                                K, N, (uint16_t *)out, (hipStream_t)stream));
 }
 
 int moe_combine(const void *y, int H, const int32_t *pair_to_row, const float *topk_w, int T,
@@ -227,13 +248,15 @@ int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
                  const float *topk_w_in, const void *w_gate, const void *w_up,
                  const void *w_down, int T, int H, int E, int k, int I, void *out, int combine,
                  void *workspace, size_t ws_bytes, void *stream) {
-  if (!x || !w_gate || !w_up || !w_down || !out || !workspace) return MOE_ERR_INVALID;
+  // w_up == NULL: w_gate holds gate and up interleaved (moe_pack_gate_up)
+  if (!x || !w_gate || !w_down || !out || !workspace) return MOE_ERR_INVALID;
   if (!logits && (!topk_idx_in || !topk_w_in)) return MOE_ERR_INVALID;
   if (T <= 0 || H <= 0 || E <= 0 || k <= 0 || I <= 0 || k > E) return MOE_ERR_INVALID;
-  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+  if (!aligned16(x) || !aligned16(w_gate) || (w_up && !aligned16(w_up)) || !aligned16(w_down) ||
       !aligned16(out) || !aligned16(workspace))
     return MOE_ERR_INVALID;
   if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!w_up && I % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (E > 1024 || k > 16) return MOE_ERR_UNSUPPORTED;
   if ((long)T * k > 0x7fffffffL / 2) return MOE_ERR_UNSUPPORTED;
   if (combine != MOE_COMBINE_GATHER && combine != MOE_COMBINE_SCATTER) return MOE_ERR_UNSUPPORTED;
@@ -283,7 +306,8 @@ int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
     if (e != hipSuccess) return MOE_ERR_DEVICE;
   }
   e = moe::launch_grouped_gemm(MOE_BF16, I, H, (const uint16_t *)x, r2p, k,
-                               (const uint16_t *)w_gate, (const uint16_t *)w_up, MOE_B_KN, plan,
+                               (const uint16_t *)w_gate, (const uint16_t *)w_up,
+                               w_up ? MOE_B_KN : MOE_B_KN_GATE_UP, plan,
                                MOE_EPI_SILU_MUL, nullptr, nullptr, 0, h, cus, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   if (combine == MOE_COMBINE_SCATTER) {

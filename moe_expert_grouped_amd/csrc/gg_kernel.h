@@ -103,6 +103,8 @@ struct GGArgs {
   int topk;                    // scatter: token of pair p is p / topk
   int N, K;
   int group_rows; // row tasks per super-block of the task order (>= 1)
+  int ldb;        // [K][N] weights: elements per k row (N, or 2N interleaved)
+  int b_il;       // gate/up interleaved in 128-column blocks in B (B2 unused)
 };
 
 // 16-byte-granule XOR swizzles of tiles stored with 64- or 128-byte rows
@@ -487,7 +489,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
     if constexpr (KN) {
       constexpr int GPR = BN / 8; // 16-byte granules per k row
       const int k = v * RPI + lane / GPR;
-      b_off[v] = (uint32_t)(((lane / GPR) * N + (((lane % GPR) ^ swz_kn<BN>(k)) * 8)) * 2);
+      b_off[v] = (uint32_t)(((lane / GPR) * args.ldb + (((lane % GPR) ^ swz_kn<BN>(k)) * 8)) * 2);
     } else {
       const int n = v * RPI + lane / A_GPR;
       b_off[v] =
@@ -513,10 +515,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
     const int gg = g < 0 ? 0 : g;
 #pragma unroll
     for (int m = 0; m < NB; ++m) {
+      // interleaved gate/up: block b of 128 columns holds gate then up
       const unsigned char *Bm =
-          reinterpret_cast<const unsigned char *>(m == 0 ? args.B : args.B2) + (size_t)gg * K * N * 2;
+          reinterpret_cast<const unsigned char *>(m == 0 || args.b_il ? args.B : args.B2) +
+          (size_t)gg * K * (KN ? args.ldb : N) * 2;
+      const int col = args.b_il ? ((n0 >> 7) << 8) + (n0 & 127) + m * 128 : n0;
       // this wavefront's first k row (or n row) of every slice
-      b_base[m] = KN ? Bm + ((size_t)(wave * B_INSTR * RPI) * N + n0) * 2
+      b_base[m] = KN ? Bm + ((size_t)(wave * B_INSTR * RPI) * args.ldb + col) * 2
                      : Bm + (size_t)(n0 + wave * B_INSTR * RPI) * K * 2;
     }
     b_i = i;
@@ -532,7 +537,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
       if (b_k == KT) b_begin(b_i + 1);
       const int ks =
           __builtin_amdgcn_readfirstlane(b_k + b_rot < KT ? b_k + b_rot : b_k + b_rot - KT);
-      b_koff = KN ? (size_t)ks * BK * N * 2 : (size_t)ks * BK * 2;
+      b_koff = KN ? (size_t)ks * BK * args.ldb * 2 : (size_t)ks * BK * 2;
       ++b_k;
     }
     b_stage = lds_addr_of(bring) + (b_issued % NBR) * BS_BYTES + wave * B_INSTR * 1024;
@@ -540,7 +545,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   };
   auto b_emit = [&](int e) {
     const int m = e / B_INSTR, q = e % B_INSTR;
-    const size_t qoff = KN ? (size_t)q * RPI * N * 2 : (size_t)q * RPI * K * 2;
+    const size_t qoff = KN ? (size_t)q * RPI * args.ldb * 2 : (size_t)q * RPI * K * 2;
     dma16s(b_off[q % QV], b_base[m] + b_koff + qoff, b_stage + m * B_BYTES + q * 1024);
   };
   auto b_issue = [&]() {

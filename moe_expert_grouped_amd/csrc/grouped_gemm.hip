@@ -120,7 +120,8 @@ hipError_t launch_gg_plan(const int32_t *block_group, const int32_t *num_rows, i
   return hipGetLastError();
 }
 
-// dtype 0 bf16 / 1 fp16; layout 0 KN / 1 NK; epilogue 0 STORE / 1 SILU_MUL /
+// dtype 0 bf16 / 1 fp16; layout 0 KN / 1 NK / 2 KN with gate and up
+// interleaved in 128-column blocks (SILU_MUL; B2 unused); epilogue 0 STORE / 1 SILU_MUL /
 // 2 WEIGHTED_SCATTER (KN only; D is then the fp32 token-row accumulator).
 // `plan` holds the row-task plan of block_group (launch_gg_plan), built
 // earlier on the same stream.
@@ -132,11 +133,14 @@ hipError_t launch_grouped_gemm(int dtype, int N, int K, const uint16_t *A,
   const TileCfg c = tile_config(epilogue, N, K);
   const int grid = num_cus; // one workgroup per CU (LDS-limited)
   const bool scat = epilogue == kEpiScatter;
-  GGArgs a{A, a_src_row, a_src_div, B, B2, plan,
+  const bool il = layout == 2; // [K][2N], gate/up interleaved in 128-column blocks
+  GGArgs a{A, a_src_row, a_src_div, B, il ? B : B2, plan,
            scat ? nullptr : (uint16_t *)D, scat ? (float *)D : nullptr,
-           epi_row_pair, pair_w, topk, N, K, c.group};
+           epi_row_pair, pair_w, topk, N, K, c.group, il ? 2 * N : N, il ? 1 : 0};
   const bool fp16 = dtype == 1;
-  const bool kn = layout == 0;
+  const bool kn = layout == 0 || il;
+  if (il && (epilogue != kEpiSiluMul || N % 128 != 0 || c.bn > 128 || 128 % c.bn != 0))
+    return hipErrorInvalidValue;
   if (scat) {
     if (!kn) return hipErrorInvalidValue;
     return fp16 ? launch_bn<kEpiScatter, true, true>(a, c, grid, stream)

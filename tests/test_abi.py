@@ -28,9 +28,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in ["moe_route", "moe_permute", "grouped_gemm", "moe_combine", "moe_finalize", "moe_layer",
-              "moe_layer_ex"]:
+              "moe_layer_ex", "moe_pack_gate_up"]:
         assert n in names
     for n in names:
         assert hasattr(lib, n), "missing export " + n
@@ -111,6 +111,10 @@ def test_grouped_gemm_validation(lib):
     assert call(cap=200) == moe.MOE_ERR_INVALID
     assert call(dtype=5) == moe.MOE_ERR_UNSUPPORTED
     assert call(lay=3) == moe.MOE_ERR_UNSUPPORTED
+    # gate/up interleaved in B: SiLU*up only, no B2, N a multiple of 128
+    assert call(lay=2, epi=1, B2=FAKE) == moe.MOE_ERR_INVALID
+    assert call(lay=2, epi=0) == moe.MOE_ERR_INVALID
+    assert call(lay=2, epi=1, N=192) == moe.MOE_ERR_UNSUPPORTED
     assert call(epi=1) == moe.MOE_ERR_INVALID          # SiLU*up needs B2
     assert call(epi=7) == moe.MOE_ERR_UNSUPPORTED
     assert call(src=FAKE, div=0) == moe.MOE_ERR_INVALID
@@ -125,6 +129,14 @@ def test_grouped_gemm_validation(lib):
     assert call(ws=NULL) == moe.MOE_ERR_WORKSPACE
     assert lib.grouped_gemm_workspace_size(256) > 0
     assert lib.grouped_gemm_workspace_size(0) == 0
+
+
+def test_pack_gate_up_validation(lib):
+    assert lib.moe_pack_gate_up(NULL, FAKE, 2, 64, 128, FAKE, NULL) == moe.MOE_ERR_INVALID
+    assert lib.moe_pack_gate_up(FAKE, FAKE, 2, 64, 128, NULL, NULL) == moe.MOE_ERR_INVALID
+    assert lib.moe_pack_gate_up(FAKE, FAKE, 0, 64, 128, FAKE, NULL) == moe.MOE_ERR_INVALID
+    assert lib.moe_pack_gate_up(FAKE, MISALIGNED, 2, 64, 128, FAKE, NULL) == moe.MOE_ERR_INVALID
+    assert lib.moe_pack_gate_up(FAKE, FAKE, 2, 64, 64, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_finalize_validation(lib):
@@ -156,6 +168,11 @@ def test_combine_and_layer_validation(lib):
     assert call_ex(-1) == moe.MOE_ERR_UNSUPPORTED
     assert call_ex(1, x=NULL) == moe.MOE_ERR_INVALID
     assert call_ex(1, wsb=ws - 1) == moe.MOE_ERR_WORKSPACE
+    # w_up == NULL: packed gate/up weights, which need I % 128 == 0 (I = 64 here)
+    assert lib.moe_layer(FAKE, FAKE, NULL, NULL, FAKE, NULL, FAKE, T, H, E, k, I, FAKE, FAKE, ws,
+                         NULL) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_layer(FAKE, FAKE, NULL, NULL, NULL, NULL, FAKE, T, H, E, k, I, FAKE, FAKE, ws,
+                         NULL) == moe.MOE_ERR_INVALID
 
 
 def test_valid_call_without_device_reports_device_error(lib):

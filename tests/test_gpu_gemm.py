@@ -311,3 +311,48 @@ def test_finalize_rounds_to_nearest_even(n):
     out = moe.finalize(acc.cuda())
     torch.cuda.synchronize()
     assert torch.equal(out.cpu().view(torch.int16), acc.to(torch.bfloat16).view(torch.int16))
+
+
+def _interleave(gate, up):
+    """[G][K][N] gate and up -> [G][K][2N]: per 128-column block, gate then up
+    (a reshape of the test's own arrays, no arithmetic)."""
+    G, K, N = gate.shape
+    return np.concatenate([gate.reshape(G, K, N // 128, 128), up.reshape(G, K, N // 128, 128)],
+                          axis=3).reshape(G, K, 2 * N)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_pack_gate_up_bit_exact(dtype):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    g = np.random.default_rng(31)
+    for E, K, N in [(1, 1, 128), (3, 64, 256), (5, 320, 1536)]:
+        gate = g.integers(0, 65535, size=(E, K, N)).astype(np.uint16)
+        up = g.integers(0, 65535, size=(E, K, N)).astype(np.uint16)
+        say("pack gate/up", dtype, E, K, N)
+        out = moe.pack_gate_up(dev16(gate, tdt), dev16(up, tdt))
+        torch.cuda.synchronize()
+        assert np.array_equal(host16(out), _interleave(gate, up))
+
+
+@pytest.mark.parametrize("tile", [None, "128,32,4,4,2", "64,32,3,10"])
+def test_gate_up_interleaved_layout(tile, monkeypatch):
+    # the interleaved weights give the same bits as the two separate matrices,
+    # and the integer-exact result of the oracle, in every SiLU*up tile shape
+    if tile:
+        monkeypatch.setenv("MOE_GG_TILE_GU", tile)
+    G, cap = 4, 11 * 128
+    m_rows = 9 * 128
+    bg = _groups(cap // 128, G, 23)
+    for N, K in [(512, 320), (128, 64), (384, 128)]:
+        A = syn.ternary_bits((cap, K), 11)
+        B = syn.ternary_bits((G, K, N), 12)
+        B2 = syn.ternary_bits((G, K, N), 13)
+        say("gemm gate/up interleaved", tile, N, K)
+        D0 = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16", B2_bits=B2, epi="silu_mul")
+        D1 = _run(A, _interleave(B, B2), bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16",
+                  layout="kn_gate_up", epi="silu_mul")
+        assert torch.equal(D0[:m_rows].view(torch.int16), D1[:m_rows].view(torch.int16))
+        ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, B2_bits=B2, epilogue="silu_mul",
+                                  rows=np.arange(m_rows, dtype=np.int32))
+        assert_close(to_f64(D1)[:m_rows], ref, "interleaved", max_frac=8e-3, rel_fro=4e-3)
+        assert np.all(np.isnan(to_f64(D1)[m_rows:]))

@@ -148,3 +148,24 @@ def test_layer_scatter_small_shapes_and_gather_agree():
 def test_layer_scatter_full_size(name, n):
     d = syn.make_config(name)
     _check_layer(d, tokens=_sample(d["T"], min(n, d["T"] - 2)), what=name, combine="scatter")
+
+
+@pytest.mark.parametrize("name", ["tiny", "tp_share", "ep_skew"])
+def test_layer_packed_gate_up_same_bits(name):
+    # the layer on pack_gate_up weights (w_up=None) gives the same bits as on
+    # the separate gate and up weights, with both combines
+    d = syn.make_config(name)
+    T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
+    D = _inputs_dev(d)
+    say("layer packed gate/up", name)
+    wgu = moe.pack_gate_up(D["wg"], D["wu"])
+    kw = dict(logits=torch.from_numpy(d["logits"]).cuda()) if "logits" in d else dict(
+        topk_idx=torch.from_numpy(d["topk_idx"]).cuda(), topk_w=torch.from_numpy(d["topk_w"]).cuda())
+    for combine in ("gather", "scatter"):
+        a = moe.layer(D["x"], D["wg"], D["wu"], D["wd"], k, combine=combine, **kw)
+        b = moe.layer(D["x"], wgu, None, D["wd"], k, combine=combine, **kw)
+        torch.cuda.synchronize()
+        if combine == "gather":
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+        else:  # the scatter's fp32 atomics sum a token's slots in no fixed order
+            assert_close(to_f64(b), to_f64(a), name + " scatter", max_frac=1e-2, rel_fro=2e-3)
