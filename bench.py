@@ -114,6 +114,21 @@ def main():
         step_scatter()
     stats_scatter = step_stats(step_scatter, a.steps, cold=False)
 
+    # the same step captured once in a HIP graph and replayed (no host launch
+    # cost per kernel; the layer launches kernels only, so it captures whole)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(a.warmup):
+        graph.replay()
+    stats_graph = step_stats(graph.replay, a.steps, cold=False)
+
     def step_unpacked():
         moe.layer(x, wg, wu, wd, k, logits=logits, topk_idx=tidx, topk_w=tw, workspace=ws, out=out)
 
@@ -205,6 +220,7 @@ def main():
         "gemm_mfma_peak_frac": round(gemm_flops / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernel_us": {n: round(v * 1e3, 2) for n, v in dur.items()},
         "layer_us_per_step": stats,
+        "hip_graph": {"layer_us_per_step": stats_graph},
         "unpacked_gate_up_weights": {"layer_us_per_step": stats_unpacked},
         "scatter_combine": {"layer_us_per_step": stats_scatter,
                             "kernel_us": {n: round(v * 1e3, 2) for n, v in dur_sc.items()}},

@@ -169,3 +169,39 @@ def test_layer_packed_gate_up_same_bits(name):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
         else:  # the scatter's fp32 atomics sum a token's slots in no fixed order
             assert_close(to_f64(b), to_f64(a), name + " scatter", max_frac=1e-2, rel_fro=2e-3)
+
+
+@pytest.mark.parametrize("combine", ["gather", "scatter"])
+def test_layer_hip_graph_replays(combine):
+    # the whole layer captured in one HIP graph (it launches kernels only: no
+    # memset node, no host synchronization, no allocation inside) replays to
+    # the eager result on every replay, with eager work and synchronizations
+    # between the replays
+    d = syn.make_config("tiny")
+    T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
+    D = _inputs_dev(d)
+    wgu = moe.pack_gate_up(D["wg"], D["wu"])
+    logits = torch.from_numpy(d["logits"]).cuda()
+    ws = moe.layer_workspace(T, H, E, k, I)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    say("layer graph", combine)
+    eager = moe.layer(D["x"], wgu, None, D["wd"], k, logits=logits, workspace=ws, combine=combine).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the path on the capture stream
+        moe.layer(D["x"], wgu, None, D["wd"], k, logits=logits, workspace=ws, out=out, combine=combine)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.layer(D["x"], wgu, None, D["wd"], k, logits=logits, workspace=ws, out=out, combine=combine)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        ws[:4096].zero_()  # eager work on the buffers the graph reads and writes
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if combine == "gather":
+            assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), rep
+        else:
+            assert_close(to_f64(out), to_f64(eager), "graph scatter %d" % rep, max_frac=1e-2, rel_fro=2e-3)
