@@ -138,12 +138,12 @@ def main():
 
     # ---- per-kernel durations: HIP events on the launch stream, same path step by step
     stream = torch.cuda.current_stream()
-    names = ["route", "permute", "gate_up", "down", "combine"]
+    names = ["route", "permute", "gate_up", "down", "combine", "permute_gather"]
     timed = []
     R = T * k
     idx_t, w_t = (tidx, tw) if given else (None, None)
     for it in range(a.warmup + a.steps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
         e[0].record(stream)
         if not given:
             idx_t, w_t = moe.route(logits, k)
@@ -158,6 +158,9 @@ def main():
         e[4].record(stream)
         moe.combine(y, P.pair_to_row, w_t, out=out)
         e[5].record(stream)
+        # the permutation with the optional row gather (x_perm), HBM-bound
+        moe.permute(idx_t, E, x=x)
+        e[6].record(stream)
         if it >= a.warmup:
             timed.append(e)
     torch.cuda.synchronize()
@@ -190,6 +193,8 @@ def main():
     # ---- algorithmic work
     gemm_flops = 6.0 * R * H * I
     gu_bytes = 4.0 * e_act * H * I + 2.0 * T * H + 2.0 * R * I      # weights, x, h
+    comb_bytes = 2.0 * R * H + 2.0 * T * H                          # y rows read, out written
+    gath_bytes = 2.0 * T * H + 2.0 * m_pad * H                      # x read once, x_perm written
     dn_bytes = 2.0 * e_act * I * H + 2.0 * R * I + 2.0 * R * H      # weights, h, y
     layer_s = ms * 1e-3
     gemm_s = (dur["gate_up"] + dur["down"]) * 1e-3
@@ -219,6 +224,11 @@ def main():
         "gemm_tflops": round(gemm_flops / gemm_s / 1e12, 2),
         "gemm_mfma_peak_frac": round(gemm_flops / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernel_us": {n: round(v * 1e3, 2) for n, v in dur.items()},
+        "hbm_gbs": {
+            n: {"us": round(dur[n] * 1e3, 2), "algorithmic_bytes": b,
+                "gbs": round(b / (dur[n] * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(b / (dur[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            for n, b in (("combine", comb_bytes), ("permute_gather", gath_bytes))},
         "layer_us_per_step": stats,
         "hip_graph": {"layer_us_per_step": stats_graph},
         "unpacked_gate_up_weights": {"layer_us_per_step": stats_unpacked},
