@@ -122,7 +122,9 @@ int moe_route(const float *logits, int T, int E, int k, int32_t *topk_idx,
  *   block_expert   [cap/128] expert of each 128-row block; -1 beyond M_pad
  *   num_padded_rows [1]   M_pad (device int32, read by grouped_gemm)
  *   x_perm         [cap][H] bf16, optional (x and x_perm both non-NULL):
- *                  x_perm[row] = x[row_to_pair[row] / k]; zeros for padding.
+ *                  x_perm[row] = x[row_to_pair[row] / k] for row < M_pad, zeros
+ *                  for the padding rows below M_pad; rows at or past M_pad are
+ *                  not written.
  * cap must be a multiple of 128 and >= moe_padded_capacity(T, k, E).
  * Expert ids outside [0, E) are undefined behaviour.
  * Workspace: moe_permute_workspace_size(T, k, E) bytes, 256-byte aligned.

@@ -142,9 +142,11 @@ class Permutation:
 
 
 def permute(topk_idx: torch.Tensor, E: int, x: torch.Tensor | None = None, cap: int | None = None,
-            workspace: torch.Tensor | None = None) -> Permutation:
+            workspace: torch.Tensor | None = None,
+            x_perm: torch.Tensor | None = None) -> Permutation:
     """Stable expert-major permutation of the (token, slot) pairs into
-    128-row-aligned blocks; optionally gathers x into x_perm."""
+    128-row-aligned blocks; optionally gathers x into x_perm [cap][H] (rows
+    below M_pad; rows at or past it are not written)."""
     _need(topk_idx, "topk_idx", torch.int32, 2)
     lib = load_library()
     T, k = topk_idx.shape
@@ -159,11 +161,17 @@ def permute(topk_idx: torch.Tensor, E: int, x: torch.Tensor | None = None, cap: 
     be = torch.empty(max(cap, 0) // ROW_BLOCK, **i32)
     mpad = torch.empty(1, **i32)
     H = 0
-    x_perm = None
     if x is not None:
         _need(x, "x", torch.bfloat16, 2)
         H = x.shape[1]
-        x_perm = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+        if x_perm is None:
+            x_perm = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+        else:
+            _need(x_perm, "x_perm", torch.bfloat16, 2)
+            if tuple(x_perm.shape) != (cap, H):
+                raise ValueError("x_perm must be [cap, H]")
+    else:
+        x_perm = None
     need = lib.moe_permute_workspace_size(T, k, E)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)

@@ -19,8 +19,8 @@
 //                            equal experts inside a wavefront; per-wave counts
 //                            in LDS order the wavefronts), then the row maps;
 //                            the same grid marks padding rows with -1
-//   pass 4  permute_gather   optional: x_perm[row] = x[token of row], zero
-//                            rows for padding (16-byte vector copies)
+//   pass 4  permute_gather   optional: x_perm[row] = x[token of row] below
+//                            M_pad, zero rows for padding (16-byte vectors)
 // Routings of at most 16384 pairs take passes 1-3 in a single launch
 // instead (permute_plan.hip).
 #include "common.h"
@@ -194,23 +194,36 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter(
   }
 }
 
+// One wavefront per row below M_pad (read on the device): each lane loads up
+// to 8 16-byte vectors of the source row before storing any, so 8 KiB per
+// wavefront are in flight (H = 4096); padding rows are zero-filled.  Rows at
+// or past M_pad are not written.
 __global__ __launch_bounds__(256) void permute_gather(const uint16_t *__restrict__ x, int H,
                                                       const int32_t *__restrict__ row_to_pair,
+                                                      const int32_t *__restrict__ num_padded_rows,
                                                       int k, int cap,
                                                       uint16_t *__restrict__ x_perm) {
-  // one wavefront per row; H % 8 == 0, 16-byte vectors
+  // H % 8 == 0, 16-byte vectors
   const int lane = threadIdx.x & 63;
   const int waves = (gridDim.x * blockDim.x) >> 6;
   const int nvec = H / 8;
-  for (int r = (blockIdx.x * blockDim.x + threadIdx.x) >> 6; r < cap; r += waves) {
+  const int rows = min(num_padded_rows[0], cap);
+  for (int r = (blockIdx.x * blockDim.x + threadIdx.x) >> 6; r < rows; r += waves) {
     const int p = row_to_pair[r];
     u32x4 *dst = reinterpret_cast<u32x4 *>(x_perm + (size_t)r * H);
-    if (p < 0) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      for (int v = lane; v < nvec; v += 64) dst[v] = z;
-    } else {
-      const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (size_t)(p / k) * H);
-      for (int v = lane; v < nvec; v += 64) dst[v] = src[v];
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (size_t)(p < 0 ? 0 : p / k) * H);
+    for (int v0 = 0; v0 < nvec; v0 += 64 * 8) {
+      u32x4 buf[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int v = v0 + u * 64 + lane;
+        buf[u] = (p >= 0 && v < nvec) ? src[v] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int v = v0 + u * 64 + lane;
+        if (v < nvec) dst[v] = buf[u];
+      }
     }
   }
 }
@@ -252,7 +265,7 @@ hipError_t launch_permute(const int32_t *idx, int T, int k, int E, const uint16_
   if (x && x_perm) {
     const int rows_per_block = 4;
     const int grid = min(cap / rows_per_block, 8192);
-    permute_gather<<<grid, 256, 0, stream>>>(x, H, row_to_pair, k, cap, x_perm);
+    permute_gather<<<grid, 256, 0, stream>>>(x, H, row_to_pair, num_padded_rows, k, cap, x_perm);
   }
   return hipGetLastError();
 }

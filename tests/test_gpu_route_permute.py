@@ -53,14 +53,19 @@ def _permute_case(idx_np, E, with_x=False, H=64, what=""):
     if with_x:
         x_bits = np.random.default_rng(T).integers(0, 65535, size=(T, H)).astype(np.uint16)
         x_bits[x_bits & 0x7f80 == 0x7f80] = 0  # keep values finite (bits are copied anyway)
-    P = moe.permute(torch.from_numpy(idx_np).cuda(), E, x=dev16(x_bits) if with_x else None)
+    cap = moe.padded_capacity(T, k, E)
+    xp = torch.full((cap, H), float("nan"), dtype=torch.bfloat16, device="cuda") if with_x else None
+    P = moe.permute(torch.from_numpy(idx_np).cuda(), E, x=dev16(x_bits) if with_x else None, x_perm=xp)
     torch.cuda.synchronize()
     for name in ("counts", "offsets", "pair_to_row", "row_to_pair", "block_expert"):
         got = getattr(P, name).cpu().numpy()
         assert np.array_equal(got, ref[name]), "%s %s" % (what, name)
-    assert int(P.num_padded_rows.item()) == ref["m_pad"]
+    m = ref["m_pad"]
+    assert int(P.num_padded_rows.item()) == m
     if with_x:
-        assert np.array_equal(host16(P.x_perm), oracle.gather(x_bits, ref["row_to_pair"], k))
+        got = host16(P.x_perm)
+        assert np.array_equal(got[:m], oracle.gather(x_bits, ref["row_to_pair"], k)[:m])
+        assert np.all(got[m:] == host16(torch.full((1,), float("nan"), dtype=torch.bfloat16))[0])
 
 
 def test_permute_cases():
