@@ -5,8 +5,9 @@
 A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: route -> permute -> gate/up grouped GEMM with the
 SiLU*up epilogue -> down grouped GEMM -> top-k weighted combine (moe_layer).
-W untimed steps, then exactly K timed steps bracketed by device
-synchronizations.  Per-kernel durations come from HIP events recorded on the
+About 200 ms of untimed back-to-back steps (the clocks of the part move for
+several milliseconds after work starts), then W untimed warmup steps, then
+exactly K timed steps bracketed by device synchronizations.  Per-kernel durations come from HIP events recorded on the
 launch stream around each step of the same path called entry point by entry
 point.  Also reported: per-step percentiles with the Infinity Cache warm and
 flushed (a 512 MiB write before each step, outside the events), the
@@ -33,8 +34,11 @@ PEAK_HBM_GBS = 8000.0       # HBM3E
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--settle-ms", type=float, default=200.0,
+                   help="untimed back-to-back steps for this long before the W warmup steps, "
+                        "so the part's clocks have settled when the timed region starts")
     p.add_argument("--config", default="tp_share")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample (0 disables it)")
@@ -95,6 +99,7 @@ def main():
         moe.layer(x, wgu, wu_arg, wd, k, logits=logits, topk_idx=tidx, topk_w=tw, workspace=ws,
                   out=out)
 
+    settle_steps = settle(step, a.settle_ms)
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -209,7 +214,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": a.steps,
-        "warmup": a.warmup,
+        "warmup": a.warmup, "settle_steps": settle_steps,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -267,6 +272,7 @@ def bench_dense(a):
     def step():
         moe.grouped_gemm(A, B, bg, nr, N=N, K=K, cap=M, b_layout="nk", out=D, workspace=ws)
 
+    settle_steps = settle(step, a.settle_ms)
     for _ in range(a.warmup):
         step()
     stream = torch.cuda.current_stream()
@@ -284,7 +290,7 @@ def bench_dense(a):
     tf = flops / (kern_ms * 1e-3) / 1e12
     print(json.dumps({
         "metric": "dense fp16 GEMM D = A.B^T (one-group grouped_gemm)", "value": round(tf, 2),
-        "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "settle_steps": settle_steps,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp16", "data": "synthetic",
         "config": {"workload": "dense fp16 GEMM M=N=K=4096, D = A.B^T, fp32 accumulate"},
@@ -314,6 +320,23 @@ def _pcts(ms):
     us = np.asarray(ms) * 1e3
     return {"median": round(float(np.median(us)), 2), "p10": round(float(np.percentile(us, 10)), 2),
             "p90": round(float(np.percentile(us, 90)), 2), "n": int(len(us))}
+
+
+def settle(step, ms):
+    """Run `step` back to back, untimed, for about `ms` milliseconds of wall
+    time (at most 20000 steps); returns the number of steps run."""
+    import torch
+    if ms <= 0:
+        return 0
+    n, t0 = 0, time.perf_counter()
+    while n < 20000:
+        for _ in range(16):
+            step()
+        n += 16
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            break
+    return n
 
 
 def step_stats(step, n, cold=True):
