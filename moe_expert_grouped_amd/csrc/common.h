@@ -52,6 +52,19 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Inclusive max-scan across the 64 lanes of a wavefront, the same lane moves
+// (lanes shifted in from outside a row, or masked off, contribute -1: every
+// value scanned is >= -1).
+__device__ __forceinline__ int wave_incl_max_scan(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x111, 0xf, 0xf, false)); // row_shr:1
+  v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x112, 0xf, 0xf, false)); // row_shr:2
+  v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x114, 0xf, 0xf, false)); // row_shr:4
+  v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x118, 0xf, 0xf, false)); // row_shr:8
+  v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x142, 0xa, 0xf, false)); // row_bcast:15
+  v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x143, 0xc, 0xf, false)); // row_bcast:31
+  return v;
+}
+
 // Row-task plan of the grouped GEMM, built on the device from the block
 // groups and the padded row count: plan[0] = number of row tasks, plan[1] =
 // number of blocks, then per row task i (one or two consecutive 128-row

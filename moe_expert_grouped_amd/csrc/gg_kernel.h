@@ -411,16 +411,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
       dma4(args.pair_w + (p < 0 ? 0 : p), lds_addr_of(&wtab[s][64 * wave]));
     }
   };
-  // The column tasks of one row task run side by side on neighbouring CUs;
-  // each starts at its own k-slice, spread evenly by column block, and wraps
-  // around (the sum over k is the same; its fp32 rounding order is fixed per
-  // task).
-  auto k_rotation = [&](int n0) {
-    return __builtin_amdgcn_readfirstlane((int)(((long)(n0 / BN) * KT) / ncol));
-  };
+  // The column tasks of one row task run side by side on neighbouring CUs
+  // of one XCD and walk k in the same order, so each A slice is fetched into
+  // that XCD's L2 once and served to all of them while it is still there.
 
   // ---------------- A stream ----------------
-  int a_i = 0, a_k = KT, a_rot = 0; // item being issued, slices of it issued, its rotation
+  int a_i = 0, a_k = KT; // item being issued, slices of it issued
   const unsigned char *a_src[A_INSTR];
   // Point the A sources at item i (its plan entry and tables have landed).
   // A one-block task loads its 128 rows twice (rows 128-255 repeat them,
@@ -430,10 +426,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
     // the consumer's waits have covered unless the A lead is long against
     // the task length; then wait for everything
     if (i > 0 && KT + LB <= 2 * LA) wait_vmcnt<0>();
-    int rt, n0, b, nb, g;
-    coords(i, rt, n0);
+    int b, nb, g;
     plan_of(i, b, nb, g);
-    a_rot = k_rotation(n0);
     const MOE_LDS int32_t *ptbl = (const MOE_LDS int32_t *)tab[i % kTabSlots];
 #pragma unroll
     for (int q = 0; q < A_INSTR; ++q) {
@@ -463,9 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   auto a_prep = [&]() {
     if (a_issued < total) {
       if (a_k == KT) a_begin(a_i + 1);
-      const int ks =
-          __builtin_amdgcn_readfirstlane(a_k + a_rot < KT ? a_k + a_rot : a_k + a_rot - KT);
-      a_koff = (uint32_t)(ks * BK * 2);
+      a_koff = (uint32_t)(a_k * BK * 2);
       ++a_k;
     }
     a_stage = lds_addr_of(aring) + (a_issued % NA) * A_BYTES + wave * A_INSTR * 1024;
@@ -496,7 +488,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
           (uint32_t)(((lane / A_GPR) * K + (((lane % A_GPR) ^ swz_rows<BK>(n)) * 8)) * 2);
     }
   }
-  int b_i = 0, b_k = KT, b_rot = 0;
+  int b_i = 0, b_k = KT;
   const unsigned char *b_base[NB];
   // Start the B stream on item i: fetch the plan entry of item i+2 and the
   // tables of item i+1, then point the B bases at item i (its plan entry
@@ -511,7 +503,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
     int rt, n0, b, nb, g;
     coords(i, rt, n0);
     plan_of(i, b, nb, g);
-    b_rot = k_rotation(n0);
     const int gg = g < 0 ? 0 : g;
 #pragma unroll
     for (int m = 0; m < NB; ++m) {
@@ -535,9 +526,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   auto b_prep = [&]() {
     if (b_issued < total) {
       if (b_k == KT) b_begin(b_i + 1);
-      const int ks =
-          __builtin_amdgcn_readfirstlane(b_k + b_rot < KT ? b_k + b_rot : b_k + b_rot - KT);
-      b_koff = KN ? (size_t)ks * BK * args.ldb * 2 : (size_t)ks * BK * 2;
+      b_koff = KN ? (size_t)b_k * BK * args.ldb * 2 : (size_t)b_k * BK * 2;
       ++b_k;
     }
     b_stage = lds_addr_of(bring) + (b_issued % NBR) * BS_BYTES + wave * B_INSTR * 1024;

@@ -63,47 +63,40 @@ static TileCfg tile_config(int epilogue, int N, int K) {
 __global__ __launch_bounds__(1024) void gg_plan_kernel(const int32_t *__restrict__ block_group,
                                                        const int32_t *__restrict__ num_rows,
                                                        int cap, int32_t *__restrict__ plan) {
-  __shared__ int s_a[1024];
-  __shared__ int s_b[1024];
-  const int t = threadIdx.x;
+  __shared__ int s_start[16]; // per wavefront: the last run start it saw
+  __shared__ int s_heads[16]; // per wavefront: its pair heads
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int nblk = max(0, min(num_rows[0], cap)) / kBM;
-  int carry_start = -1, carry_count = 0;
+  int carry_start = -1, carry_count = 0; // over the chunks before
   for (int base = 0; base < nblk; base += 1024) {
     const int b = base + t;
     const int g = b < nblk ? block_group[b] : -1;
     const int gp = (b > 0 && b < nblk) ? block_group[b - 1] : -1;
     const int gn = (b + 1 < nblk) ? block_group[b + 1] : -1;
     const bool start = g >= 0 && (b == 0 || gp != g);
-    // inclusive max-scan of run starts
-    s_a[t] = start ? b : -1;
+    // the start of block b's run: inclusive max-scan of run starts
+    int rs = wave_incl_max_scan(start ? b : -1);
+    if (lane == 63) s_start[w] = rs;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int v = t >= off ? s_a[t - off] : -1;
-      __syncthreads();
-      s_a[t] = max(s_a[t], v);
-      __syncthreads();
-    }
-    const int rs = max(s_a[t], carry_start);
+    int before = carry_start;
+    for (int j = 0; j < w; ++j) before = max(before, s_start[j]);
+    rs = max(rs, before);
+    // a pair head is a block at an even distance from its run's start
     const bool head = g >= 0 && ((b - rs) & 1) == 0;
-    // inclusive sum-scan of heads
-    s_b[t] = head ? 1 : 0;
+    const int hs = wave_incl_scan(head ? 1 : 0);
+    if (lane == 63) s_heads[w] = hs;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int v = t >= off ? s_b[t - off] : 0;
-      __syncthreads();
-      s_b[t] += v;
-      __syncthreads();
-    }
+    int idx = carry_count + hs - 1;
+    for (int j = 0; j < w; ++j) idx += s_heads[j];
     if (head) {
-      const int idx = carry_count + s_b[t] - 1;
       plan[kPlanHead + 2 * idx] = b | (gn == g ? kPlanTwo : 0);
       plan[kPlanHead + 2 * idx + 1] = g;
     }
-    const int last_rs = max(s_a[1023], carry_start);
-    const int total = s_b[1023];
-    __syncthreads();
-    carry_start = last_rs;
-    carry_count += total;
+    for (int j = 0; j < 16; ++j) {
+      carry_start = max(carry_start, s_start[j]);
+      carry_count += s_heads[j];
+    }
+    __syncthreads(); // the next chunk rewrites s_start / s_heads
   }
   if (t == 0) {
     plan[0] = carry_count;

@@ -205,6 +205,55 @@ def test_block_pairing_integer_exact(pattern, epi):
     assert np.all(np.isnan(got[m_rows:]))          # rows past num_rows: not written
 
 
+def _plan_by_definition(bg, num_rows, cap):
+    """The row-task plan from its definition: inside each maximal run of blocks
+    with one non-negative group, blocks pair up from the run's first block (an
+    odd run ends in a one-block task); entries in block order."""
+    nblk = max(0, min(num_rows, cap)) // 128
+    out, b = [], 0
+    while b < nblk:
+        g = int(bg[b])
+        if g < 0:
+            b += 1
+            continue
+        e = b
+        while e < nblk and bg[e] == g:
+            e += 1
+        for s in range(b, e, 2):
+            out += [s | ((1 << 30) if s + 1 < e else 0), g]
+        b = e
+    return np.array([len(out) // 2, nblk] + out, np.int32)
+
+
+# block counts around the plan kernel's 1024-block chunks, runs of every
+# length crossing them, negative groups, row counts past cap and not whole blocks
+@pytest.mark.parametrize("nblk,num_rows_extra", [(1, 0), (5, 77), (1023, 0), (1024, 0), (1025, 5),
+                                                 (2050, 0), (3000, 1 << 20)])
+def test_row_task_plan_matches_definition(nblk, num_rows_extra):
+    g = np.random.default_rng(nblk)
+    runs, total = [], 0
+    while total < nblk:
+        n = int(g.integers(1, 8)) if g.random() < 0.9 else int(g.integers(8, 1500))
+        grp = -1 if g.random() < 0.15 else int(g.integers(0, 5))
+        runs.append(np.full(n, grp, np.int32))
+        total += n
+    bg = np.concatenate(runs)[:nblk]
+    cap = nblk * 128
+    num_rows = cap - 64 if num_rows_extra == 77 else cap + num_rows_extra
+    K = N = 64
+    A = torch.zeros((cap, K), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((5, K, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(moe.gemm_workspace(cap).numel(), dtype=torch.uint8, device="cuda")
+    say("row-task plan", "blocks", nblk, "num_rows", num_rows)
+    moe.grouped_gemm(A, B, torch.from_numpy(bg).cuda(),
+                     torch.tensor([num_rows], dtype=torch.int32, device="cuda"),
+                     N=N, K=K, cap=cap, workspace=ws)
+    torch.cuda.synchronize()
+    ref = _plan_by_definition(bg, num_rows, cap)
+    got = ws[:4 * len(ref)].view(torch.int32).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
 def test_padding_rows_not_written():
     # rows whose source (or epilogue pair) is negative are padding: left untouched
     K, N, G, T = 128, 256, 3, 200
