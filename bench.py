@@ -93,6 +93,9 @@ def main():
     # timing (a weight-load transform: the gate/up GEMM then streams each k row
     # of a weight tile as one 512-byte piece); the plain layout is timed too
     packed = I % 128 == 0
+    # moe_layer's rule: weights loaded non-temporally when the experts
+    # average at most two 128-row blocks (each weight tile read about once)
+    stream_w = T * k <= 2 * 128 * E
     wgu = moe.pack_gate_up(wg, wu) if packed else wg
     wu_arg = None if packed else wu
     torch.cuda.synchronize()
@@ -159,9 +162,10 @@ def main():
         e[2].record(stream)
         h = moe.grouped_gemm(x, wgu, P.block_expert, P.num_padded_rows, N=I, K=H, cap=P.cap,
                              a_src_row=P.row_to_pair, a_src_div=k, B2=wu_arg, epilogue="silu_mul",
-                             b_layout="kn_gate_up" if packed else "kn")
+                             b_layout="kn_gate_up" if packed else "kn", b_stream=stream_w)
         e[3].record(stream)
-        y = moe.grouped_gemm(h, wd, P.block_expert, P.num_padded_rows, N=H, K=I, cap=P.cap)
+        y = moe.grouped_gemm(h, wd, P.block_expert, P.num_padded_rows, N=H, K=I, cap=P.cap,
+                             row_pair=P.row_to_pair, b_stream=stream_w)
         e[4].record(stream)
         moe.combine(y, P.pair_to_row, w_t, out=out)
         e[5].record(stream)
@@ -184,7 +188,8 @@ def main():
         acc.zero_()
         e[1].record(stream)
         moe.grouped_gemm(h, wd, P.block_expert, P.num_padded_rows, N=H, K=I, cap=P.cap,
-                         epilogue="weighted_scatter", row_pair=P.row_to_pair, pair_w=w_t, out=acc)
+                         epilogue="weighted_scatter", row_pair=P.row_to_pair, pair_w=w_t, out=acc,
+                         b_stream=stream_w)
         e[2].record(stream)
         moe.finalize(acc, out=out)
         e[3].record(stream)
@@ -252,7 +257,8 @@ def main():
         "config": {"workload": "%s MoE layer share" % a.config, "T": T, "H": H, "E": E, "top_k": k,
                    "I": I, "routing": cfg.get("routing"), "m_pad": m_pad, "active_experts": e_act,
                    "gate_up_weights": ("interleaved in 128-column blocks (moe_pack_gate_up, once "
-                                       "before timing)") if packed else "separate [E][H][I]"},
+                                       "before timing)") if packed else "separate [E][H][I]",
+                   "weight_loads": "non-temporal" if stream_w else "default"},
         "layer_us": round(ms * 1e3, 2),
         "gemm_tflops": round(gemm_flops / gemm_s / 1e12, 2),
         "gemm_mfma_peak_frac": round(gemm_flops / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),

@@ -71,6 +71,13 @@ extern "C" {
  * (moe_pack_gate_up builds it).  Each k row of a task's weight tile is then
  * one contiguous 512-byte piece instead of two 256-byte ones. */
 #define MOE_B_KN_GATE_UP 2
+/* Flag OR-ed into a [K][N] layout (MOE_B_KN, MOE_B_KN_GATE_UP): B is loaded
+ * with the non-temporal (streaming) cache policy.  For weights each of whose
+ * tiles is read by about one row task (the groups average at most two
+ * 128-row blocks): the weights then do not push the A rows and the outputs
+ * out of the caches.  A hint only: results are bit-identical without it.
+ * Not with MOE_B_NK (MOE_ERR_UNSUPPORTED). */
+#define MOE_B_STREAM 0x100
 
 /* Epilogues of grouped_gemm. */
 #define MOE_EPI_STORE 0    /* D[r][n] = round(acc)                              */
@@ -154,7 +161,8 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, const void *x,
  *              MOE_EPI_SILU_MUL (the up weights; B holds the gate weights).
  *              MOE_B_KN_GATE_UP: B is [G][K][2N], gate and up interleaved
  *              (see the define), B2 must be NULL, the epilogue must be
- *              MOE_EPI_SILU_MUL and N % 128 == 0.
+ *              MOE_EPI_SILU_MUL and N % 128 == 0.  Either [K][N] layout may
+ *              carry MOE_B_STREAM (non-temporal weight loads).
  *   D          [cap][N] for MOE_EPI_STORE and MOE_EPI_SILU_MUL.
  *   epi_row_pair  optional for MOE_EPI_STORE / MOE_EPI_SILU_MUL: rows r with
  *              epi_row_pair[r] < 0 are padding and are not written (the MoE
@@ -169,9 +177,8 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, const void *x,
  *              order, so results are reproducible only up to fp32 rounding
  *              order.  MOE_B_KN only.  For the MoE down GEMM:
  *              epi_row_pair = row_to_pair, pair_w = topk_w.
- * Accumulation is fp32 (MFMA), over k in a fixed per-task order (each
- * column block starts at its own k offset and wraps around); the store
- * epilogues round to nearest even, so STORE and SILU_MUL results are
+ * Accumulation is fp32 (MFMA), over k in ascending 32-deep slices; the
+ * store epilogues round to nearest even, so STORE and SILU_MUL results are
  * deterministic.
  * Consecutive blocks of one group are computed as 256-row tasks; the pairing
  * is planned on the device, in the workspace, before the GEMM runs.
@@ -230,6 +237,9 @@ int moe_finalize(const float *acc, size_t n, void *out, void *stream);
  *   w_up == NULL: w_gate is the packed [E][H][2I] tensor of
  *   moe_pack_gate_up (MOE_B_KN_GATE_UP; requires I % 128 == 0), which the
  *   gate/up GEMM streams as contiguous 512-byte row pieces.
+ * When T * k <= 256 * E (the experts average at most two 128-row blocks,
+ * so each weight tile is read by about one row task) both GEMMs load the
+ * weights with MOE_B_STREAM.
  * Intermediates: h = SiLU(gate)*up stored as bf16 [M_pad][I], expert outputs
  * y stored as bf16 [M_pad][H]; both live in the workspace.  The combine is
  * MOE_COMBINE_GATHER (deterministic: same input, same bits).

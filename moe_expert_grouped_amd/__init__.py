@@ -35,6 +35,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_gfx950.so")
 ROW_BLOCK = 128
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
+MOE_B_STREAM = 0x100  # flag on a [K][N] b_layout: non-temporal weight loads
 _DTYPES = {torch.bfloat16: 0, torch.float16: 1}
 _LAYOUTS = {"kn": 0, "nk": 1, "kn_gate_up": 2}
 _EPIS = {"store": 0, "silu_mul": 1, "weighted_scatter": 2}
@@ -189,9 +190,13 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
                  B2: torch.Tensor | None = None, b_layout: str = "kn", epilogue: str = "store",
                  row_pair: torch.Tensor | None = None, pair_w: torch.Tensor | None = None,
                  T: int | None = None, out: torch.Tensor | None = None,
-                 workspace: torch.Tensor | None = None) -> torch.Tensor:
+                 workspace: torch.Tensor | None = None, b_stream: bool = False) -> torch.Tensor:
     """D[r] = A[a(r)] . B[block_group[r // 128]] for r < min(num_rows, cap),
     or SiLU(A.B) * (A.B2) with epilogue="silu_mul".  Returns D [cap, N].
+
+    b_stream=True loads B with the non-temporal cache policy (MOE_B_STREAM;
+    [K][N] layouts only): for weights each tile of which is read by about one
+    row task.  The results are the same bits.
 
     With row_pair given and epilogue "store" or "silu_mul", rows r with
     row_pair[r] < 0 are padding and are not written (nor are rows whose
@@ -236,7 +241,7 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
         workspace = gemm_workspace(cap, A.device)
     _check("grouped_gemm", lib.grouped_gemm(
         _DTYPES[A.dtype], N, K, cap, _ptr(A), _ptr(a_src_row), a_src_div, _ptr(B), _ptr(B2),
-        _LAYOUTS[b_layout], _ptr(block_group), _ptr(num_rows), _EPIS[epilogue], _ptr(row_pair),
+        _LAYOUTS[b_layout] | (MOE_B_STREAM if b_stream else 0), _ptr(block_group), _ptr(num_rows), _EPIS[epilogue], _ptr(row_pair),
         _ptr(pair_w), k, _ptr(out), _ptr(workspace), 0 if workspace is None else workspace.numel(),
         _stream()))
     return out

@@ -4,7 +4,8 @@
 
 Every .hip file under csrc/ is compiled to an object in parallel, then linked
 into one shared library next to this file.  gg_inst.hip is compiled once per
-(epilogue, B layout, dtype) combination of the grouped GEMM (GG_VARIANTS), so
+(epilogue, B layout, dtype, B cache policy) combination of the grouped GEMM
+(GG_VARIANTS), so
 the heavy template instantiations build side by side.  The build always
 recompiles.
 """
@@ -37,8 +38,11 @@ FLAGS = [
 # (epilogue, B stored [K][N], fp16) of every grouped GEMM instantiation the
 # dispatcher in grouped_gemm.hip declares: store and SiLU*up in both layouts
 # and dtypes, the weighted scatter for [K][N] weights.
-GG_VARIANTS = [(e, kn, f) for e in (0, 1) for kn in (1, 0) for f in (0, 1)] + \
-              [(2, 1, 0), (2, 1, 1)]
+# (epilogue, [K][N] B, fp16, non-temporal B): the non-temporal weight loads
+# exist for the [K][N] layouts only
+GG_VARIANTS = [(e, kn, f, 0) for e in (0, 1) for kn in (1, 0) for f in (0, 1)] + \
+              [(2, 1, 0, 0), (2, 1, 1, 0)] + \
+              [(e, 1, f, 1) for e in (0, 1, 2) for f in (0, 1)]
 
 
 def _compile(job) -> str:
@@ -59,8 +63,8 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
         if os.path.basename(src) == "gg_inst.hip":
-            jobs += [(src, (("GG_EPI", e), ("GG_KN", kn), ("GG_FP16", f)))
-                     for e, kn, f in GG_VARIANTS]
+            jobs += [(src, (("GG_EPI", e), ("GG_KN", kn), ("GG_FP16", f), ("GG_NT", nt)))
+                     for e, kn, f, nt in GG_VARIANTS]
         else:
             jobs.append((src, ()))
     # the instantiations are the slow ones: start them first

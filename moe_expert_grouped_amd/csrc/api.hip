@@ -19,7 +19,8 @@ hipError_t launch_permute(const int32_t *, int, int, int, const uint16_t *, int,
                           void *, hipStream_t);
 hipError_t launch_grouped_gemm(int, int, int, const uint16_t *, const int32_t *, int,
                                const uint16_t *, const uint16_t *, int, const int32_t *, int,
-                               const int32_t *, const float *, int, void *, int, hipStream_t);
+                               const int32_t *, const float *, int, void *, int, bool,
+                               hipStream_t);
 hipError_t launch_gg_plan(const int32_t *, const int32_t *, int, int32_t *, hipStream_t);
 size_t gg_plan_bytes(int cap);
 hipError_t launch_combine(const uint16_t *, int, const int32_t *, const float *, int, int,
@@ -140,8 +141,11 @@ int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t 
     return MOE_ERR_INVALID;
   if (N <= 0 || K <= 0 || cap <= 0) return MOE_ERR_INVALID;
   if (dtype != MOE_BF16 && dtype != MOE_FP16) return MOE_ERR_UNSUPPORTED;
+  const bool b_stream = (b_layout & MOE_B_STREAM) != 0;
+  b_layout &= ~MOE_B_STREAM;
   if (b_layout != MOE_B_KN && b_layout != MOE_B_NK && b_layout != MOE_B_KN_GATE_UP)
     return MOE_ERR_UNSUPPORTED;
+  if (b_stream && b_layout == MOE_B_NK) return MOE_ERR_UNSUPPORTED;
   if (epilogue != MOE_EPI_STORE && epilogue != MOE_EPI_SILU_MUL &&
       epilogue != MOE_EPI_WEIGHTED_SCATTER)
     return MOE_ERR_UNSUPPORTED;
@@ -169,7 +173,8 @@ int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t 
     return MOE_ERR_DEVICE;
   return launch_status(moe::launch_grouped_gemm(
       dtype, N, K, (const uint16_t *)A, a_src_row, a_src_div, (const uint16_t *)B,
-      (const uint16_t *)B2, b_layout, plan, epilogue, epi_row_pair, pair_w, k, D, cus, s));
+      (const uint16_t *)B2, b_layout, plan, epilogue, epi_row_pair, pair_w, k, D, cus, b_stream,
+      s));
 }
 
 int moe_pack_gate_up(const void *w_gate, const void *w_up, int E, int K, int N, void *out,
@@ -305,23 +310,27 @@ int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
     e = moe::launch_gg_plan(bexp, mpad, cap, plan, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
   }
+  // weights streamed (non-temporal loads) when the experts average at most
+  // two 128-row blocks: each weight tile is then read by about one row task
+  const bool stream_w = (long)T * k <= 2L * MOE_ROW_BLOCK * E;
   e = moe::launch_grouped_gemm(MOE_BF16, I, H, (const uint16_t *)x, r2p, k,
                                (const uint16_t *)w_gate, (const uint16_t *)w_up,
                                w_up ? MOE_B_KN : MOE_B_KN_GATE_UP, plan,
-                               MOE_EPI_SILU_MUL, nullptr, nullptr, 0, h, cus, s);
+                               MOE_EPI_SILU_MUL, nullptr, nullptr, 0, h, cus, stream_w, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   if (combine == MOE_COMBINE_SCATTER) {
     e = moe::launch_zero(oacc, (long)T * H, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     e = moe::launch_grouped_gemm(MOE_BF16, H, I, h, nullptr, 1, (const uint16_t *)w_down,
                                  nullptr, MOE_B_KN, plan, MOE_EPI_WEIGHTED_SCATTER, r2p, rw, k,
-                                 oacc, cus, s);
+                                 oacc, cus, stream_w, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     return launch_status(moe::launch_finalize(oacc, (long)T * H, (uint16_t *)out, s));
   }
   // padding rows of y are never read: the down GEMM skips their stores
   e = moe::launch_grouped_gemm(MOE_BF16, H, I, h, nullptr, 1, (const uint16_t *)w_down, nullptr,
-                               MOE_B_KN, plan, MOE_EPI_STORE, r2p, nullptr, 0, y, cus, s);
+                               MOE_B_KN, plan, MOE_EPI_STORE, r2p, nullptr, 0, y, cus, stream_w,
+                               s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   e = moe::launch_combine(y, H, p2r, rw, T, k, (uint16_t *)out, s);
   return launch_status(e);

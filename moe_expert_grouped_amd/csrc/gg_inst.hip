@@ -1,7 +1,8 @@
 // gg_inst.hip -- one instantiation of the grouped GEMM launch for the
-// (epilogue, B layout, dtype) combination chosen at compile time with
-// -DGG_EPI=<0|1|2> -DGG_KN=<0|1> -DGG_FP16=<0|1>; the build compiles this
-// file once per combination the dispatcher in grouped_gemm.hip names.
+// (epilogue, B layout, dtype, B cache policy) combination chosen at compile
+// time with -DGG_EPI=<0|1|2> -DGG_KN=<0|1> -DGG_FP16=<0|1> -DGG_NT=<0|1>; the
+// build compiles this file once per combination the dispatcher in
+// grouped_gemm.hip names.
 #include "gg_kernel.h"
 
 #ifndef GG_EPI
@@ -13,8 +14,11 @@
 #ifndef GG_FP16
 #define GG_FP16 0
 #endif
+#ifndef GG_NT
+#define GG_NT 0
+#endif
 
 namespace moe {
-template hipError_t launch_bn<GG_EPI, (GG_KN != 0), (GG_FP16 != 0)>(const GGArgs &, const TileCfg &,
-                                                                    int, hipStream_t);
+template hipError_t launch_bn<GG_EPI, (GG_KN != 0), (GG_FP16 != 0), (GG_NT != 0)>(
+    const GGArgs &, const TileCfg &, int, hipStream_t);
 } // namespace moe

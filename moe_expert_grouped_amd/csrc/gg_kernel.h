@@ -143,10 +143,17 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds_addr) {
 }
 // The same with a wave-uniform 64-bit base (SGPR pair) and a 32-bit per-lane
 // byte offset: the per-lane state is one register instead of a pointer.
+// NT: the non-temporal (streaming) cache policy, for data read about once.
+template <bool NT>
 __device__ __forceinline__ void dma16s(uint32_t voff, const void *sbase, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
-               "s"(sbase), "s"(lds_addr)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff),
+                 "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+                 "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void *g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g),
@@ -296,7 +303,7 @@ __device__ __forceinline__ void scatter_tile(const f32x16 (&acc)[1][MI][NI], flo
 // ring freed at the previous barrier), so the B stream runs NBR - NA
 // slices further ahead and may already be on a later task than the A
 // stream; each stream keeps its own task cursor.
-template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR>
+template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR, bool BNT>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) {
   constexpr int NB = EPI == kEpiSiluMul ? 2 : 1; // B matrices
   constexpr int ARP = BK * 2;                    // bytes per A row (and [N][K] B row) per slice
@@ -535,7 +542,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   auto b_emit = [&](int e) {
     const int m = e / B_INSTR, q = e % B_INSTR;
     const size_t qoff = KN ? (size_t)q * RPI * args.ldb * 2 : (size_t)q * RPI * K * 2;
-    dma16s(b_off[q % QV], b_base[m] + b_koff + qoff, b_stage + m * B_BYTES + q * 1024);
+    dma16s<BNT>(b_off[q % QV], b_base[m] + b_koff + qoff, b_stage + m * B_BYTES + q * 1024);
   };
   auto b_issue = [&]() {
     b_prep();
@@ -763,9 +770,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   wait_vmcnt<0>();
 }
 
-template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR>
+template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR, bool BNT>
 static hipError_t launch_one(const GGArgs &a, int grid, hipStream_t stream) {
-  grouped_gemm_kernel<BN, BK, EPI, KN, FP16, NA, NBR><<<grid, kThreads, 0, stream>>>(a);
+  grouped_gemm_kernel<BN, BK, EPI, KN, FP16, NA, NBR, BNT><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -786,14 +793,14 @@ inline bool tile_supported(int nbm, int bn, int bk, int na, int nb) {
          (bn == 64 && na == 4 && nb == 8);
 }
 
-// Launch of one (epilogue, B layout, dtype) combination with the tile shape
-// c.  Explicitly instantiated in gg_inst.hip, one object per combination;
-// the dispatcher declares those instantiations extern.
-template <int EPI, bool KN, bool FP16>
+// Launch of one (epilogue, B layout, dtype, B cache policy) combination
+// with the tile shape c.  Explicitly instantiated in gg_inst.hip, one object
+// per combination; the dispatcher declares those instantiations extern.
+template <int EPI, bool KN, bool FP16, bool BNT>
 hipError_t launch_bn(const GGArgs &a, const TileCfg &c, int grid, hipStream_t s) {
 #define MOE_GG_CASE(BNV, NAV, NBV)                                                            \
   if (c.bn == BNV && c.bk == 32 && c.na == NAV && c.nb == NBV)                                \
-    return launch_one<BNV, 32, EPI, KN, FP16, NAV, NBV>(a, grid, s);
+    return launch_one<BNV, 32, EPI, KN, FP16, NAV, NBV, BNT>(a, grid, s);
   if constexpr (EPI == kEpiSiluMul) {
     MOE_GG_CASE(128, 3, 6) MOE_GG_CASE(128, 4, 4) MOE_GG_CASE(64, 3, 10) MOE_GG_CASE(64, 4, 4)
   } else {

@@ -6,19 +6,26 @@
 
 namespace moe {
 
-#define MOE_GG_EXTERN(EPI, KN, FP16)                                                          \
-  extern template hipError_t launch_bn<EPI, KN, FP16>(const GGArgs &, const TileCfg &, int,   \
-                                                       hipStream_t);
-MOE_GG_EXTERN(kEpiStore, true, false)
-MOE_GG_EXTERN(kEpiStore, true, true)
-MOE_GG_EXTERN(kEpiStore, false, false)
-MOE_GG_EXTERN(kEpiStore, false, true)
-MOE_GG_EXTERN(kEpiSiluMul, true, false)
-MOE_GG_EXTERN(kEpiSiluMul, true, true)
-MOE_GG_EXTERN(kEpiSiluMul, false, false)
-MOE_GG_EXTERN(kEpiSiluMul, false, true)
-MOE_GG_EXTERN(kEpiScatter, true, false)
-MOE_GG_EXTERN(kEpiScatter, true, true)
+#define MOE_GG_EXTERN(EPI, KN, FP16, NT)                                                      \
+  extern template hipError_t launch_bn<EPI, KN, FP16, NT>(const GGArgs &, const TileCfg &, int, \
+                                                           hipStream_t);
+MOE_GG_EXTERN(kEpiStore, true, false, false)
+MOE_GG_EXTERN(kEpiStore, true, true, false)
+MOE_GG_EXTERN(kEpiStore, false, false, false)
+MOE_GG_EXTERN(kEpiStore, false, true, false)
+MOE_GG_EXTERN(kEpiSiluMul, true, false, false)
+MOE_GG_EXTERN(kEpiSiluMul, true, true, false)
+MOE_GG_EXTERN(kEpiSiluMul, false, false, false)
+MOE_GG_EXTERN(kEpiSiluMul, false, true, false)
+MOE_GG_EXTERN(kEpiScatter, true, false, false)
+MOE_GG_EXTERN(kEpiScatter, true, true, false)
+// weights streamed with the non-temporal policy ([K][N] layouts only)
+MOE_GG_EXTERN(kEpiStore, true, false, true)
+MOE_GG_EXTERN(kEpiStore, true, true, true)
+MOE_GG_EXTERN(kEpiSiluMul, true, false, true)
+MOE_GG_EXTERN(kEpiSiluMul, true, true, true)
+MOE_GG_EXTERN(kEpiScatter, true, false, true)
+MOE_GG_EXTERN(kEpiScatter, true, true, true)
 #undef MOE_GG_EXTERN
 
 // Tile configurations: (BN, BK, A ring depth, B ring depth, super-block row
@@ -113,16 +120,31 @@ hipError_t launch_gg_plan(const int32_t *block_group, const int32_t *num_rows, i
   return hipGetLastError();
 }
 
+// [K][N] weights loaded with the non-temporal policy (each weight tile read
+// by about one row task: streamed, not kept in the caches)
+static hipError_t launch_kn_stream(const GGArgs &a, const TileCfg &c, int epilogue, bool fp16,
+                                   int grid, hipStream_t stream) {
+  if (epilogue == kEpiScatter)
+    return fp16 ? launch_bn<kEpiScatter, true, true, true>(a, c, grid, stream)
+                : launch_bn<kEpiScatter, true, false, true>(a, c, grid, stream);
+  if (epilogue == kEpiSiluMul)
+    return fp16 ? launch_bn<kEpiSiluMul, true, true, true>(a, c, grid, stream)
+                : launch_bn<kEpiSiluMul, true, false, true>(a, c, grid, stream);
+  return fp16 ? launch_bn<kEpiStore, true, true, true>(a, c, grid, stream)
+              : launch_bn<kEpiStore, true, false, true>(a, c, grid, stream);
+}
+
 // dtype 0 bf16 / 1 fp16; layout 0 KN / 1 NK / 2 KN with gate and up
 // interleaved in 128-column blocks (SILU_MUL; B2 unused); epilogue 0 STORE / 1 SILU_MUL /
-// 2 WEIGHTED_SCATTER (KN only; D is then the fp32 token-row accumulator).
-// `plan` holds the row-task plan of block_group (launch_gg_plan), built
-// earlier on the same stream.
+// 2 WEIGHTED_SCATTER (KN only; D is then the fp32 token-row accumulator);
+// b_stream: B loaded with the non-temporal policy (KN only).  `plan` holds
+// the row-task plan of block_group (launch_gg_plan), built earlier on the
+// same stream.
 hipError_t launch_grouped_gemm(int dtype, int N, int K, const uint16_t *A,
                                const int32_t *a_src_row, int a_src_div, const uint16_t *B,
                                const uint16_t *B2, int layout, const int32_t *plan, int epilogue,
                                const int32_t *epi_row_pair, const float *pair_w, int topk,
-                               void *D, int num_cus, hipStream_t stream) {
+                               void *D, int num_cus, bool b_stream, hipStream_t stream) {
   const TileCfg c = tile_config(epilogue, N, K);
   const int grid = num_cus; // one workgroup per CU (LDS-limited)
   const bool scat = epilogue == kEpiScatter;
@@ -134,21 +156,23 @@ hipError_t launch_grouped_gemm(int dtype, int N, int K, const uint16_t *A,
   const bool kn = layout == 0 || il;
   if (il && (epilogue != kEpiSiluMul || N % 128 != 0 || c.bn > 128 || 128 % c.bn != 0))
     return hipErrorInvalidValue;
+  if (b_stream && !kn) return hipErrorInvalidValue;
+  if (b_stream) return launch_kn_stream(a, c, epilogue, fp16, grid, stream);
   if (scat) {
     if (!kn) return hipErrorInvalidValue;
-    return fp16 ? launch_bn<kEpiScatter, true, true>(a, c, grid, stream)
-                : launch_bn<kEpiScatter, true, false>(a, c, grid, stream);
+    return fp16 ? launch_bn<kEpiScatter, true, true, false>(a, c, grid, stream)
+                : launch_bn<kEpiScatter, true, false, false>(a, c, grid, stream);
   }
   if (epilogue == kEpiSiluMul) {
-    if (kn) return fp16 ? launch_bn<kEpiSiluMul, true, true>(a, c, grid, stream)
-                        : launch_bn<kEpiSiluMul, true, false>(a, c, grid, stream);
-    return fp16 ? launch_bn<kEpiSiluMul, false, true>(a, c, grid, stream)
-                : launch_bn<kEpiSiluMul, false, false>(a, c, grid, stream);
+    if (kn) return fp16 ? launch_bn<kEpiSiluMul, true, true, false>(a, c, grid, stream)
+                        : launch_bn<kEpiSiluMul, true, false, false>(a, c, grid, stream);
+    return fp16 ? launch_bn<kEpiSiluMul, false, true, false>(a, c, grid, stream)
+                : launch_bn<kEpiSiluMul, false, false, false>(a, c, grid, stream);
   }
-  if (kn) return fp16 ? launch_bn<kEpiStore, true, true>(a, c, grid, stream)
-                      : launch_bn<kEpiStore, true, false>(a, c, grid, stream);
-  return fp16 ? launch_bn<kEpiStore, false, true>(a, c, grid, stream)
-              : launch_bn<kEpiStore, false, false>(a, c, grid, stream);
+  if (kn) return fp16 ? launch_bn<kEpiStore, true, true, false>(a, c, grid, stream)
+                      : launch_bn<kEpiStore, true, false, false>(a, c, grid, stream);
+  return fp16 ? launch_bn<kEpiStore, false, true, false>(a, c, grid, stream)
+              : launch_bn<kEpiStore, false, false, false>(a, c, grid, stream);
 }
 
 } // namespace moe

@@ -115,6 +115,11 @@ def test_grouped_gemm_validation(lib):
     assert call(lay=2, epi=1, B2=FAKE) == moe.MOE_ERR_INVALID
     assert call(lay=2, epi=0) == moe.MOE_ERR_INVALID
     assert call(lay=2, epi=1, N=192) == moe.MOE_ERR_UNSUPPORTED
+    # non-temporal weight loads: a flag on the [K][N] layouts only
+    assert call(lay=1 | moe.MOE_B_STREAM) == moe.MOE_ERR_UNSUPPORTED
+    assert call(lay=3 | moe.MOE_B_STREAM) == moe.MOE_ERR_UNSUPPORTED
+    assert call(lay=2 | moe.MOE_B_STREAM, epi=1, B2=FAKE) == moe.MOE_ERR_INVALID
+    assert call(lay=0x200) == moe.MOE_ERR_UNSUPPORTED
     assert call(epi=1) == moe.MOE_ERR_INVALID          # SiLU*up needs B2
     assert call(epi=7) == moe.MOE_ERR_UNSUPPORTED
     assert call(src=FAKE, div=0) == moe.MOE_ERR_INVALID

@@ -307,6 +307,40 @@ def _run_scatter(P, A, B, w, *, N, K, dtype="bf16", out=None):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("epi,layout", [("store", "kn"), ("silu_mul", "kn"), ("silu_mul", "kn_gate_up"),
+                                        ("weighted_scatter", "kn")])
+def test_streamed_weights_same_bits(dtype, epi, layout):
+    # MOE_B_STREAM changes only the cache policy of the weight loads: the
+    # same bits as without it (integer-exact data, so the scatter's atomic
+    # sums are unique too)
+    T, k, E, K = 300, 2, 5, 256
+    N = 128 if epi == "silu_mul" else 256
+    P, A, B, w = _scatter_case(T, k, E, K, N, 70, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    Bt = dev16(B, tdt)
+    B2t = dev16(syn.ternary_bits((E, K, N), 71, dtype), tdt) if epi == "silu_mul" else None
+    if layout == "kn_gate_up":
+        Bt, B2t = moe.pack_gate_up(Bt, B2t), None
+    At = dev16(A, tdt)
+    bexp = torch.from_numpy(P["block_expert"]).cuda()
+    mpad = torch.tensor([P["m_pad"]], dtype=torch.int32, device="cuda")
+    r2p = torch.from_numpy(P["row_to_pair"]).cuda()
+    say("streamed weights", dtype, epi, layout)
+
+    def run(stream):
+        if epi == "weighted_scatter":
+            return moe.grouped_gemm(At, Bt, bexp, mpad, N=N, K=K, cap=P["cap"], epilogue=epi,
+                                    row_pair=r2p, pair_w=torch.from_numpy(w).cuda(), b_stream=stream)
+        out = torch.full((P["cap"], N), float("nan"), dtype=tdt, device="cuda")
+        return moe.grouped_gemm(At, Bt, bexp, mpad, N=N, K=K, cap=P["cap"], B2=B2t, b_layout=layout,
+                                epilogue=epi, row_pair=r2p, out=out, b_stream=stream)
+    plain, streamed = run(False), run(True)
+    torch.cuda.synchronize()
+    iv = torch.int32 if epi == "weighted_scatter" else torch.int16
+    assert torch.equal(plain.view(iv), streamed.view(iv))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("T,k,E,K,N", [(150, 3, 4, 320, 256), (200, 1, 5, 64, 128), (90, 2, 3, 128, 192)])
 def test_weighted_scatter_integer_exact(dtype, T, k, E, K, N):
     P, A, B, w = _scatter_case(T, k, E, K, N, seed=T + N, dtype=dtype)
