@@ -52,7 +52,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 #pragma unroll
   for (int h = 0; h < 4; ++h)
     o[h] = (uint32_t)f32_to_bf16(acc[2 * h]) | ((uint32_t)f32_to_bf16(acc[2 * h + 1]) << 16);
-  *reinterpret_cast<u32x4 *>(out + (size_t)t * H + col) = o;
+  // non-temporal: the output is written once and not read here
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(out + (size_t)t * H + col));
 }
 
 hipError_t launch_combine(const uint16_t *y, int H, const int32_t *pair_to_row, const float *w,

@@ -20,10 +20,13 @@
 //                            in LDS order the wavefronts), then the row maps;
 //                            the same grid marks padding rows with -1
 //   pass 4  permute_gather   optional: x_perm[row] = x[token of row] below
-//                            M_pad, zero rows for padding (16-byte vectors)
+//                            M_pad (each x row read once, stored to its k
+//                            rows), zero rows for padding (16-byte vectors)
 // Routings of at most 16384 pairs take passes 1-3 in a single launch
 // instead (permute_plan.hip).
 #include "common.h"
+
+#include <algorithm>
 
 namespace moe {
 
@@ -194,37 +197,43 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter(
   }
 }
 
-// One wavefront per row below M_pad (read on the device): each lane loads up
-// to 8 16-byte vectors of the source row before storing any, so 8 KiB per
-// wavefront are in flight (H = 4096); padding rows are zero-filled.  Rows at
-// or past M_pad are not written.
+// The row gather, token by token: one wavefront per (token, 512-column
+// chunk) loads the chunk of x[t] once (64 lanes x 16 bytes) and stores it
+// to the rows of the token's k pairs (pairs without a row are skipped);
+// then the same grid zero-fills the chunks of the padding rows below M_pad
+// (read on the device).  Rows at or past M_pad are not written.  The stores
+// are non-temporal: x_perm is written once and not read back here.
 __global__ __launch_bounds__(256) void permute_gather(const uint16_t *__restrict__ x, int H,
+                                                      const int32_t *__restrict__ pair_to_row,
                                                       const int32_t *__restrict__ row_to_pair,
                                                       const int32_t *__restrict__ num_padded_rows,
-                                                      int k, int cap,
+                                                      int T, int k, int cap,
                                                       uint16_t *__restrict__ x_perm) {
   // H % 8 == 0, 16-byte vectors
   const int lane = threadIdx.x & 63;
-  const int waves = (gridDim.x * blockDim.x) >> 6;
-  const int nvec = H / 8;
-  const int rows = min(num_padded_rows[0], cap);
-  for (int r = (blockIdx.x * blockDim.x + threadIdx.x) >> 6; r < rows; r += waves) {
-    const int p = row_to_pair[r];
-    u32x4 *dst = reinterpret_cast<u32x4 *>(x_perm + (size_t)r * H);
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (size_t)(p < 0 ? 0 : p / k) * H);
-    for (int v0 = 0; v0 < nvec; v0 += 64 * 8) {
-      u32x4 buf[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int v = v0 + u * 64 + lane;
-        buf[u] = (p >= 0 && v < nvec) ? src[v] : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int v = v0 + u * 64 + lane;
-        if (v < nvec) dst[v] = buf[u];
-      }
+  const long wid = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const long nw = ((long)gridDim.x * blockDim.x) >> 6;
+  const int chunks = (H + 511) / 512;
+  const long tok_chunks = (long)T * chunks;
+  for (long q = wid; q < tok_chunks; q += nw) {
+    const int t = (int)(q / chunks);
+    const int col = (int)(q - (long)t * chunks) * 512 + lane * 8;
+    if (col >= H) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(x + (size_t)t * H + col);
+    for (int j = 0; j < k; ++j) {
+      const int r = pair_to_row[(size_t)t * k + j];
+      if (r < 0) continue;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(x_perm + (size_t)r * H + col));
     }
+  }
+  const int rows = min(num_padded_rows[0], cap);
+  const long row_chunks = (long)rows * chunks;
+  for (long q = wid; q < row_chunks; q += nw) {
+    const int r = (int)(q / chunks);
+    const int col = (int)(q - (long)r * chunks) * 512 + lane * 8;
+    if (col >= H || row_to_pair[r] >= 0) continue;
+    __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u},
+                                reinterpret_cast<u32x4 *>(x_perm + (size_t)r * H + col));
   }
 }
 
@@ -263,9 +272,11 @@ hipError_t launch_permute(const int32_t *idx, int T, int k, int E, const uint16_
                                                           row_to_pair);
   }
   if (x && x_perm) {
-    const int rows_per_block = 4;
-    const int grid = min(cap / rows_per_block, 8192);
-    permute_gather<<<grid, 256, 0, stream>>>(x, H, row_to_pair, num_padded_rows, k, cap, x_perm);
+    // four wavefronts per workgroup, one (token, chunk) each per pass
+    const long waves = (long)T * ((H + 511) / 512);
+    const int grid = (int)std::min<long>((waves + 3) / 4, 8192);
+    permute_gather<<<grid, 256, 0, stream>>>(x, H, pair_to_row, row_to_pair, num_padded_rows, T,
+                                             k, cap, x_perm);
   }
   return hipGetLastError();
 }
