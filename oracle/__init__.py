@@ -44,6 +44,8 @@ def _bind(path):
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I = ctypes.c_int
+    lib.oracle_router_logits.argtypes = [P, P, I, I, I, P]
+    lib.oracle_router_logits.restype = None
     lib.oracle_route.argtypes = [P, I, I, I, P, P]
     lib.oracle_route.restype = None
     lib.oracle_permute.argtypes = [P, I, I, I, I, P, P, P, P, P]
@@ -122,6 +124,20 @@ def padded_capacity(T: int, k: int, E: int) -> int:
     R = T * k
     cap = R + min(E, R) * (ROW_BLOCK - 1)
     return (cap + ROW_BLOCK - 1) // ROW_BLOCK * ROW_BLOCK
+
+
+def router_logits(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """logits[t][e] = x[t] . W[e] in double (x [T][H], W [E][H], bf16 bits):
+    the linear router whose output the routing takes.  Returns float64 [T,E]."""
+    xb, xp = _c(x_bits, np.uint16)
+    wb, wp = _c(w_bits, np.uint16)
+    T, H = xb.shape
+    E = wb.shape[0]
+    if wb.shape[1] != H:
+        raise ValueError("W must be [E][H]")
+    out = np.empty((T, E), np.float64)
+    _load().oracle_router_logits(xp, wp, T, H, E, out.ctypes.data_as(ctypes.c_void_p))
+    return out
 
 
 def route(logits: np.ndarray, k: int):

@@ -82,6 +82,25 @@ int oracle_num_threads(void) {
 }
 
 /* ------------------------------------------------------------------ */
+/* O0 router logits, the input of O1: the pages take the logits as given */
+/* (part (1), section 4: the route that the reorder follows); the reading */
+/* taken is the plain linear router, logits[t][e] = x[t] . W[e] with W   */
+/* stored [E][H] (one row of hidden weights per expert, no bias).        */
+/* ------------------------------------------------------------------ */
+void oracle_router_logits(const uint16_t *x, const uint16_t *w, int T, int H, int E,
+                          double *logits) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    for (int e = 0; e < E; ++e) {
+      double s = 0.0;
+      for (int h = 0; h < H; ++h)
+        s += bf16_to_double(x[(size_t)t * H + h]) * bf16_to_double(w[(size_t)e * H + h]);
+      logits[(size_t)t * E + e] = s;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
 /* O1 route: top-k of each token's router logits, softmax over the k    */
 /* selected logits.  Slot 0 holds the largest logit; equal logits go to  */
 /* the lower expert id.                                                  */

@@ -10,6 +10,10 @@ from test_oracle_pins import PINS
 
 # (name, exact text in the oracle source, replacement)
 MUTATIONS = [
+    ("router_transposed_w", "bf16_to_double(w[(size_t)e * H + h]);",
+     "bf16_to_double(w[(size_t)h * E + e]);"),
+    ("router_dropped_term", "for (int h = 0; h < H; ++h)\n        s += bf16_to_double(x[",
+     "for (int h = 1; h < H; ++h)\n        s += bf16_to_double(x["),
     ("tie_to_higher_id", "if (best < 0 || l[e] > l[best]) best = e;",
      "if (best < 0 || l[e] >= l[best]) best = e;"),
     ("softmax_sign", "z += exp((double)l[idx[(size_t)t * k + j]] - m);",

@@ -45,6 +45,28 @@ def f32(bits):
 # ---------------------------------------------------------------- pins as functions of an oracle API
 # (so that the mutation tests can run the same pins against planted mistakes)
 
+def pin_router_logits(O):
+    rng = np.random.default_rng(21)
+    # one-hot token rows pick out one hidden column of W exactly (non-square
+    # T, H, E, so a transposed W or a wrong row stride shows)
+    T, H, E = 7, 40, 5
+    W = syn.bf16_bits(rng.standard_normal((E, H)).astype(np.float32))
+    hs = rng.integers(0, H, size=T)
+    x = np.zeros((T, H), np.uint16)
+    x[np.arange(T), hs] = 0x3F80  # bf16 1.0
+    lg = O.router_logits(x, W)
+    assert np.array_equal(lg, f32(W)[:, hs].T)
+    # entries in {-1, 0, 1}: integer logits, exact against an integer matrix product
+    x = syn.ternary_bits((33, 96), 22)
+    W = syn.ternary_bits((11, 96), 23)
+    lg = O.router_logits(x, W)
+    assert np.array_equal(lg, (f32(x).astype(np.int64) @ f32(W).astype(np.int64).T).astype(np.float64))
+    # linear in x: doubling a row doubles its logits exactly
+    x2 = x.copy()
+    x2[0] = syn.bf16_bits(2.0 * f32(x[:1]).astype(np.float32))[0]
+    assert np.array_equal(O.router_logits(x2, W)[0], 2.0 * lg[0])
+
+
 def pin_route_bruteforce(O):
     rng = np.random.default_rng(1)
     for T, E, k in [(50, 8, 2), (40, 64, 4), (30, 257, 8), (20, 5, 5), (10, 1, 1), (33, 16, 1)]:
@@ -379,7 +401,7 @@ def pin_pipeline_equals_definition(O):
     assert np.max(np.abs(err)) < 2e-2 * np.max(np.abs(ref))
 
 
-PINS = [pin_route_bruteforce, pin_route_closed_forms, pin_route_golden, pin_permute, pin_gather,
+PINS = [pin_router_logits, pin_route_bruteforce, pin_route_closed_forms, pin_route_golden, pin_permute, pin_gather,
         pin_gemm_random, pin_gemm_integer_exact, pin_fp16_decode, pin_silu, pin_combine, pin_weighted_scatter,
         pin_layer_dense_special_case, pin_layer_bruteforce, pin_layer_golden,
         pin_pipeline_equals_definition]
