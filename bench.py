@@ -222,6 +222,14 @@ def main():
             lambda: moe.permute(idx_t, E, x=x, x_perm=next_buf("xp", xps), workspace=pws),
             a.steps),
     }
+    # the router front end (moe_router: logits = x . W_r^T, then the routing)
+    # on the same tokens, with seeded router weights [E][H]
+    wr_bits = syn.bf16_bits((np.random.default_rng(7).standard_normal((E, H)) /
+                             np.sqrt(H)).astype(np.float32))
+    wr = torch.from_numpy(wr_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    rws = torch.empty(max(moe.load_library().moe_router_workspace_size(T, H, E), 256),
+                      dtype=torch.uint8, device="cuda")
+    batched["router"] = graph_batch_us(lambda: moe.router(x, wr, k, workspace=rws), a.steps)
     # the row gather alone: the permutation with it minus the permutation
     batched["gather"] = batched["permute_with_gather"] - batched["permute"]
     m_pad = int(P.num_padded_rows.item())
@@ -233,6 +241,7 @@ def main():
     gu_bytes = 4.0 * e_act * H * I + 2.0 * T * H + 2.0 * R * I      # weights, x, h
     comb_bytes = 2.0 * R * H + 2.0 * T * H                          # y rows read, out written
     gath_bytes = 2.0 * T * H + 2.0 * m_pad * H                      # x read once, x_perm written
+    router_bytes = 2.0 * T * H + 2.0 * E * H + 8.0 * T * k          # x, W_r, the routing
     dn_bytes = 2.0 * e_act * I * H + 2.0 * R * I + 2.0 * R * H      # weights, h, y
     layer_s = ms * 1e-3
     gemm_s = (dur["gate_up"] + dur["down"]) * 1e-3
@@ -271,7 +280,8 @@ def main():
             for n, us, b in (("gate_up", dur["gate_up"] * 1e3, gu_bytes),
                              ("down", dur["down"] * 1e3, dn_bytes),
                              ("combine", batched["combine"], comb_bytes),
-                             ("gather", batched["gather"], gath_bytes))},
+                             ("gather", batched["gather"], gath_bytes),
+                             ("router", batched["router"], router_bytes))},
         "layer_us_per_step": stats,
         "hip_graph": {"layer_us_per_step": stats_graph},
         "unpacked_gate_up_weights": {"layer_us_per_step": stats_unpacked},

@@ -116,6 +116,36 @@ int moe_route(const float *logits, int T, int E, int k, int32_t *topk_idx,
               float *topk_w, void *stream);
 
 /* ------------------------------------------------------------------------
+ * moe_router -- the router front end in one launch: the logits of the
+ * linear router, then exactly moe_route on them.       [P2 s.4, the route]
+ * The pages take the logits as given; the step before them is read as the
+ * plain linear router without bias:
+ *   logits[t][e] = sum_h x[t][h] * w_router[e][h]
+ * accumulated in fp32 from the bf16 products: the hidden dimension is cut
+ * into 4 S parts (S a power of two fixed by T and H alone), each summed on
+ * the matrix cores, then the parts are added in a fixed order -- the same
+ * bits on every run and every device.  The selection and weights are those
+ * of moe_route taken on these fp32 logits.
+ *   x        [T][H] bf16, 16-byte aligned
+ *   w_router [E][H] bf16 (one row per expert, the nn.Linear layout), 16-byte
+ *            aligned
+ *   logits   [T][E] fp32 out, or NULL (not written)
+ *   topk_idx [T][k] int32 out;  topk_w [T][k] fp32 out
+ * Requires 1 <= k <= E, k <= 16, E <= 128, H % 64 == 0
+ * (MOE_ERR_UNSUPPORTED otherwise).  workspace: moe_router_workspace_size
+ * bytes, 16-byte aligned (MOE_ERR_WORKSPACE if short).
+ * ---------------------------------------------------------------------- */
+int moe_router(const void *x, const void *w_router, int T, int H, int E, int k,
+               float *logits, int32_t *topk_idx, float *topk_w, void *workspace,
+               size_t ws_bytes, void *stream);
+
+/* Workspace bytes of moe_router (0: none needed, workspace may be NULL; 0
+ * also for unsupported sizes).  Fewer than 8161 tokens cut the hidden
+ * dimension into up to 16 slices (S of them: S * T * E floats of partial
+ * logits). */
+size_t moe_router_workspace_size(int T, int H, int E);
+
+/* ------------------------------------------------------------------------
  * moe_permute -- reorder (token, slot) pairs into expert-contiguous,
  * 128-row-aligned blocks.                              [P1 s.4; P2 s.4, s.5]
  * Pair p = t*k + j routed to expert e = topk_idx[p].  Outputs:

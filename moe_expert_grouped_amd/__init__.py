@@ -65,6 +65,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "moe_version": ([], ctypes.c_char_p),
             "moe_padded_capacity": ([I, I, I], I),
             "moe_route": ([P, I, I, I, P, P, P], I),
+            "moe_router": ([P, P, I, I, I, I, P, P, P, P, Z, P], I),
+            "moe_router_workspace_size": ([I, I, I], Z),
             "moe_permute_workspace_size": ([I, I, I], Z),
             "moe_permute": ([P, I, I, I, P, I, P, P, P, P, P, P, P, I, P, Z, P], I),
             "grouped_gemm_workspace_size": ([I], Z),
@@ -126,6 +128,32 @@ def route(logits: torch.Tensor, k: int):
     w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
     _check("moe_route", load_library().moe_route(_ptr(logits), T, E, k, _ptr(idx), _ptr(w), _stream()))
     return idx, w
+
+
+def router(x: torch.Tensor, w_router: torch.Tensor, k: int, with_logits: bool = False,
+           workspace: torch.Tensor | None = None):
+    """The linear router and the routing in one launch: logits = x . w_router^T
+    (x [T,H] bf16, w_router [E,H] bf16, fp32 accumulation), then the top-k and
+    softmax of `route` on those logits.  Returns (idx int32 [T,k], w fp32 [T,k],
+    logits fp32 [T,E] or None)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_router, "w_router", torch.bfloat16, 2)
+    T, H = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != H:
+        raise ValueError("w_router must be [E, H]")
+    dev = x.device
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    lg = torch.empty((T, E), dtype=torch.float32, device=dev) if with_logits else None
+    lib = load_library()
+    need = lib.moe_router_workspace_size(T, H, E)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check("moe_router", lib.moe_router(_ptr(x), _ptr(w_router), T, H, E, k, _ptr(lg), _ptr(idx),
+                                        _ptr(w), _ptr(workspace),
+                                        0 if workspace is None else workspace.numel(), _stream()))
+    return idx, w, lg
 
 
 # ---------------------------------------------------------------- permute

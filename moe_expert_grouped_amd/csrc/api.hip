@@ -8,6 +8,10 @@
 
 namespace moe {
 hipError_t launch_route(const float *, int, int, int, int32_t *, float *, hipStream_t);
+bool router_fits(int H, int E);
+size_t router_workspace_bytes(int T, int H, int E);
+hipError_t launch_router(const uint16_t *, const uint16_t *, int, int, int, int, float *,
+                         int32_t *, float *, void *, hipStream_t);
 hipError_t launch_pack_gate_up(const uint16_t *, const uint16_t *, int, int, int, uint16_t *,
                                hipStream_t);
 bool permute_plan_fits(int T, int E, int k);
@@ -97,6 +101,27 @@ int moe_route(const float *logits, int T, int E, int k, int32_t *topk_idx, float
   if (device_cus() == 0) return MOE_ERR_DEVICE;
   return launch_status(
       moe::launch_route(logits, T, E, k, topk_idx, topk_w, (hipStream_t)stream));
+}
+
+size_t moe_router_workspace_size(int T, int H, int E) {
+  if (T <= 0 || H <= 0 || E <= 0 || !moe::router_fits(H, E)) return 0;
+  return align256(moe::router_workspace_bytes(T, H, E));
+}
+
+int moe_router(const void *x, const void *w_router, int T, int H, int E, int k, float *logits,
+               int32_t *topk_idx, float *topk_w, void *workspace, size_t ws_bytes,
+               void *stream) {
+  if (!x || !w_router || !topk_idx || !topk_w) return MOE_ERR_INVALID;
+  if (T <= 0 || H <= 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID;
+  if (!moe::router_fits(H, E) || k > 16) return MOE_ERR_UNSUPPORTED;
+  const size_t need = moe::router_workspace_bytes(T, H, E);
+  if (need && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return MOE_ERR_INVALID;
+  if (device_cus() == 0) return MOE_ERR_DEVICE;
+  return launch_status(moe::launch_router((const uint16_t *)x, (const uint16_t *)w_router, T, H,
+                                          E, k, logits, topk_idx, topk_w, workspace,
+                                          (hipStream_t)stream));
 }
 
 size_t moe_permute_workspace_size(int T, int k, int E) {

@@ -8,24 +8,12 @@
 // softmax over the k selected logits.
 //
 // Design: one 64-lane wavefront per token.  Each lane holds ceil(E/64)
-// logits in registers (E <= 1024).  Each of the k rounds finds the lane-local
-// best untaken (value, id), then a cross-lane butterfly reduction picks the
-// global best with the lower-id tie-break; comparisons are exact fp32, so the
-// selection matches any correct implementation bit for bit.  The softmax is
-// fp32 on the k selected values.  Memory traffic is 4*T*E + 8*T*k bytes with
+// logits in registers (E <= 1024); the selection and the softmax are
+// topk_softmax (topk.h).  Memory traffic is 4*T*E + 8*T*k bytes with
 // coalesced row loads; the kernel is latency-bound at the shapes of interest.
-#include "common.h"
+#include "topk.h"
 
 namespace moe {
-
-struct Cand {
-  float v;
-  int e;
-};
-
-__device__ __forceinline__ bool better(const Cand &a, const Cand &b) {
-  return a.v > b.v || (a.v == b.v && a.e < b.e);
-}
 
 template <int EPL>
 __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ logits, int T,
@@ -38,59 +26,12 @@ __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ lo
 
   const float *row = logits + (size_t)t * E;
   float v[EPL];
-  bool taken[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
-    taken[i] = e >= E; // slots past E never compete
     v[i] = e < E ? row[e] : 0.0f;
   }
-
-  float sel_v = 0.0f; // lane j keeps the j-th selected logit / id
-  int sel_e = 0;
-  float top = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    Cand c{0.0f, 0x7fffffff};
-    bool have = false;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      if (!taken[i]) {
-        Cand d{v[i], lane + 64 * i};
-        if (!have || better(d, c)) c = d;
-        have = true;
-      }
-    }
-    // a lane with nothing left offers an id that loses every comparison
-    if (!have) c.v = -__builtin_inff();
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      Cand o;
-      o.v = __shfl_xor(c.v, off, 64);
-      o.e = __shfl_xor(c.e, off, 64);
-      if (better(o, c)) c = o;
-    }
-    // c is now the same (value, id) in every lane
-    if (j == 0) top = c.v;
-    if (lane == j) {
-      sel_v = c.v;
-      sel_e = c.e;
-    }
-    const int owner_slot = c.e >> 6;
-    if ((c.e & 63) == lane) {
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (i == owner_slot) taken[i] = true;
-    }
-  }
-
-  const float ex = lane < k ? expf(sel_v - top) : 0.0f;
-  float s = ex;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-  if (lane < k) {
-    topk_idx[(size_t)t * k + lane] = sel_e;
-    topk_w[(size_t)t * k + lane] = ex / s;
-  }
+  topk_softmax<EPL>(v, E, k, lane, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
 }
 
 hipError_t launch_route(const float *logits, int T, int E, int k, int32_t *topk_idx,

@@ -28,8 +28,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 15, names
-    for n in ["moe_route", "moe_permute", "grouped_gemm", "moe_combine", "moe_finalize", "moe_layer",
+    assert len(names) == 17, names
+    for n in ["moe_route", "moe_router", "moe_permute", "grouped_gemm", "moe_combine", "moe_finalize", "moe_layer",
               "moe_layer_ex", "moe_pack_gate_up"]:
         assert n in names
     for n in names:
@@ -71,6 +71,32 @@ def test_layer_workspace_layout(lib):
 FAKE = ctypes.c_void_p(4096)       # aligned non-null; never dereferenced
 MISALIGNED = ctypes.c_void_p(4098)
 NULL = None
+
+
+def test_router_validation(lib):
+    def call(x=FAKE, w=FAKE, T=4, H=256, E=8, k=2, lg=NULL, idx=FAKE, wo=FAKE, ws=FAKE, wsb=1 << 20):
+        return lib.moe_router(x, w, T, H, E, k, lg, idx, wo, ws, wsb, NULL)
+    assert call(x=NULL) == moe.MOE_ERR_INVALID
+    assert call(w=NULL) == moe.MOE_ERR_INVALID
+    assert call(idx=NULL) == moe.MOE_ERR_INVALID
+    assert call(wo=NULL) == moe.MOE_ERR_INVALID
+    assert call(x=MISALIGNED) == moe.MOE_ERR_INVALID
+    assert call(w=MISALIGNED) == moe.MOE_ERR_INVALID
+    assert call(T=0) == moe.MOE_ERR_INVALID
+    assert call(k=9) == moe.MOE_ERR_INVALID          # k > E
+    assert call(H=96) == moe.MOE_ERR_UNSUPPORTED     # H % 64
+    assert call(E=129) == moe.MOE_ERR_UNSUPPORTED
+    assert call(E=64, k=17) == moe.MOE_ERR_UNSUPPORTED
+    assert call(ws=NULL) == moe.MOE_ERR_WORKSPACE    # 4 tokens: the hidden dimension is split
+    assert call(wsb=16) == moe.MOE_ERR_WORKSPACE
+    assert call(ws=MISALIGNED) == moe.MOE_ERR_INVALID
+    assert call(lg=FAKE) == moe.MOE_ERR_DEVICE       # valid arguments; no GPU here
+    # the slices: only a short routing needs the workspace, which holds S partial [T][E] tiles
+    assert lib.moe_router_workspace_size(2048, 4096, 64) == 4 * 2048 * 64 * 4
+    assert lib.moe_router_workspace_size(8192, 4096, 64) == 0
+    assert lib.moe_router_workspace_size(300, 192, 128) == 0
+    assert lib.moe_router_workspace_size(4, 256, 8) == 4 * 4 * 8 * 4
+    assert lib.moe_router_workspace_size(4, 96, 8) == 0
 
 
 def test_route_validation(lib):

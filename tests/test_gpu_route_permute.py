@@ -108,6 +108,40 @@ def _small_layer_inputs(T, H, E, k, I, seed):
             dev16(bits((E, I, H))))
 
 
+# router front end: every column-tile count (E up to 32, 64, 96, 128), a
+# hidden quarter below and above one load batch, ragged token blocks, the
+# tp_share router shape
+@pytest.mark.parametrize("T,H,E,k", [(2048, 4096, 64, 4), (77, 256, 5, 2), (300, 192, 128, 16),
+                                     (33, 64, 33, 3), (1, 512, 1, 1), (1000, 1024, 96, 8),
+                                     (512, 4096, 16, 1)])
+def test_router_matches_oracle(T, H, E, k):
+    g = np.random.default_rng(T + H + E + k)
+    x = syn.bf16_bits(g.standard_normal((T, H)).astype(np.float32))
+    W = syn.bf16_bits((g.standard_normal((E, H)) / np.sqrt(H)).astype(np.float32))
+    say("router", "T", T, "H", H, "E", E, "k", k)
+    idx, w, lg = moe.router(dev16(x), dev16(W), k, with_logits=True)
+    torch.cuda.synchronize()
+    idx, w, lg = idx.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy()
+    # logits: within the fp32 summation bound of the exact sum (bf16 products
+    # are exact in fp32; H additions at most, each off by half an ulp)
+    ref = oracle.router_logits(x, W)
+    mag = oracle.router_logits(x & 0x7FFF, W & 0x7FFF)    # sum of |x||w|
+    bound = H * 2.0 ** -24 / (1 - H * 2.0 ** -24) * mag
+    assert np.all(np.abs(lg.astype(np.float64) - ref) <= bound)
+    # the selection on the kernel's own fp32 logits: exactly the routing rule
+    ridx, rw = oracle.route(lg, k)
+    assert np.array_equal(idx, ridx)
+    assert np.max(np.abs(w.astype(np.float64) - rw) / np.abs(rw)) <= 1e-6
+    # against the routing of the exact logits: a token may differ only at a
+    # near tie, where the two choices are within the logits' error bound
+    oidx, _ = oracle.route(ref.astype(np.float32), k)
+    for t in np.nonzero(np.any(idx != oidx, axis=1))[0]:
+        a, b = set(idx[t]), set(oidx[t])
+        pairs = [(e, f) for e in a - b for f in b - a] or list(zip(idx[t], oidx[t]))
+        for e, f in pairs:
+            assert abs(ref[t, e] - ref[t, f]) <= 2 * (bound[t, e] + bound[t, f]), (t, e, f)
+
+
 # shapes of every variant of the one-launch routing + permutation + plan
 # (tokens per thread 1, 2, 4 x top-k list of 4, 8, 16) and one shape that
 # takes the separate kernels instead (E not a multiple of 4)
