@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
   u32x4 o;
 #pragma unroll
   for (int h = 0; h < 4; ++h)
-    o[h] = (uint32_t)f32_to_bf16(acc[2 * h]) | ((uint32_t)f32_to_bf16(acc[2 * h + 1]) << 16);
+    o[h] = pack2_bf16(acc[2 * h], acc[2 * h + 1]);
   // non-temporal: the output is written once and not read here
   __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(out + (size_t)t * H + col));
 }
@@ -83,10 +83,10 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float *__restrict__
     const f32x4 a = *reinterpret_cast<const f32x4 *>(acc + i);
     const f32x4 b = *reinterpret_cast<const f32x4 *>(acc + i + 4);
     u32x4 o;
-    o[0] = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
-    o[1] = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
-    o[2] = (uint32_t)f32_to_bf16(b[0]) | ((uint32_t)f32_to_bf16(b[1]) << 16);
-    o[3] = (uint32_t)f32_to_bf16(b[2]) | ((uint32_t)f32_to_bf16(b[3]) << 16);
+    o[0] = pack2_bf16(a[0], a[1]);
+    o[1] = pack2_bf16(a[2], a[3]);
+    o[2] = pack2_bf16(b[0], b[1]);
+    o[3] = pack2_bf16(b[2], b[3]);
     *reinterpret_cast<u32x4 *>(out + i) = o;
   } else {
     for (long j = i; j < n; ++j) out[j] = f32_to_bf16(acc[j]);

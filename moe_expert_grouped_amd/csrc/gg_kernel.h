@@ -218,22 +218,28 @@ __device__ __forceinline__ void task_coords(int task, int GR, int ncol, int nrt,
 // epilogues run the matrix instructions with the operands swapped (weights
 // as the first operand), so each 32 x 32 accumulator tile is the transpose:
 // register 4 q + e of lane l holds row l % 32, column 8 q + 4 (l / 32) + e.
-// A lane thus owns 4 consecutive columns of one row and stores them as one
-// 8-byte piece straight from its registers (lanes l and l + 32 together
-// write 16 contiguous bytes of the row), with no LDS staging.  Rows whose
-// entry in `skip` (the task's pair table, if any) is negative are padding and
-// are not written.
+// Stored straight from registers, each store instruction would write 16
+// bytes to each of 32 rows (32 separate pieces), which the memory pipeline
+// issues at about a tenth of its byte rate.  So each 32-row tile goes
+// through `stg` (this wavefront's 32 x WC staging rows in LDS, 16-byte chunks
+// XOR-swizzled by row): lanes write their converted 8-byte pieces, then read
+// back whole rows, CPR lanes per row, and store 16 contiguous bytes each --
+// a store instruction covers 64 / CPR rows of WC columns.  Rows whose entry
+// in `skip` (the task's pair table, if any) is negative are padding and are
+// not written.
 template <int NB, bool FP16, int MI, int NI>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint16_t *Dt, int N,
                                            const MOE_LDS int32_t *skip, int lane, int row0,
-                                           int col0) {
+                                           int col0, MOE_LDS unsigned char *stg) {
+  constexpr int WC = NI * 32;  // columns of this wavefront
+  constexpr int RB = WC * 2;   // bytes per staged row
+  constexpr int CPR = RB / 16; // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR; // rows per store instruction
+  static_assert(CPR >= 4 && (CPR & (CPR - 1)) == 0 && 64 % CPR == 0, "staging rows");
+  const int r = lane & 31;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
-    const int trow = row0 + i * 32 + (lane & 31); // row inside the task
-    const bool keep = !skip || skip[trow] >= 0;
-    // byte offset inside the task's tile (< 2^32): the address is the
-    // wave-uniform tile base plus one 32-bit register
-    const uint32_t rowoff = (uint32_t)((trow * N + col0 + 4 * (lane >> 5)) * 2);
+    // this lane's row r: 8-byte piece (j, q) is granule 8 j + 2 q + l / 32
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
 #pragma unroll
@@ -241,25 +247,39 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint
         uint32_t pk[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          uint16_t o[2];
+          float o[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             float v = acc_read(acc[0][i][j][4 * q + 2 * h + e]);
             if constexpr (NB == 2) {
+              // SiLU(v) * u with the hardware reciprocal (about 1 ulp, far
+              // below the bf16 rounding that follows) instead of a correctly
+              // rounded division, which costs ~10 instructions per value
               const float u = acc_read(acc[1][i][j][4 * q + 2 * h + e]);
-              v = v / (1.0f + __expf(-v)) * u;
+              v = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;
             }
-            o[e] = FP16 ? f32_to_f16(v) : f32_to_bf16(v);
+            o[e] = v;
           }
-          pk[h] = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+          // one packed round-to-nearest-even conversion per two values
+          pk[h] = FP16 ? pack2_f16(o[0], o[1]) : pack2_bf16(o[0], o[1]);
         }
-        if (keep)
-          *reinterpret_cast<uint2 *>(reinterpret_cast<unsigned char *>(Dt) + rowoff +
-                                     (j * 32 + 8 * q) * 2) = uint2{pk[0], pk[1]};
+        const int chunk = (4 * j + q) ^ (r & (CPR - 1));
+        *(MOE_LDS u32x2 *)(stg + r * RB + chunk * 16 + (lane >> 5) * 8) = u32x2{pk[0], pk[1]};
       }
       // one 32 x 32 tile at a time: unrolled freely, the scheduler would
       // convert every tile at once and hold ~100 registers of temporaries
       __builtin_amdgcn_sched_barrier(0);
+    }
+    // whole rows back out: lane l stores chunk l % CPR of row l / CPR (+ RPI per step)
+#pragma unroll
+    for (int rr = 0; rr < 32 / RPI; ++rr) {
+      const int row = rr * RPI + lane / CPR;
+      const int ch = lane % CPR;
+      const u32x4 v = *(const MOE_LDS u32x4 *)(stg + row * RB + ((ch ^ (row & (CPR - 1))) * 16));
+      const int trow = row0 + i * 32 + row; // row inside the task
+      if (!skip || skip[trow] >= 0)
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(Dt) +
+                                   (uint32_t)((trow * N + col0 + ch * 8) * 2)) = v;
     }
   }
 }
@@ -760,10 +780,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
         scatter_tile<4, NI>(acc, args.Dacc, N, pair_table(s), (const MOE_LDS float *)wtab[s],
                             args.topk, lane, wm * 128, n0 + wn * WC);
       } else {
+        // staging: the stages of the slice just consumed, which every
+        // wavefront finished reading at its barrier and which the next DMA
+        // issue (in the next slice) overwrites -- wavefronts 0, 1 in the A
+        // stage, 2, 3 in the B stage, 32 rows x WC columns each
+        constexpr int SW = 32 * WC * 2;
+        static_assert(2 * SW <= A_BYTES && 2 * SW <= BS_BYTES, "staging space");
+        MOE_LDS unsigned char *stg =
+            wave < 2 ? (MOE_LDS unsigned char *)aring + ((c - 1) % NA) * A_BYTES + wave * SW
+                     : (MOE_LDS unsigned char *)bring + ((c - 1) % NBR) * BS_BYTES +
+                           (wave - 2) * SW;
         store_tile<NB, FP16, 4, NI>(acc, args.D + (size_t)b * kBM * N + n0, N,
-                                    has_tab ? pair_table(s) : nullptr, lane, wm * 128, wn * WC);
+                                    has_tab ? pair_table(s) : nullptr, lane, wm * 128, wn * WC,
+                                    stg);
       }
     }
+    // every wavefront's staging is read back before any wavefront issues the
+    // next slice's DMA into those stages
+    if constexpr (!SCAT) block_barrier();
     clear_acc();
   }
   // drain any DMA still in flight before the workgroup retires its LDS
