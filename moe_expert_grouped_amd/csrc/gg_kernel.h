@@ -222,7 +222,8 @@ __device__ __forceinline__ void task_coords(int task, int GR, int ncol, int nrt,
 // bytes to each of 32 rows (32 separate pieces), which the memory pipeline
 // issues at about a tenth of its byte rate.  So each 32-row tile goes
 // through `stg` (this wavefront's 32 x WC staging rows in LDS, 16-byte chunks
-// XOR-swizzled by row): lanes write their converted 8-byte pieces, then read
+// XOR-swizzled by row, their 8-byte halves swapped in every other group of 8
+// rows, so neither the writes nor the reads conflict on banks): lanes write their converted 8-byte pieces, then read
 // back whole rows, CPR lanes per row, and store 16 contiguous bytes each --
 // a store instruction covers 64 / CPR rows of WC columns.  Rows whose entry
 // in `skip` (the task's pair table, if any) is negative are padding and are
@@ -263,8 +264,11 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint
           // one packed round-to-nearest-even conversion per two values
           pk[h] = FP16 ? pack2_f16(o[0], o[1]) : pack2_bf16(o[0], o[1]);
         }
+        // chunk XOR row, and the two 8-byte halves swapped in rows with bit
+        // 3 set: the 16 lanes of a quarter-wavefront hit distinct banks
         const int chunk = (4 * j + q) ^ (r & (CPR - 1));
-        *(MOE_LDS u32x2 *)(stg + r * RB + chunk * 16 + (lane >> 5) * 8) = u32x2{pk[0], pk[1]};
+        const int half = (lane >> 5) ^ ((r >> 3) & 1);
+        *(MOE_LDS u32x2 *)(stg + r * RB + chunk * 16 + half * 8) = u32x2{pk[0], pk[1]};
       }
       // one 32 x 32 tile at a time: unrolled freely, the scheduler would
       // convert every tile at once and hold ~100 registers of temporaries
@@ -275,7 +279,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint
     for (int rr = 0; rr < 32 / RPI; ++rr) {
       const int row = rr * RPI + lane / CPR;
       const int ch = lane % CPR;
-      const u32x4 v = *(const MOE_LDS u32x4 *)(stg + row * RB + ((ch ^ (row & (CPR - 1))) * 16));
+      u32x4 v = *(const MOE_LDS u32x4 *)(stg + row * RB + ((ch ^ (row & (CPR - 1))) * 16));
+      if ((row >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]}; // halves back in column order
       const int trow = row0 + i * 32 + row; // row inside the task
       if (!skip || skip[trow] >= 0)
         *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(Dt) +
