@@ -73,8 +73,6 @@ template <int N, class F> __device__ __forceinline__ void static_for(F &&f) {
 
 constexpr int kBM = 128;     // rows per block: alignment unit and plan granule
 constexpr int kTM = 256;     // rows per task: one or two blocks of one group
-constexpr int kWaves = 4;    // wavefronts per workgroup, one per SIMD
-constexpr int kThreads = 64 * kWaves;
 // Ring slots of the per-task tables.  The tables of task i are fetched when
 // the B stream starts task i-1 and read until task i's epilogue; those of
 // task i+4 (same slot) are fetched when the B stream -- NBR-1 slices ahead
@@ -328,15 +326,19 @@ __device__ __forceinline__ void scatter_tile(const f32x16 (&acc)[1][MI][NI], flo
 // ring freed at the previous barrier), so the B stream runs NBR - NA
 // slices further ahead and may already be on a later task than the A
 // stream; each stream keeps its own task cursor.
-template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR, bool BNT>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) {
+// WV: wavefronts per workgroup, 4 (one per SIMD, 256 accumulators each) or 8
+// (two per SIMD, 128 accumulators each: while one issues its fragment reads
+// and DMA, the other feeds the matrix pipe).  Each covers 128 rows and
+// BN / (WV / 2) columns of the task.
+template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR, bool BNT, int WV>
+__global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
   constexpr int NB = EPI == kEpiSiluMul ? 2 : 1; // B matrices
   constexpr int ARP = BK * 2;                    // bytes per A row (and [N][K] B row) per slice
   constexpr int A_BYTES = kTM * ARP;             // one A stage
   constexpr int B_BYTES = BK * BN * 2;           // one B matrix of one B stage
   constexpr int BS_BYTES = NB * B_BYTES;         // one B stage
-  constexpr int A_INSTR = A_BYTES / 1024 / kWaves;    // DMA instructions per wavefront per A slice
-  constexpr int B_INSTR = B_BYTES / 1024 / kWaves;    // per B matrix per B slice
+  constexpr int A_INSTR = A_BYTES / 1024 / WV;    // DMA instructions per wavefront per A slice
+  constexpr int B_INSTR = B_BYTES / 1024 / WV;    // per B matrix per B slice
   constexpr int A_LOADS = A_INSTR;
   constexpr int B_LOADS = NB * B_INSTR;
   constexpr int LA = NA - 1;                          // A issue lead (slices)
@@ -352,11 +354,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   static_assert(LA >= 2, "the A stream leads by at least two slices");
   constexpr int A_RPI = 1024 / ARP;                   // A rows per DMA instruction
   constexpr int A_GPR = ARP / 16;                     // 16-byte granules per A row
-  constexpr int WC = BN / 2;                          // columns per wavefront per matrix
+  constexpr int WCOL = WV / 2;                        // wavefronts across the columns
+  constexpr int WC = BN / WCOL;                       // columns per wavefront per matrix
+  constexpr int TR = kTM / WV;                        // table rows fetched per wavefront
   constexpr int NI = WC / 32;
   constexpr bool SCAT = EPI == kEpiScatter;
   static_assert(BK == 32, "two 16-deep k steps per slice");
-  static_assert(B_INSTR >= 1 && A_INSTR * A_RPI * kWaves == kTM, "DMA split");
+  static_assert(WV == 4 || WV == 8, "wavefronts per workgroup");
+  static_assert(NI >= 1 && B_INSTR >= 1 && A_INSTR * A_RPI * WV == kTM, "DMA split");
   static_assert(NA >= 2 && NBR >= NA, "ring depths");
 
   __shared__ __attribute__((aligned(1024))) unsigned char aring[NA * A_BYTES];
@@ -367,13 +372,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   __shared__ __attribute__((aligned(16))) int32_t tab[kTabSlots][kTM];
   __shared__ __attribute__((aligned(16))) int32_t etab[SCAT ? kTabSlots : 1][SCAT ? kTM : 1];
   __shared__ __attribute__((aligned(16))) float wtab[SCAT ? kTabSlots : 1][SCAT ? kTM : 1];
-  __shared__ __attribute__((aligned(16))) int32_t ptab[kWaves][kPlanSlots][2]; // plan entries
+  __shared__ __attribute__((aligned(16))) int32_t ptab[WV][kPlanSlots][2]; // plan entries
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / WCOL;
+  const int wn = wave % WCOL;
   const int N = args.N, K = args.K;
   const int KT = K / BK;
   const bool has_a = args.a_src_row != nullptr;
@@ -414,19 +419,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
     b = e & (kPlanTwo - 1);
     nb = (e & kPlanTwo) ? 2 : 1;
   };
-  // DMA this wavefront's 64 rows of the pair tables of item i (its plan
+  // DMA this wavefront's TR rows of the pair tables of item i (its plan
   // entry has landed).  Rows of the missing second block of a one-block
   // task repeat the first block's rows.
   auto fetch_tables = [&](int i) {
     if (!has_tab) return;
     int b, nb, g;
     plan_of(i, b, nb, g);
-    const int r = 64 * wave + lane;
+    const int r = TR * wave + (lane % TR);
     const size_t src = (size_t)b * kBM + (nb == 2 ? r : (r & (kBM - 1)));
     const int s = i % kTabSlots;
-    dma4(tab_src + src, lds_addr_of(&tab[s][64 * wave]));
+    if (lane < TR) dma4(tab_src + src, lds_addr_of(&tab[s][TR * wave]));
     if constexpr (SCAT)
-      if (own_e) dma4(args.epi_row_pair + src, lds_addr_of(&etab[s][64 * wave]));
+      if (own_e && lane < TR) dma4(args.epi_row_pair + src, lds_addr_of(&etab[s][TR * wave]));
   };
   // the epilogue's pair per row
   auto pair_table = [&](int s) -> const MOE_LDS int32_t * {
@@ -434,13 +439,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
       if (own_e) return (const MOE_LDS int32_t *)etab[s];
     return (const MOE_LDS int32_t *)tab[s];
   };
-  // DMA the routing weights of this wavefront's 64 rows of item i (its pair
+  // DMA the routing weights of this wavefront's TR rows of item i (its pair
   // table has landed).
   auto fetch_weights = [&](int i) {
     if constexpr (SCAT) {
       const int s = i % kTabSlots;
-      const int p = pair_table(s)[64 * wave + lane];
-      dma4(args.pair_w + (p < 0 ? 0 : p), lds_addr_of(&wtab[s][64 * wave]));
+      const int p = pair_table(s)[TR * wave + (lane % TR)];
+      if (lane < TR) dma4(args.pair_w + (p < 0 ? 0 : p), lds_addr_of(&wtab[s][TR * wave]));
     }
   };
   // The column tasks of one row task run side by side on neighbouring CUs
@@ -787,14 +792,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
       } else {
         // staging: the stages of the slice just consumed, which every
         // wavefront finished reading at its barrier and which the next DMA
-        // issue (in the next slice) overwrites -- wavefronts 0, 1 in the A
-        // stage, 2, 3 in the B stage, 32 rows x WC columns each
+        // issue (in the next slice) overwrites -- the first half of the
+        // wavefronts in the A stage, the second in the B stage, 32 rows x WC
+        // columns each
         constexpr int SW = 32 * WC * 2;
-        static_assert(2 * SW <= A_BYTES && 2 * SW <= BS_BYTES, "staging space");
+        static_assert((WV / 2) * SW <= A_BYTES && (WV / 2) * SW <= BS_BYTES, "staging space");
         MOE_LDS unsigned char *stg =
-            wave < 2 ? (MOE_LDS unsigned char *)aring + ((c - 1) % NA) * A_BYTES + wave * SW
-                     : (MOE_LDS unsigned char *)bring + ((c - 1) % NBR) * BS_BYTES +
-                           (wave - 2) * SW;
+            wave < WV / 2
+                ? (MOE_LDS unsigned char *)aring + ((c - 1) % NA) * A_BYTES + wave * SW
+                : (MOE_LDS unsigned char *)bring + ((c - 1) % NBR) * BS_BYTES +
+                      (wave - WV / 2) * SW;
         store_tile<NB, FP16, 4, NI>(acc, args.D + (size_t)b * kBM * N + n0, N,
                                     has_tab ? pair_table(s) : nullptr, lane, wm * 128, wn * WC,
                                     stg);
@@ -809,23 +816,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs args) 
   wait_vmcnt<0>();
 }
 
-template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR, bool BNT>
+template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR, bool BNT, int WV = 4>
 static hipError_t launch_one(const GGArgs &a, int grid, hipStream_t stream) {
-  grouped_gemm_kernel<BN, BK, EPI, KN, FP16, NA, NBR, BNT><<<grid, kThreads, 0, stream>>>(a);
+  grouped_gemm_kernel<BN, BK, EPI, KN, FP16, NA, NBR, BNT, WV><<<grid, 64 * WV, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 // Tile configuration of one launch: BN (columns per matrix), BK (k per
-// slice), A and B ring depths, row tasks per super-block of the task order.
+// slice), A and B ring depths, row tasks per super-block of the task order,
+// wavefronts per workgroup.
 struct TileCfg {
   int bn, bk, na, nb, group;
+  int waves = 4;
 };
 
 // The instantiated (BN, BK, NA, NBR) per B-matrix count; the rings stay
 // within 144 KiB so the tables and staging tiles fit in the 160 KiB of LDS.
 // Every BN has the 4/4 rings, safe for any K (2 KT >= 3).
-inline bool tile_supported(int nbm, int bn, int bk, int na, int nb) {
+inline bool tile_supported(int nbm, int bn, int bk, int na, int nb, int waves = 4) {
   if (bk != 32) return false;
+  // eight wavefronts: the full-size rings of the default tiles, no scatter
+  if (waves == 8) return na == 3 && nb == 6 && ((nbm == 1 && bn == 256) || (nbm == 2 && bn == 128));
+  if (waves != 4) return false;
   if (na == 4 && nb == 4) return bn == 64 || bn == 128 || (bn == 256 && nbm == 1);
   if (nbm == 2) return (bn == 128 && na == 3 && nb == 6) || (bn == 64 && na == 3 && nb == 10);
   return (bn == 256 && na == 3 && nb == 6) || (bn == 128 && na == 3 && nb == 10) ||
@@ -838,15 +850,21 @@ inline bool tile_supported(int nbm, int bn, int bk, int na, int nb) {
 template <int EPI, bool KN, bool FP16, bool BNT>
 hipError_t launch_bn(const GGArgs &a, const TileCfg &c, int grid, hipStream_t s) {
 #define MOE_GG_CASE(BNV, NAV, NBV)                                                            \
-  if (c.bn == BNV && c.bk == 32 && c.na == NAV && c.nb == NBV)                                \
+  if (c.waves == 4 && c.bn == BNV && c.bk == 32 && c.na == NAV && c.nb == NBV)                \
     return launch_one<BNV, 32, EPI, KN, FP16, NAV, NBV, BNT>(a, grid, s);
+#define MOE_GG_CASE8(BNV, NAV, NBV)                                                           \
+  if (c.waves == 8 && c.bn == BNV && c.bk == 32 && c.na == NAV && c.nb == NBV)                \
+    return launch_one<BNV, 32, EPI, KN, FP16, NAV, NBV, BNT, 8>(a, grid, s);
   if constexpr (EPI == kEpiSiluMul) {
     MOE_GG_CASE(128, 3, 6) MOE_GG_CASE(128, 4, 4) MOE_GG_CASE(64, 3, 10) MOE_GG_CASE(64, 4, 4)
+    MOE_GG_CASE8(128, 3, 6)
   } else {
     MOE_GG_CASE(256, 3, 6) MOE_GG_CASE(256, 4, 4) MOE_GG_CASE(128, 3, 10) MOE_GG_CASE(128, 4, 4)
     MOE_GG_CASE(64, 4, 8) MOE_GG_CASE(64, 4, 4)
+    if constexpr (EPI == kEpiStore) { MOE_GG_CASE8(256, 3, 6) }
   }
 #undef MOE_GG_CASE
+#undef MOE_GG_CASE8
   return hipErrorInvalidValue;
 }
 

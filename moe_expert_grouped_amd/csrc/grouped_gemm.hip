@@ -29,34 +29,44 @@ MOE_GG_EXTERN(kEpiScatter, true, true, true)
 #undef MOE_GG_EXTERN
 
 // Tile configurations: (BN, BK, A ring depth, B ring depth, super-block row
-// tasks).  Defaults: gate/up 128 gate + 128 up columns, down / dense 256
-// columns (128 when N is not a multiple of 256, 64 below that), 32-deep
-// slices, a 3-deep A ring and a 6-deep B ring (weights are most of the
-// bytes in flight).  Each can be overridden for tuning sweeps with
-// MOE_GG_TILE="<bn>,<bk>,<na>,<nb>[,<group rows>]" (MOE_GG_TILE_GU, if set,
+// tasks, wavefronts).  Defaults: gate/up 128 gate + 128 up columns, down /
+// dense 256 columns (128 when N is not a multiple of 256, 64 below that),
+// 32-deep slices, a 3-deep A ring and a 6-deep B ring (weights are most of
+// the bytes in flight); the 128 / 256-column tiles with eight wavefronts
+// (two per SIMD: one's matrix instructions run while the other issues its
+// fragment reads and DMA), except for the weighted scatter.  Each can be overridden for tuning sweeps with
+// MOE_GG_TILE="<bn>,<bk>,<na>,<nb>[,<group rows>[,<wavefronts>]]" (MOE_GG_TILE_GU, if set,
 // for the SiLU*up epilogue only).  A configuration is used
 // only if it is instantiated, divides N, and its B ring keeps the per-task
 // tables safe for this K (2 * K / BK >= nb - 1); otherwise the 4-deep rings,
 // instantiated for every BN.
 static bool tile_usable(const TileCfg &c, int epilogue, int N, int K) {
   return c.group >= 1 && c.bn > 0 && c.bk > 0 && N % c.bn == 0 && K % c.bk == 0 &&
+         (c.waves == 4 || epilogue != kEpiScatter) &&
          2 * (K / c.bk) >= c.nb - 1 &&
-         tile_supported(epilogue == kEpiSiluMul ? 2 : 1, c.bn, c.bk, c.na, c.nb);
+         tile_supported(epilogue == kEpiSiluMul ? 2 : 1, c.bn, c.bk, c.na, c.nb, c.waves);
 }
 
 static TileCfg tile_config(int epilogue, int N, int K) {
   TileCfg c;
+  // the full-size tiles run eight wavefronts (two per SIMD) except the
+  // weighted scatter
+  const int w = epilogue == kEpiScatter ? 4 : 8;
   if (epilogue == kEpiSiluMul)
-    c = N % 128 == 0 ? TileCfg{128, 32, 3, 6, 1} : TileCfg{64, 32, 3, 10, 1};
+    c = N % 128 == 0 ? TileCfg{128, 32, 3, 6, 1, w} : TileCfg{64, 32, 3, 10, 1};
   else
-    c = N % 256 == 0 ? TileCfg{256, 32, 3, 6, 1}
+    c = N % 256 == 0 ? TileCfg{256, 32, 3, 6, 1, w}
                      : (N % 128 == 0 ? TileCfg{128, 32, 3, 10, 1} : TileCfg{64, 32, 4, 8, 1});
-  if (!tile_usable(c, epilogue, N, K)) c.na = c.nb = 4; // short K: shallower rings
+  if (!tile_usable(c, epilogue, N, K)) { // short K: shallower rings, four wavefronts
+    c.na = c.nb = 4;
+    c.waves = 4;
+  }
   const char *env = epilogue == kEpiSiluMul ? getenv("MOE_GG_TILE_GU") : nullptr;
   if (!env) env = getenv("MOE_GG_TILE");
   if (env) {
     TileCfg e{0, 0, 0, 0, 1};
-    const int n = sscanf(env, "%d,%d,%d,%d,%d", &e.bn, &e.bk, &e.na, &e.nb, &e.group);
+    const int n =
+        sscanf(env, "%d,%d,%d,%d,%d,%d", &e.bn, &e.bk, &e.na, &e.nb, &e.group, &e.waves);
     if (n >= 4 && tile_usable(e, epilogue, N, K)) c = e;
   }
   return c;

@@ -135,9 +135,9 @@ def test_dense_fp16_degenerate_case_sampled():
 
 # bn, bk, A ring depth, B ring depth[, super-block row tasks]
 TILES = [("store", "256,32,3,6"), ("store", "256,32,4,4,2"), ("store", "128,32,3,10"),
-         ("store", "64,32,4,8,3"), ("store", "256,32,3,6,4"),
+         ("store", "64,32,4,8,3"), ("store", "256,32,3,6,4"), ("store", "256,32,3,6,1,8"),
          ("silu_mul", "128,32,3,6"), ("silu_mul", "128,32,4,4,2"), ("silu_mul", "64,32,3,10"),
-         ("silu_mul", "128,32,3,6,3")]
+         ("silu_mul", "128,32,3,6,3"), ("silu_mul", "128,32,3,6,1,8")]
 
 
 @pytest.mark.parametrize("epi,tile", TILES, ids=["%s-%s" % t for t in TILES])
@@ -165,6 +165,30 @@ def test_tile_configurations_integer_exact(epi, tile, monkeypatch):
         else:
             assert_close(got[:m_rows], ref, "tile " + tile, max_frac=8e-3, rel_fro=4e-3)
         assert np.all(np.isnan(got[m_rows:]))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_eight_wavefronts_integer_exact(dtype, layout, monkeypatch):
+    # the eight-wavefront workgroups (two per SIMD, a 128-row x 64-column
+    # share of a 256 x 256 task each) on both B layouts, gathered rows, a
+    # ragged group table and a block without a group
+    monkeypatch.setenv("MOE_GG_TILE", "256,32,3,6,1,8")
+    G, N, K = 3, 768, 384
+    cap = 9 * 128
+    bg = np.array([0, 0, 0, 2, -1, 1, 1, 2, 2], np.int32)
+    T = 700
+    A = syn.ternary_bits((T, K), 31, dtype)
+    B = syn.ternary_bits((G, K, N) if layout == "kn" else (G, N, K), 32, dtype)
+    src = np.random.default_rng(3).integers(0, T * 2, size=cap).astype(np.int32)
+    say("gemm eight wavefronts", dtype, layout)
+    D = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=cap, dtype=dtype, layout=layout, src=src, div=2)
+    ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, is_fp16=dtype == "fp16", b_layout=layout,
+                              a_src_row=src, a_src_div=2)
+    got = to_f64(D)
+    real = np.repeat(bg, 128) >= 0
+    assert np.array_equal(got[real], ref[real])
+    assert np.all(np.isnan(got[~real]))
 
 
 # block-group patterns for the pairing of blocks into 256-row tasks: runs of
