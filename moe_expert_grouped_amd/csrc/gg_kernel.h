@@ -234,6 +234,9 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint
   constexpr int RB = WC * 2;   // bytes per staged row
   constexpr int CPR = RB / 16; // 16-byte chunks per row
   constexpr int RPI = 64 / CPR; // rows per store instruction
+  // the chunk swizzle takes row bits from SH up: with 64-byte rows two rows
+  // share a 128-byte line of banks, and the row's low bit already tells them apart
+  constexpr int SH = CPR == 4 ? 1 : 0;
   static_assert(CPR >= 4 && (CPR & (CPR - 1)) == 0 && 64 % CPR == 0, "staging rows");
   const int r = lane & 31;
 #pragma unroll
@@ -264,7 +267,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint
         }
         // chunk XOR row, and the two 8-byte halves swapped in rows with bit
         // 3 set: the 16 lanes of a quarter-wavefront hit distinct banks
-        const int chunk = (4 * j + q) ^ (r & (CPR - 1));
+        const int chunk = (4 * j + q) ^ ((r >> SH) & (CPR - 1));
         const int half = (lane >> 5) ^ ((r >> 3) & 1);
         *(MOE_LDS u32x2 *)(stg + r * RB + chunk * 16 + half * 8) = u32x2{pk[0], pk[1]};
       }
@@ -277,7 +280,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint
     for (int rr = 0; rr < 32 / RPI; ++rr) {
       const int row = rr * RPI + lane / CPR;
       const int ch = lane % CPR;
-      u32x4 v = *(const MOE_LDS u32x4 *)(stg + row * RB + ((ch ^ (row & (CPR - 1))) * 16));
+      u32x4 v = *(const MOE_LDS u32x4 *)(stg + row * RB + ((ch ^ ((row >> SH) & (CPR - 1))) * 16));
       if ((row >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]}; // halves back in column order
       const int trow = row0 + i * 32 + row; // row inside the task
       if (!skip || skip[trow] >= 0)
