@@ -358,11 +358,17 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 def gemm_source_sha256():
     """SHA-256 of the grouped GEMM sources (kernel header, instantiation
-    unit, dispatcher), concatenated in that order."""
+    unit, dispatcher), concatenated in that order, with // comments and
+    blank lines dropped and runs of whitespace folded: comment edits do not
+    change the code the counters were taken on."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in GEMM_SRCS:
-        h.update(open(f, "rb").read())
+        for line in open(f, encoding="utf-8"):
+            code = re.sub(r"\s+", " ", re.sub(r"//.*", "", line)).strip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

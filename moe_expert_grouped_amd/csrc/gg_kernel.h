@@ -1,5 +1,6 @@
 // gg_kernel.h -- the grouped GEMM of the MoE layer on CDNA4 (gfx950): kernel
-// templates, instantiated per (epilogue, B layout, dtype) by gg_inst.hip.
+// templates, instantiated per (epilogue, B layout, dtype, B cache policy) by
+// gg_inst.hip.
 //
 // What it computes ("Comm-compute fusion (3)", section 4, the grouped GEMM
 // template): output rows come in 128-row blocks; block b belongs to group
@@ -21,10 +22,12 @@
 //     once for up to 256 rows, halving weight traffic per row against
 //     128-row tasks.  A plan kernel pairs consecutive blocks of each group
 //     (gg_plan_kernel) so the task list is dense;
-//   * persistent grid of one 256-thread workgroup (4 wavefronts, one per
-//     SIMD) per CU; the task list is cut into 8 contiguous ranges, one per
+//   * persistent grid of one workgroup per CU, 8 wavefronts (two per SIMD:
+//     one's matrix instructions run while the other issues its fragment
+//     reads and DMA) for the full-size store and SiLU*up tiles, 4 (one per
+//     SIMD) otherwise; the task list is cut into 8 contiguous ranges, one per
 //     XCD (workgroup w runs on XCD w % 8), so the column tasks of one row
-//     task share its A rows in that XCD's L2;
+//     task share its A rows in that XCD's L2, walking k in the same order;
 //   * 32-deep K slices stream through LDS rings with direct global->LDS DMA
 //     (global_load_lds_dwordx4), no registers spent on staging: a shallow
 //     ring for A tiles (mostly L2 hits) and a deeper one for the weight
@@ -45,11 +48,15 @@
 //     tiles stored [K][N] with the gfx950 transpose read ds_read_b64_tr_b16,
 //     which hands each lane 4 consecutive k of one column -- the MFMA B
 //     operand layout;
-//   * v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulators; wavefront (wm, wn)
-//     owns rows [128 wm, 128 wm + 128) and columns [BN/2 wn, BN/2 wn + BN/2)
-//     of each B matrix.  A one-block task loads its 128 rows twice; the
-//     second copy's products are not stored (they hide under the weight
-//     stream in the HBM-bound shapes, and keep one fixed register layout).
+//   * v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulators; with WV
+//     wavefronts, wavefront (wm, wn) owns rows [128 wm, 128 wm + 128) and
+//     columns [WC wn, WC wn + WC) of each B matrix, WC = BN / (WV / 2).  A
+//     one-block task loads its 128 rows twice; the second copy's products
+//     are not stored (they hide under the weight stream in the HBM-bound
+//     shapes, and keep one fixed register layout);
+//   * the store epilogues convert pairs with one packed instruction and go
+//     through LDS (the stages of the slice just consumed) so each store
+//     writes whole row pieces; the weighted scatter adds with fp32 atomics.
 #pragma once
 #include <stdio.h>
 #include <stdlib.h>
