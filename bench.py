@@ -352,13 +352,14 @@ def bench_dense(a):
 
 
 CSRC = os.path.join(ROOT, "moe_expert_grouped_amd", "csrc")
-GEMM_SRCS = [os.path.join(CSRC, f) for f in ("gg_kernel.h", "gg_inst.hip", "grouped_gemm.hip")]
+GEMM_SRCS = [os.path.join(CSRC, f)
+             for f in ("gg_kernel.h", "gg_inst.hip", "grouped_gemm.hip", "common.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def gemm_source_sha256():
     """SHA-256 of the grouped GEMM sources (kernel header, instantiation
-    unit, dispatcher), concatenated in that order, with // comments and
+    unit, dispatcher, shared device helpers), concatenated in that order, with // comments and
     blank lines dropped and runs of whitespace folded: comment edits do not
     change the code the counters were taken on."""
     import hashlib

@@ -38,18 +38,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __uint_as_float(((uint32_t)b) << 16);
-}
-
-// fp32 -> IEEE half, round-to-nearest-even (the hardware conversion).
-__device__ __forceinline__ uint16_t f32_to_f16(float f) {
-  _Float16 h = (_Float16)f;
-  return __builtin_bit_cast(uint16_t, h);
-}
-
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
-
 // Inclusive prefix sum across the 64 lanes of a wavefront, with DPP lane
 // moves (no LDS permutes): shifts right by 1, 2, 4, 8 inside each row of 16
 // lanes (lanes shifted in from outside the row add 0), then row r adds the
