@@ -24,6 +24,50 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// Direct global->LDS DMA.  Issued through inline asm so that the compiler
+// neither tracks these loads nor inserts its own (conservative) waits for
+// them: lane i of the wavefront writes bytes [16 i, 16 i + 16) (or [4 i, 4 i
+// + 4) for the dword form) after the wave-uniform LDS byte address in M0
+// (one wait state between the M0 write and its use).  Completion is awaited
+// explicitly with wait_vmcnt; loads complete in issue order.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+               "s"(lds_addr)
+               : "memory", "m0");
+}
+// The same with a wave-uniform 64-bit base (SGPR pair) and a 32-bit per-lane
+// byte offset: the per-lane state is one register instead of a pointer.
+// NT: the non-temporal (streaming) cache policy, for data read about once.
+template <bool NT>
+__device__ __forceinline__ void dma16s(uint32_t voff, const void *sbase, uint32_t lds_addr) {
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff),
+                 "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+                 "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void *g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g),
+               "s"(lds_addr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
+  return (uint32_t)(uintptr_t)(const MOE_LDS void *)p;
+}
+
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// LDS wait through the builtin, so the compiler's own wait insertion knows
+// the reads issued before it have completed (encoding: vmcnt and expcnt at
+// their maximum, lgkmcnt 0)
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // Two fp32 values -> a packed pair (a in the low half), round-to-nearest-
 // even: one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {

@@ -135,50 +135,6 @@ template <int BN> __device__ __forceinline__ int swz_kn(int k) {
     return 2 * (k & 3);
 }
 
-// Direct global->LDS DMA.  Issued through inline asm so that the compiler
-// neither tracks these loads nor inserts its own (conservative) waits for
-// them: lane i of the wavefront writes bytes [16 i, 16 i + 16) (or [4 i, 4 i
-// + 4) for the dword form) after the wave-uniform LDS byte address in M0
-// (one wait state between the M0 write and its use).  Completion is awaited
-// explicitly with wait_vmcnt; loads complete in issue order.
-__device__ __forceinline__ void dma16(const void *g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
-               "s"(lds_addr)
-               : "memory", "m0");
-}
-// The same with a wave-uniform 64-bit base (SGPR pair) and a 32-bit per-lane
-// byte offset: the per-lane state is one register instead of a pointer.
-// NT: the non-temporal (streaming) cache policy, for data read about once.
-template <bool NT>
-__device__ __forceinline__ void dma16s(uint32_t voff, const void *sbase, uint32_t lds_addr) {
-  if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff),
-                 "s"(sbase), "s"(lds_addr)
-                 : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
-                 "s"(sbase), "s"(lds_addr)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void *g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g),
-               "s"(lds_addr)
-               : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
-  return (uint32_t)(uintptr_t)(const MOE_LDS void *)p;
-}
-
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// LDS wait through the builtin, so the compiler's own wait insertion knows
-// the reads issued before it have completed (encoding: vmcnt and expcnt at
-// their maximum, lgkmcnt 0)
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
 template <bool FP16>
 __device__ __forceinline__ f32x16 mfma32(const i16x4 a0, const i16x4 a1, const i16x4 b0,
                                          const i16x4 b1, f32x16 acc) {

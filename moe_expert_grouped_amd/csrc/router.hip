@@ -8,23 +8,24 @@
 // those of moe_route (topk_softmax in topk.h), taken on the fp32 logits
 // computed here.
 //
-// Design (gfx950): one 4-wavefront workgroup per (32 tokens, hidden slice),
-// each wavefront a quarter of the slice with 32x32x16 bf16 matrix
-// instructions.  A routing of few tokens cuts H into up to 16 slices
-// so the launch still covers the chip (a CU streams only a few tens of GB/s
-// of these row pieces, so the bandwidth must come from all of them).  The A
-// operand (32 token rows x 16 hidden) and the B operand (16 hidden x 32
-// experts, i.e. 32 rows of W) are both 16 contiguous bytes per lane, so
-// both are loaded straight from global memory into registers, a batch of k
-// steps ahead of the matrix instructions that use them; the k order within
-// groups of four steps is permuted so that each lane reads 64 contiguous
-// bytes of its row per group.  The four wavefronts' [32 x E] tiles meet in
-// LDS and are summed in wavefront order; with one slice each wavefront then
-// routes 8 of the tokens, with several the slices' partial logits go to a
-// workspace and a second launch adds them in slice order and routes (one
-// fixed rounding order either way).  (128-token workgroups, which read half
-// the W bytes per token, need 16 slices at T = 2048, and their partials
-// then cost as much as x: 20.9 against 14.5 us.)
+// Design (gfx950): one 4-wavefront workgroup per (32 tokens, hidden slice).
+// A routing of few tokens cuts H into up to 16 slices so the launch still
+// covers the chip.  The slice streams through a 4-stage LDS ring in chunks of
+// 64 hidden values -- 128 bytes of every x row and W row, one whole cache
+// line -- by direct global->LDS DMA, 8 rows per instruction: loading the
+// 32x32x16 operands straight into registers touches 32 rows per instruction
+// and is bound by the request rate, not by bytes.  In each chunk wavefront w
+// takes k step w (16 of the 64 values) for every 32-expert column tile:
+// its A fragment (32 token rows x 16) and B fragments (32 W rows x 16) are
+// one 16-byte LDS read per lane each, the 16-byte granules of a row XOR-
+// swizzled by row / 2 so that 16 consecutive rows hit 16 distinct bank
+// groups.  The four wavefronts' [32 x E] tiles meet in LDS (in the ring,
+// once the last chunk is consumed) and are summed in wavefront order; with
+// one slice each wavefront then routes 8 of the tokens, with several the
+// slices' partial logits go to a workspace and a second launch adds them in
+// slice order and routes (one fixed rounding order either way).  (128-token
+// workgroups, which read half the W bytes per token, need 16 slices at
+// T = 2048, and their partials then cost as much as x.)
 // Traffic: 2 T H (x, once) + 2 E H per workgroup (W, from L2) + 8 S T E
 // (partials, S > 1) + 4 T E (logits, if written) + 8 T k bytes.
 #include "topk.h"
@@ -50,10 +51,15 @@ size_t router_workspace_bytes(int T, int H, int E) {
   return s > 1 ? (size_t)s * T * E * sizeof(float) : 0;
 }
 
-// Workgroup (b, s): tokens 32 b .. 32 b + 31, hidden slice s (of S), a
-// quarter of the slice per wavefront; with S == 1 it also routes its
-// tokens, else it writes its [32 x E] partial logits to part_out[s] for
-// router_select_kernel.
+constexpr int kRouterChunk = 64; // hidden values per ring stage (128 bytes of a row)
+constexpr int kRouterStages = 4;
+
+// LDS position of 16-byte granule g of ring row r (8 granules per row)
+__device__ __forceinline__ int router_swz(int g, int r) { return g ^ ((r >> 1) & 7); }
+
+// Workgroup (b, s): tokens 32 b .. 32 b + 31, hidden slice s (of S); with
+// S == 1 it also routes its tokens, else it writes its [32 x E] partial
+// logits to part_out[s] for router_select_kernel.
 // NT 32-expert column tiles: E <= 32 NT
 template <int NT>
 __global__ __launch_bounds__(256) void router_kernel(const uint16_t *__restrict__ x,
@@ -62,86 +68,83 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t *__restrict_
                                                      float *__restrict__ logits,
                                                      int32_t *__restrict__ topk_idx,
                                                      float *__restrict__ topk_w) {
-  constexpr int EP = 32 * NT;     // expert columns computed
-  constexpr int LD = EP + 1;      // LDS row stride in floats
-  constexpr int U = NT <= 2 ? 8 : 4; // k steps per load batch
-  __shared__ float part[kRouterWaves][kRouterTok][LD];
+  constexpr int EP = 32 * NT;                // expert columns computed
+  constexpr int LD = EP + 1;                 // LDS row stride of the partial tiles, in floats
+  constexpr int XB = kRouterTok * 128;       // x bytes of a stage: 32 rows x 128 bytes
+  constexpr int SB = XB + EP * 128;          // stage bytes: then EP rows of W
+  constexpr int NI = 1 + NT;                 // DMA instructions per wavefront per chunk
+  static_assert(kRouterTok == 8 * kRouterWaves, "one x instruction per wavefront");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kRouterStages * SB];
+  // after the last chunk the ring holds the wavefronts' partial tiles
+  static_assert(sizeof(float) * kRouterWaves * kRouterTok * LD <= kRouterStages * SB, "fits");
+  float(*part)[kRouterTok][LD] = reinterpret_cast<float(*)[kRouterTok][LD]>(ring);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * kRouterTok;
-  const int hs = H / S;             // this workgroup's hidden slice
-  const int hq = hs / kRouterWaves; // this wavefront's part of it, a multiple of 16
-  const int hoff = blockIdx.y * hs + wave * hq;
-  const int q = lane >> 5;          // which 8 of a k step's 16 hidden values this lane holds
+  const int hs = H / S; // this workgroup's hidden slice, a multiple of 64
+  const int h0 = blockIdx.y * hs;
+  const int nchunk = hs / kRouterChunk;
 
-  // A: lane l holds 8 hidden values of token row t0 + l % 32, B the same 8 of
-  // W row 32 n + l % 32 (the operand layouts of the 32x32x16 instruction).
-  // Which 8: the k steps go in groups of four over 64 hidden values, and
-  // lane half q takes the 32 values [32 q, 32 q + 32) of the group, 8 per
-  // step -- each lane reads 64 contiguous bytes of its row over a group (the
-  // sum over k is the same; its order is fixed).  Steps past the last whole
-  // group take 16 consecutive values, 8 per lane half.
-  const int steps = hq / 16;
-  const int steps4 = steps & ~3;
-  auto vec = [&](int st) { return st < steps4 ? 8 * (st >> 2) + 4 * q + (st & 3) : 2 * st + q; };
-  // rows past T and experts past E read row 0 instead (loads stay unconditional,
-  // so the compiler can keep the next batch in flight): their logits are
-  // never written or selected
-  const int ti = t0 + (lane & 31);
-  const bool tv = ti < T;
-  const bf16x8 *xa = reinterpret_cast<const bf16x8 *>(x + (size_t)(tv ? ti : 0) * H + hoff);
-  const bf16x8 *wb[NT];
-  bool ev[NT];
+  // DMA instruction j of a chunk fills ring rows 8 j .. 8 j + 7 (x rows for
+  // j < 4, then W rows); wavefront w issues j = w and j = 4 + w + 4 m.  Lane
+  // l writes granule l % 8 of row 8 j + l / 8, so it fetches the row's
+  // granule router_swz(l % 8, row).  Rows past T and experts past E read the
+  // last valid row: their products are never written or selected.
+  const int rr = lane >> 3; // row within the instruction
+  const int xrow = 8 * wave + rr;
+  const int tok = min(t0 + xrow, T - 1);
+  const uint16_t *xs = x + (size_t)tok * H + h0 + 8 * router_swz(lane & 7, xrow);
+  const uint16_t *wsrc[NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int e = 32 * n + (lane & 31);
-    ev[n] = e < E;
-    wb[n] = reinterpret_cast<const bf16x8 *>(w + (size_t)(ev[n] ? e : 0) * H + hoff);
+  for (int m = 0; m < NT; ++m) {
+    const int wr = 8 * (wave + 4 * m) + rr;
+    wsrc[m] = w + (size_t)min(wr, E - 1) * H + h0 + 8 * router_swz(lane & 7, wr);
   }
+  const uint32_t ring_lds = lds_addr_of(ring);
+  auto issue = [&](int c) {
+    const uint32_t st = ring_lds + (c % kRouterStages) * SB;
+    dma16(xs + c * kRouterChunk, st + wave * 1024);
+#pragma unroll
+    for (int m = 0; m < NT; ++m) dma16(wsrc[m] + c * kRouterChunk, st + XB + (wave + 4 * m) * 1024);
+  };
+
   f32x16 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x16{};
+  // operand rows of this lane (token row, and W row 32 n + row of tile n)
+  // and the granule of this wavefront's k step: lane half q holds hidden
+  // values 8 q .. 8 q + 7 of the step (the 32x32x16 operand layouts)
+  const int row = lane & 31;
+  const int gpos = router_swz(2 * wave + (lane >> 5), row) * 16;
 
-  // Batches of U k steps alternate between two register sets, so the next
-  // batch's loads are in flight while the matrix instructions use this one.
-  bf16x8 a0[U], b0[U][NT], a1[U], b1[U][NT];
-  auto load = [&](bf16x8(&a)[U], bf16x8(&b)[U][NT], int s0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int v = vec(s0 + u);
-      a[u] = xa[v];
-#pragma unroll
-      for (int n = 0; n < NT; ++n) b[u][n] = wb[n][v];
-    }
-  };
-  auto mma = [&](const bf16x8(&a)[U], const bf16x8(&b)[U][NT]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[u][n], acc[n], 0, 0, 0);
-  };
-  const int nb = steps / U; // whole batches
-  if (nb > 0) load(a0, b0, 0);
-  int bi = 0;
-  for (; bi + 1 < nb; bi += 2) {
-    load(a1, b1, (bi + 1) * U);
-    mma(a0, b0);
-    if (bi + 2 < nb) load(a0, b0, (bi + 2) * U);
-    mma(a1, b1);
-  }
-  if (bi < nb) mma(a0, b0); // an odd batch count ends in the first set
-  for (int s = nb * U; s < steps; ++s) {
-    const int v = vec(s);
-    const bf16x8 a = xa[v];
+  const int pre = min(kRouterStages - 1, nchunk);
+  for (int c = 0; c < pre; ++c) issue(c);
+  for (int c = 0; c < nchunk; ++c) {
+    // chunk c has landed for this wavefront once only the chunks issued
+    // after it (at most kRouterStages - 2) are in flight; the barrier makes
+    // it so for every wavefront, and frees the stage of chunk c - 1
+    const int after = min(kRouterStages - 2, nchunk - 1 - c);
+    if (after >= 2)
+      wait_vmcnt<2 * NI>();
+    else if (after == 1)
+      wait_vmcnt<NI>();
+    else
+      wait_vmcnt<0>();
+    block_barrier();
+    if (c + kRouterStages - 1 < nchunk) issue(c + kRouterStages - 1);
+    const MOE_LDS unsigned char *sb =
+        (const MOE_LDS unsigned char *)ring + (c % kRouterStages) * SB;
+    const bf16x8 a = *(const MOE_LDS bf16x8 *)(sb + row * 128 + gpos);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const bf16x8 b = wb[n][v];
+      const bf16x8 b = *(const MOE_LDS bf16x8 *)(sb + XB + (32 * n + row) * 128 + gpos);
       acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[n], 0, 0, 0);
     }
   }
 
+  // every wavefront is done reading the ring (the last wait was for all DMA)
+  __syncthreads();
   // accumulator r of lane l: token 8 (r / 4) + 4 (l / 32) + r % 4, expert 32 n + l % 32
 #pragma unroll
   for (int n = 0; n < NT; ++n)
