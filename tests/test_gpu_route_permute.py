@@ -39,6 +39,31 @@ def test_route_ties_and_special_rows():
     _route_case(big, 6, "wide-range")
 
 
+def test_route_special_values():
+    """The selection order on the fp32 bit patterns that order tricks get
+    wrong: -0 equal to +0 (ties to the lower id), denormals, the smallest
+    normals and +-FLT_MAX, with many duplicates.  Weights of experts far below
+    the top are exactly 0 on both sides, so they are compared with an absolute
+    floor."""
+    vals = np.array([-0.0, 0.0, 1e-45, -1e-45, 1.1754944e-38, -1.1754944e-38, 3.4028235e38,
+                     -3.4028235e38, 1.0, -1.0, 2.0, -2.0], dtype=np.float32)
+    g = np.random.default_rng(23)
+    for E, k in ((12, 4), (70, 9), (130, 16)):
+        lg = vals[g.integers(0, len(vals), size=(300, E))]
+        lg[0, :] = -0.0
+        lg[1, :] = 0.0
+        lg[2, ::2] = -0.0  # alternating -0 / +0: equal, so the lowest ids win
+        lg[2, 1::2] = 0.0
+        say("route special values E", E, "k", k)
+        idx, w = moe.route(torch.from_numpy(lg).cuda(), k)
+        torch.cuda.synchronize()
+        ridx, rw = oracle.route(lg, k)
+        assert np.array_equal(idx.cpu().numpy(), ridx), (E, k)
+        assert np.array_equal(ridx[2], np.arange(k)), "the oracle takes -0 == +0"
+        wg = w.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(wg - rw) <= 1e-6 * np.abs(rw) + 1e-37), (E, k)
+
+
 def test_route_config_shapes():
     for name in ("tiny", "tp_share", "prefill"):
         d = syn.make_config(name, with_weights=False)
