@@ -246,17 +246,9 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint
       u32x4 v = *(const MOE_LDS u32x4 *)(stg + row * RB + ((ch ^ ((row >> SH) & (CPR - 1))) * 16));
       if ((row >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]}; // halves back in column order
       const int trow = row0 + i * 32 + row; // row inside the task
-      if (!skip || skip[trow] >= 0) {
-        u32x4 *dst = reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(Dt) +
-                                               (uint32_t)((trow * N + col0 + ch * 8) * 2));
-        // a plain product (the down GEMM's y, read once by the combine) is
-        // stored non-temporally: the down GEMM ran 4 us faster, the combine
-        // no slower; SiLU*up's h stays cached for the down GEMM that reads it
-        if constexpr (NB == 1)
-          __builtin_nontemporal_store(v, dst);
-        else
-          *dst = v;
-      }
+      if (!skip || skip[trow] >= 0)
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(Dt) +
+                                   (uint32_t)((trow * N + col0 + ch * 8) * 2)) = v;
     }
   }
 }
