@@ -116,8 +116,10 @@ int moe_route(const float *logits, int T, int E, int k, int32_t *topk_idx,
               float *topk_w, void *stream);
 
 /* ------------------------------------------------------------------------
- * moe_router -- the router front end in one launch: the logits of the
- * linear router, then exactly moe_route on them.       [P2 s.4, the route]
+ * moe_router -- the router front end: the logits of the linear router,
+ * then exactly moe_route on them (one launch; two when the hidden dimension
+ * is sliced, the second adding the slices and routing).
+ *                                                       [P2 s.4, the route]
  * The pages take the logits as given; the step before them is read as the
  * plain linear router without bias:
  *   logits[t][e] = sum_h x[t][h] * w_router[e][h]

@@ -1,5 +1,5 @@
 // router.hip -- the router front end: logits = x . W^T and the routing of
-// those logits in one launch.
+// those logits (one launch, or two when the hidden dimension is sliced).
 //
 // The pages take the router logits as given (the route that the reorder of
 // "Comm-compute fusion (1)", section 4 follows); the step before them is the
