@@ -278,6 +278,34 @@ def test_row_task_plan_matches_definition(nblk, num_rows_extra):
     assert np.array_equal(got, ref)
 
 
+def test_zero_rows_write_nothing():
+    """A device-side row count of 0 (a share that received no rows): the plan
+    holds no task, no workgroup runs one, and no output element is written,
+    for every epilogue."""
+    K, N, cap, T, k = 128, 256, 4 * 128, 64, 2
+    bg_np = np.array([0, 1, 1, 0], np.int32)
+    bg = torch.from_numpy(bg_np).cuda()
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+    A = torch.ones((cap, K), dtype=torch.bfloat16, device="cuda")
+    B = torch.ones((2, K, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.full((moe.gemm_workspace(cap).numel(),), 0x55, dtype=torch.uint8, device="cuda")
+    for epi in ("store", "silu_mul"):
+        say("zero rows", epi)
+        out = torch.full((cap, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        moe.grouped_gemm(A, B, bg, zero, N=N, K=K, cap=cap, B2=B if epi == "silu_mul" else None,
+                         epilogue=epi, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.isnan(out).all(), epi
+        assert np.array_equal(ws[:8].view(torch.int32).cpu().numpy(), _plan_by_definition(bg_np, 0, cap))
+    say("zero rows", "weighted_scatter")
+    acc = torch.full((T, N), 3.0, dtype=torch.float32, device="cuda")
+    row_pair = (torch.arange(cap, dtype=torch.int32, device="cuda") % (T * k)).contiguous()
+    moe.grouped_gemm(A, B, bg, zero, N=N, K=K, cap=cap, epilogue="weighted_scatter", row_pair=row_pair,
+                     pair_w=torch.ones((T, k), dtype=torch.float32, device="cuda"), out=acc, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(acc, torch.full_like(acc, 3.0))
+
+
 def test_padding_rows_not_written():
     # rows whose source (or epilogue pair) is negative are padding: left untouched
     K, N, G, T = 128, 256, 3, 200
