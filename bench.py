@@ -302,6 +302,7 @@ def main():
     }
     if a.cpu_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(d, a.cpu_seconds)
+        rec["cpu_baseline_router"] = cpu_router_baseline(d["x"], wr_bits, k)
     print(json.dumps(rec), flush=True)
 
 
@@ -348,6 +349,7 @@ def bench_dense(a):
         "roofline": {"kernel": "grouped_gemm (one group, B [N][K], fp16)", "bound": "mfma",
                      "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        **({"cpu_baseline": cpu_dense_baseline(d, a.cpu_seconds)} if a.cpu_seconds > 0 else {}),
     }), flush=True)
 
 
@@ -540,6 +542,41 @@ def cpu_baseline(d, target_s):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": "%d of %d tokens (all %d routed slots each), fp64 per-token loops" % (len(toks), T, k)}
+
+
+def cpu_router_baseline(x_bits, wr_bits, k):
+    """The oracle of the router front end (fp64 logits, then the routing) on
+    all tokens of the workload, beside the router leg."""
+    import oracle
+    t0 = time.perf_counter()
+    lg = oracle.router_logits(x_bits, wr_bits)
+    oracle.route(lg.astype(np.float32), k)
+    dt = time.perf_counter() - t0
+    return {"value": round(dt * 1e6, 1), "unit": "us per call", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "all %d tokens: fp64 logits x . W_r^T, then the top-%d routing" % (x_bits.shape[0], k)}
+
+
+def cpu_dense_baseline(d, target_s):
+    """The oracle of the dense case on a bounded sample of output rows."""
+    import oracle
+    M, N, K = d["M"], d["N"], d["K"]
+    B = d["B"].reshape(1, N, K)
+    bg = np.zeros(M // 128, np.int32)
+    n = 8
+    rng = np.random.default_rng(0)
+    while True:
+        rows = np.sort(rng.choice(M, min(n, M), replace=False)).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.grouped_gemm(d["A"], B, bg, N=N, K=K, is_fp16=True, b_layout="nk", rows=rows)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= M:
+            break
+        n = int(min(M, max(2 * n, n * target_s / max(dt, 1e-3) * 1.1)))
+    flops = 2.0 * len(rows) * N * K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "%d of %d rows of D, fp64 dot products" % (len(rows), M)}
 
 
 if __name__ == "__main__":
