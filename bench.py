@@ -495,7 +495,7 @@ def measured_peaks():
     return {"mfma_bf16_tflops": round(mfma, 1), "mfma_published": PEAK_BF16_TFLOPS,
             "hbm_read_gbs": round(hbm, 1), "hbm_published": PEAK_HBM_GBS,
             "how": "MFMA-only loop (8 independent 32x32x16 bf16 chains per wavefront, %d workgroups); "
-                   "read-only stream of 2 GiB, 16-byte non-temporal loads" % wgs}
+                   "read-only stream of 2 GiB, 16-byte loads, 1 MiB contiguous per workgroup" % wgs}
 
 
 def recorded_traffic(name):

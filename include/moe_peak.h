@@ -27,9 +27,9 @@ long long moe_peak_mfma_flops(int workgroups, int iters);
 int moe_peak_mfma(int workgroups, int iters, float *sink, void *stream);
 
 /* Read-only stream of `bytes` (16-byte aligned buffer; the last bytes % 16
- * are not read) by `workgroups` workgroups of 256 threads, 16-byte
- * non-temporal loads.  sink: `workgroups` unsigned, written only in a case
- * that never happens. */
+ * are not read) by `workgroups` workgroups of 256 threads, each reading its
+ * own contiguous part with 16-byte loads.  sink: `workgroups` unsigned,
+ * written only in a case that never happens. */
 int moe_peak_read(const void *buf, size_t bytes, int workgroups, unsigned *sink, void *stream);
 
 #ifdef __cplusplus

@@ -1,6 +1,7 @@
 // peak.hip -- measured peaks of the part, reported next to the published
 // ones: an MFMA-only loop (bf16 v_mfma_f32_32x32x16, no memory traffic) and a
-// read-only HBM stream (16-byte loads, grid-stride).  Measurement only: the
+// read-only HBM stream (16-byte loads, one contiguous part per
+// workgroup).  Measurement only: the
 // MoE path never calls these; they live in their own library,
 // libmoe_peak_gfx950.so (include/moe_peak.h).
 #include <hip/hip_runtime.h>
@@ -40,21 +41,26 @@ __global__ __launch_bounds__(256) void mfma_loop(int iters, float *sink) {
   if (s == -1.2345f) sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
-// Grid-stride read of n16 16-byte vectors, 8 loads in flight per thread; the
-// XOR of everything read is written only if it equals a sentinel.
+// Each workgroup reads its own contiguous part of the n16 16-byte vectors
+// (n16 / gridDim.x of them; the last one also takes the remainder), 4 KiB per
+// step across its 256 threads, 8 steps in flight per thread -- the pattern
+// that streamed fastest among grid-stride, per-workgroup and LDS-DMA forms;
+// the XOR of everything read is written only if it equals a sentinel.
 __global__ __launch_bounds__(256) void read_stream(const u32x4 *__restrict__ p, size_t n16,
                                                    unsigned *sink) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t per = n16 / gridDim.x;
+  const size_t b0 = (size_t)blockIdx.x * per;
+  const size_t b1 = blockIdx.x + 1 == gridDim.x ? n16 : b0 + per;
+  size_t i = b0 + threadIdx.x;
   u32x4 acc = {0, 0, 0, 0};
-  for (; i + 7 * stride < n16; i += 8 * stride) {
+  for (; i + 7 * 256 < b1; i += 8 * 256) {
     u32x4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+    for (int u = 0; u < 8; ++u) v[u] = p[i + u * 256];
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc ^= v[u];
   }
-  for (; i < n16; i += stride) acc ^= p[i];
+  for (; i < b1; i += 256) acc ^= p[i];
   if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9e3779b9u) sink[blockIdx.x] = acc[0];
 }
 
