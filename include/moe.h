@@ -165,7 +165,8 @@ size_t moe_router_workspace_size(int T, int H, int E);
  *                  for the padding rows below M_pad; rows at or past M_pad are
  *                  not written.
  * cap must be a multiple of 128 and >= moe_padded_capacity(T, k, E).
- * Expert ids outside [0, E) are undefined behaviour.
+ * A pair whose expert id lies outside [0, E) gets no row: pair_to_row[p] =
+ * -1, it counts for no expert, and moe_combine adds nothing for it.
  * Workspace: moe_permute_workspace_size(T, k, E) bytes, 256-byte aligned.
  * ---------------------------------------------------------------------- */
 size_t moe_permute_workspace_size(int T, int k, int E);
@@ -241,6 +242,28 @@ int grouped_gemm(int dtype, int N, int K, int cap, const void *A,
                  void *D, void *workspace, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * grouped_gemm_tuned -- grouped_gemm with the launch shape named by the
+ * caller, for tests and tuning sweeps (the product entry points always take
+ * the library's own choice).                                      [P1 s.4]
+ * The same operation, arguments and results as grouped_gemm, plus:
+ *   tile  NULL (the default configuration) or int32[6] =
+ *         {columns per task (per B matrix), k per slice, A ring depth,
+ *          B ring depth, row tasks per super-block of the task order,
+ *          wavefronts per workgroup}; only instantiated configurations run
+ *         (MOE_ERR_UNSUPPORTED otherwise, never a silent fallback).
+ *   grid  persistent workgroups, 0 = one per compute unit (the product
+ *         choice); a smaller grid gives each workgroup more tasks, which
+ *         the result does not depend on.  0 <= grid <= 65535.
+ * ---------------------------------------------------------------------- */
+int grouped_gemm_tuned(int dtype, int N, int K, int cap, const void *A,
+                       const int32_t *a_src_row, int a_src_div, const void *B,
+                       const void *B2, int b_layout, const int32_t *block_group,
+                       const int32_t *num_rows, int epilogue,
+                       const int32_t *epi_row_pair, const float *pair_w, int k,
+                       void *D, const int32_t *tile, int grid, void *workspace,
+                       size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * moe_combine -- top-k weighted reduction back to token order.    [P2 s.4]
  *   out[t][n] = round_bf16( sum_{j<k} topk_w[t][j] * y[pair_to_row[t*k+j]][n] )
  * accumulated in fp32 in slot order.
@@ -276,7 +299,8 @@ int moe_finalize(const float *acc, size_t n, void *out, void *stream);
  * y stored as bf16 [M_pad][H]; both live in the workspace.  The combine is
  * MOE_COMBINE_GATHER (deterministic: same input, same bits).
  * Requires H % 64 == 0, I % 64 == 0, plus the limits of the steps.
- * Workspace: moe_layer_workspace_size(T, H, E, k, I) bytes, 256-byte aligned.
+ * Workspace: moe_layer_workspace_size_ex(T, H, E, k, I, MOE_COMBINE_GATHER)
+ * bytes (or more), 256-byte aligned.
  * ---------------------------------------------------------------------- */
 size_t moe_layer_workspace_size(int T, int H, int E, int k, int I);
 
@@ -288,11 +312,19 @@ size_t moe_layer_workspace_size(int T, int H, int E, int k, int I);
  *   6 block_expert [cap/128]    7 num_padded_rows [1] int32
  *   8 h [cap][I] bf16           9 y [cap][H] bf16
  *  10 permute scratch          11 grouped-GEMM row-task plan
- *  12 out_acc [T][H] fp32 (MOE_COMBINE_SCATTER only)
+ *  12 out_acc [T][H] fp32 (MOE_COMBINE_SCATTER only; it comes last, so
+ *     the gather combine needs only off[12] bytes)
  *  13 total size
  * Returns MOE_OK or MOE_ERR_INVALID. */
 int moe_layer_workspace_layout(int T, int H, int E, int k, int I,
                                size_t off[14]);
+
+/* Workspace bytes of moe_layer_ex with the given combine: off[12] of the
+ * layout for MOE_COMBINE_GATHER (no out_acc), off[13] for
+ * MOE_COMBINE_SCATTER; 0 for invalid sizes or an unknown combine.
+ * moe_layer_workspace_size is the larger of the two. */
+size_t moe_layer_workspace_size_ex(int T, int H, int E, int k, int I,
+                                   int combine);
 
 int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
               const float *topk_w_in, const void *w_gate, const void *w_up,
@@ -306,7 +338,8 @@ int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
  *                        by the call) with MOE_EPI_WEIGHTED_SCATTER, then
  *                        moe_finalize rounds it into out; y is never stored.
  *                        Sums of a token's k slots are in no fixed order.
- * Same arguments, workspace and limits as moe_layer otherwise. */
+ * Workspace: moe_layer_workspace_size_ex(T, H, E, k, I, combine) bytes.
+ * Same arguments and limits as moe_layer otherwise. */
 int moe_layer_ex(const void *x, const float *logits,
                  const int32_t *topk_idx_in, const float *topk_w_in,
                  const void *w_gate, const void *w_up, const void *w_down,

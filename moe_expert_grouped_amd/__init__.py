@@ -71,10 +71,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "moe_permute": ([P, I, I, I, P, I, P, P, P, P, P, P, P, I, P, Z, P], I),
             "grouped_gemm_workspace_size": ([I], Z),
             "grouped_gemm": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P, I, P, P, Z, P], I),
+            "grouped_gemm_tuned": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P, I, P, P, I, P, Z, P],
+                                   I),
             "moe_combine": ([P, I, P, P, I, I, P, P], I),
             "moe_finalize": ([P, Z, P, P], I),
             "moe_pack_gate_up": ([P, P, I, I, I, P, P], I),
             "moe_layer_workspace_size": ([I, I, I, I, I], Z),
+            "moe_layer_workspace_size_ex": ([I, I, I, I, I, I], Z),
             "moe_layer_workspace_layout": ([I, I, I, I, I, ctypes.POINTER(Z)], I),
             "moe_layer": ([P, P, P, P, P, P, P, I, I, I, I, I, P, P, Z, P], I),
             "moe_layer_ex": ([P, P, P, P, P, P, P, I, I, I, I, I, P, I, P, Z, P], I),
@@ -218,7 +221,8 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
                  B2: torch.Tensor | None = None, b_layout: str = "kn", epilogue: str = "store",
                  row_pair: torch.Tensor | None = None, pair_w: torch.Tensor | None = None,
                  T: int | None = None, out: torch.Tensor | None = None,
-                 workspace: torch.Tensor | None = None, b_stream: bool = False) -> torch.Tensor:
+                 workspace: torch.Tensor | None = None, b_stream: bool = False,
+                 tile: tuple | None = None, grid: int = 0) -> torch.Tensor:
     """D[r] = A[a(r)] . B[block_group[r // 128]] for r < min(num_rows, cap),
     or SiLU(A.B) * (A.B2) with epilogue="silu_mul".  Returns D [cap, N].
 
@@ -236,7 +240,13 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
     case it is accumulated into.
 
     `workspace` holds the device-built row-task plan (grouped_gemm_workspace_size(cap)
-    bytes; allocated here if not given)."""
+    bytes; allocated here if not given).
+
+    tile / grid (tests and tuning sweeps; grouped_gemm_tuned): tile is
+    (columns per task, k per slice, A ring depth, B ring depth, row tasks per
+    super-block, wavefronts) of an instantiated configuration, grid the
+    number of persistent workgroups (0: one per compute unit).  The defaults
+    are the library's own choice."""
     _need(A, "A", (torch.bfloat16, torch.float16))
     _need(B, "B", A.dtype)
     _need(block_group, "block_group", torch.int32)
@@ -267,11 +277,19 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
     lib = load_library()
     if workspace is None:
         workspace = gemm_workspace(cap, A.device)
-    _check("grouped_gemm", lib.grouped_gemm(
-        _DTYPES[A.dtype], N, K, cap, _ptr(A), _ptr(a_src_row), a_src_div, _ptr(B), _ptr(B2),
-        _LAYOUTS[b_layout] | (MOE_B_STREAM if b_stream else 0), _ptr(block_group), _ptr(num_rows), _EPIS[epilogue], _ptr(row_pair),
-        _ptr(pair_w), k, _ptr(out), _ptr(workspace), 0 if workspace is None else workspace.numel(),
-        _stream()))
+    args = (_DTYPES[A.dtype], N, K, cap, _ptr(A), _ptr(a_src_row), a_src_div, _ptr(B), _ptr(B2),
+            _LAYOUTS[b_layout] | (MOE_B_STREAM if b_stream else 0), _ptr(block_group),
+            _ptr(num_rows), _EPIS[epilogue], _ptr(row_pair), _ptr(pair_w), k, _ptr(out))
+    ws = (_ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
+    if tile is None and not grid:
+        _check("grouped_gemm", lib.grouped_gemm(*args, *ws))
+    else:
+        t = None
+        if tile is not None:
+            if len(tile) != 6:
+                raise ValueError("tile must have 6 entries")
+            t = (ctypes.c_int32 * 6)(*[int(v) for v in tile])
+        _check("grouped_gemm_tuned", lib.grouped_gemm_tuned(*args, t, int(grid), *ws))
     return out
 
 
@@ -356,8 +374,10 @@ def layer_workspace_layout(T, H, E, k, I):
     return {name: int(arr[i]) for i, name in enumerate(LAYOUT_NAMES)} | {"total": int(arr[13])}
 
 
-def layer_workspace(T, H, E, k, I, device="cuda") -> torch.Tensor:
-    n = load_library().moe_layer_workspace_size(T, H, E, k, I)
+def layer_workspace(T, H, E, k, I, device="cuda", combine: str = "scatter") -> torch.Tensor:
+    """A moe_layer workspace; combine="gather" sizes it for the gather combine
+    only (no fp32 token-row accumulator), "scatter" for both."""
+    n = load_library().moe_layer_workspace_size_ex(T, H, E, k, I, _COMBINES[combine])
     if n == 0:
         raise ValueError("invalid layer sizes")
     return torch.empty(n, dtype=torch.uint8, device=device)
@@ -387,7 +407,7 @@ def layer(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: tor
         _need(topk_idx, "topk_idx", torch.int32, 2)
         _need(topk_w, "topk_w", torch.float32, 2)
     if workspace is None:
-        workspace = layer_workspace(T, H, E, k, I, x.device)
+        workspace = layer_workspace(T, H, E, k, I, x.device, combine)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     if combine == "gather":

@@ -24,7 +24,8 @@ hipError_t launch_permute(const int32_t *, int, int, int, const uint16_t *, int,
 hipError_t launch_grouped_gemm(int, int, int, const uint16_t *, const int32_t *, int,
                                const uint16_t *, const uint16_t *, int, const int32_t *, int,
                                const int32_t *, const float *, int, void *, int, bool,
-                               hipStream_t);
+                               hipStream_t, const int32_t *tile = nullptr);
+bool gg_tile_usable(const int32_t *tile, int epilogue, int N, int K);
 hipError_t launch_gg_plan(const int32_t *, const int32_t *, int, int32_t *, hipStream_t);
 size_t gg_plan_bytes(int cap);
 hipError_t launch_combine(const uint16_t *, int, const int32_t *, const float *, int, int,
@@ -156,17 +157,22 @@ size_t grouped_gemm_workspace_size(int cap) {
   return align256(moe::gg_plan_bytes(cap));
 }
 
-int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t *a_src_row,
-                 int a_src_div, const void *B, const void *B2, int b_layout,
-                 const int32_t *block_group, const int32_t *num_rows, int epilogue,
-                 const int32_t *epi_row_pair, const float *pair_w, int k, void *D,
-                 void *workspace, size_t ws_bytes, void *stream) {
+} // extern "C"
+
+namespace {
+
+// Argument checks of every grouped GEMM entry point (the workspace aside).
+// Splits the MOE_B_STREAM flag off b_layout.
+int check_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t *a_src_row,
+               int a_src_div, const void *B, const void *B2, int &b_layout, bool &b_stream,
+               const int32_t *block_group, const int32_t *num_rows, int epilogue,
+               const int32_t *epi_row_pair, const float *pair_w, int k, const void *D) {
   if (!A || !B || !block_group || !num_rows || !D) return MOE_ERR_INVALID;
   if (!aligned16(A) || !aligned16(B) || !aligned16(D) || (B2 && !aligned16(B2)))
     return MOE_ERR_INVALID;
   if (N <= 0 || K <= 0 || cap <= 0) return MOE_ERR_INVALID;
   if (dtype != MOE_BF16 && dtype != MOE_FP16) return MOE_ERR_UNSUPPORTED;
-  const bool b_stream = (b_layout & MOE_B_STREAM) != 0;
+  b_stream = (b_layout & MOE_B_STREAM) != 0;
   b_layout &= ~MOE_B_STREAM;
   if (b_layout != MOE_B_KN && b_layout != MOE_B_NK && b_layout != MOE_B_KN_GATE_UP)
     return MOE_ERR_UNSUPPORTED;
@@ -188,18 +194,61 @@ int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t 
   if (a_src_row && a_src_div <= 0) return MOE_ERR_INVALID;
   if (N % 64 != 0 || K % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (cap % MOE_ROW_BLOCK != 0) return MOE_ERR_INVALID;
-  if (workspace && !aligned16(workspace)) return MOE_ERR_INVALID;
-  if (!workspace || ws_bytes < grouped_gemm_workspace_size(cap)) return MOE_ERR_WORKSPACE;
-  const int cus = device_cus();
-  if (cus == 0) return MOE_ERR_DEVICE;
-  hipStream_t s = (hipStream_t)stream;
-  int32_t *plan = (int32_t *)workspace;
+  return MOE_OK;
+}
+
+// The plan kernel into `plan`, then the GEMM (arguments checked).
+int gemm_enqueue(int dtype, int N, int K, int cap, const void *A, const int32_t *a_src_row,
+                 int a_src_div, const void *B, const void *B2, int b_layout, bool b_stream,
+                 const int32_t *block_group, const int32_t *num_rows, int epilogue,
+                 const int32_t *epi_row_pair, const float *pair_w, int k, void *D, int32_t *plan,
+                 const int32_t *tile, int grid, hipStream_t s) {
   if (moe::launch_gg_plan(block_group, num_rows, cap, plan, s) != hipSuccess)
     return MOE_ERR_DEVICE;
   return launch_status(moe::launch_grouped_gemm(
       dtype, N, K, (const uint16_t *)A, a_src_row, a_src_div, (const uint16_t *)B,
-      (const uint16_t *)B2, b_layout, plan, epilogue, epi_row_pair, pair_w, k, D, cus, b_stream,
-      s));
+      (const uint16_t *)B2, b_layout, plan, epilogue, epi_row_pair, pair_w, k, D, grid, b_stream,
+      s, tile));
+}
+
+} // namespace
+
+extern "C" {
+
+int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t *a_src_row,
+                 int a_src_div, const void *B, const void *B2, int b_layout,
+                 const int32_t *block_group, const int32_t *num_rows, int epilogue,
+                 const int32_t *epi_row_pair, const float *pair_w, int k, void *D,
+                 void *workspace, size_t ws_bytes, void *stream) {
+  return grouped_gemm_tuned(dtype, N, K, cap, A, a_src_row, a_src_div, B, B2, b_layout,
+                            block_group, num_rows, epilogue, epi_row_pair, pair_w, k, D, nullptr,
+                            0, workspace, ws_bytes, stream);
+}
+
+int grouped_gemm_tuned(int dtype, int N, int K, int cap, const void *A, const int32_t *a_src_row,
+                       int a_src_div, const void *B, const void *B2, int b_layout,
+                       const int32_t *block_group, const int32_t *num_rows, int epilogue,
+                       const int32_t *epi_row_pair, const float *pair_w, int k, void *D,
+                       const int32_t *tile, int grid, void *workspace, size_t ws_bytes,
+                       void *stream) {
+  bool b_stream = false;
+  int st = check_gemm(dtype, N, K, cap, A, a_src_row, a_src_div, B, B2, b_layout, b_stream,
+                      block_group, num_rows, epilogue, epi_row_pair, pair_w, k, D);
+  if (st != MOE_OK) return st;
+  if (grid < 0 || grid > 65535) return MOE_ERR_INVALID;
+  if (tile) {
+    if (!moe::gg_tile_usable(tile, epilogue, N, K)) return MOE_ERR_UNSUPPORTED;
+    // the interleaved gate/up layout needs column tiles inside 128-column blocks
+    if (b_layout == MOE_B_KN_GATE_UP && (tile[0] > 128 || 128 % tile[0] != 0))
+      return MOE_ERR_UNSUPPORTED;
+  }
+  if (workspace && !aligned16(workspace)) return MOE_ERR_INVALID;
+  if (!workspace || ws_bytes < grouped_gemm_workspace_size(cap)) return MOE_ERR_WORKSPACE;
+  const int cus = device_cus();
+  if (cus == 0) return MOE_ERR_DEVICE;
+  return gemm_enqueue(dtype, N, K, cap, A, a_src_row, a_src_div, B, B2, b_layout, b_stream,
+                      block_group, num_rows, epilogue, epi_row_pair, pair_w, k, D,
+                      (int32_t *)workspace, tile, grid > 0 ? grid : cus, (hipStream_t)stream);
 }
 
 int moe_pack_gate_up(const void *w_gate, const void *w_up, int E, int K, int N, void *out,
@@ -266,6 +315,13 @@ size_t moe_layer_workspace_size(int T, int H, int E, int k, int I) {
   return off[13];
 }
 
+size_t moe_layer_workspace_size_ex(int T, int H, int E, int k, int I, int combine) {
+  size_t off[14];
+  if (moe_layer_workspace_layout(T, H, E, k, I, off) != MOE_OK) return 0;
+  if (combine == MOE_COMBINE_GATHER) return off[12]; // out_acc, last, is the scatter's only
+  return combine == MOE_COMBINE_SCATTER ? off[13] : 0;
+}
+
 int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
               const float *topk_w_in, const void *w_gate, const void *w_up, const void *w_down,
               int T, int H, int E, int k, int I, void *out, void *workspace, size_t ws_bytes,
@@ -292,7 +348,8 @@ int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
   if (combine != MOE_COMBINE_GATHER && combine != MOE_COMBINE_SCATTER) return MOE_ERR_UNSUPPORTED;
   size_t off[14];
   moe_layer_workspace_layout(T, H, E, k, I, off);
-  if (ws_bytes < off[13]) return MOE_ERR_WORKSPACE;
+  // the fp32 token-row accumulator (last in the layout) only for the scatter
+  if (ws_bytes < (combine == MOE_COMBINE_SCATTER ? off[13] : off[12])) return MOE_ERR_WORKSPACE;
   const int cus = device_cus();
   if (cus == 0) return MOE_ERR_DEVICE;
 

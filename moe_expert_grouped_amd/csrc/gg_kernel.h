@@ -58,9 +58,6 @@
 //     through LDS (the stages of the slice just consumed) so each store
 //     writes whole row pieces; the weighted scatter adds with fp32 atomics.
 #pragma once
-#include <stdio.h>
-#include <stdlib.h>
-
 #include <utility>
 
 #include "common.h"

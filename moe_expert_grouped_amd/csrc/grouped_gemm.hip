@@ -34,12 +34,12 @@ MOE_GG_EXTERN(kEpiScatter, true, true, true)
 // 32-deep slices, a 3-deep A ring and a 6-deep B ring (weights are most of
 // the bytes in flight); the 128 / 256-column tiles with eight wavefronts
 // (two per SIMD: one's matrix instructions run while the other issues its
-// fragment reads and DMA), except for the weighted scatter.  Each can be overridden for tuning sweeps with
-// MOE_GG_TILE="<bn>,<bk>,<na>,<nb>[,<group rows>[,<wavefronts>]]" (MOE_GG_TILE_GU, if set,
-// for the SiLU*up epilogue only).  A configuration is used
-// only if it is instantiated, divides N, and its B ring keeps the per-task
-// tables safe for this K (2 * K / BK >= nb - 1); otherwise the 4-deep rings,
-// instantiated for every BN.
+// fragment reads and DMA), except for the weighted scatter.  A configuration
+// is used only if it is instantiated, divides N, and its B ring keeps the
+// per-task tables safe for this K (2 * K / BK >= nb - 1); otherwise the
+// 4-deep rings, instantiated for every BN.  grouped_gemm_tuned (tests and
+// tuning sweeps) names another instantiated configuration explicitly; the
+// product entry points always take this choice.
 static bool tile_usable(const TileCfg &c, int epilogue, int N, int K) {
   return c.group >= 1 && c.bn > 0 && c.bk > 0 && N % c.bn == 0 && K % c.bk == 0 &&
          (c.waves == 4 || epilogue != kEpiScatter) &&
@@ -61,15 +61,14 @@ static TileCfg tile_config(int epilogue, int N, int K) {
     c.na = c.nb = 4;
     c.waves = 4;
   }
-  const char *env = epilogue == kEpiSiluMul ? getenv("MOE_GG_TILE_GU") : nullptr;
-  if (!env) env = getenv("MOE_GG_TILE");
-  if (env) {
-    TileCfg e{0, 0, 0, 0, 1};
-    const int n =
-        sscanf(env, "%d,%d,%d,%d,%d,%d", &e.bn, &e.bk, &e.na, &e.nb, &e.group, &e.waves);
-    if (n >= 4 && tile_usable(e, epilogue, N, K)) c = e;
-  }
   return c;
+}
+
+// An explicit tile configuration {bn, bk, na, nb, group rows, wavefronts}
+// (grouped_gemm_tuned): whether this GEMM can run it.
+bool gg_tile_usable(const int32_t *t, int epilogue, int N, int K) {
+  const TileCfg c{t[0], t[1], t[2], t[3], t[4], t[5]};
+  return tile_usable(c, epilogue, N, K);
 }
 
 // Plan of row tasks (one workgroup of 1024 threads): inside each maximal run
@@ -149,14 +148,20 @@ static hipError_t launch_kn_stream(const GGArgs &a, const TileCfg &c, int epilog
 // 2 WEIGHTED_SCATTER (KN only; D is then the fp32 token-row accumulator);
 // b_stream: B loaded with the non-temporal policy (KN only).  `plan` holds
 // the row-task plan of block_group (launch_gg_plan), built earlier on the
-// same stream.
+// same stream.  grid: persistent workgroups (one per CU in the product
+// path; LDS holds one per CU, any count >= 1 computes the same result);
+// tile: NULL for the default configuration.
 hipError_t launch_grouped_gemm(int dtype, int N, int K, const uint16_t *A,
                                const int32_t *a_src_row, int a_src_div, const uint16_t *B,
                                const uint16_t *B2, int layout, const int32_t *plan, int epilogue,
                                const int32_t *epi_row_pair, const float *pair_w, int topk,
-                               void *D, int num_cus, bool b_stream, hipStream_t stream) {
-  const TileCfg c = tile_config(epilogue, N, K);
-  const int grid = num_cus; // one workgroup per CU (LDS-limited)
+                               void *D, int grid, bool b_stream, hipStream_t stream,
+                               const int32_t *tile) {
+  // the default configuration, or the explicit one of grouped_gemm_tuned
+  // (checked by gg_tile_usable before the call)
+  const TileCfg c =
+      tile ? TileCfg{tile[0], tile[1], tile[2], tile[3], tile[4], tile[5]} : tile_config(epilogue, N, K);
+  if (tile && !tile_usable(c, epilogue, N, K)) return hipErrorInvalidValue;
   const bool scat = epilogue == kEpiScatter;
   const bool il = layout == 2; // [K][2N], gate/up interleaved in 128-column blocks
   GGArgs a{A, a_src_row, a_src_div, B, il ? B : B2, plan,

@@ -23,7 +23,8 @@
 //                            M_pad (each x row read once, stored to its k
 //                            rows), zero rows for padding (16-byte vectors)
 // Routings of at most 16384 pairs take passes 1-3 in a single launch
-// instead (permute_plan.hip).
+// instead (permute_plan.hip).  On both paths a pair whose expert id lies
+// outside [0, E) gets no row (pair_to_row = -1) and counts for no expert.
 #include "common.h"
 
 #include <algorithm>
@@ -43,7 +44,10 @@ __global__ __launch_bounds__(kPermThreads) void permute_hist(const int32_t *__re
   __syncthreads();
   const long p0 = (long)c * kPermChunk;
   const long p1 = min(p0 + kPermChunk, R);
-  for (long p = p0 + threadIdx.x; p < p1; p += blockDim.x) atomicAdd(&cnt[idx[p]], 1);
+  for (long p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
+    const int e = idx[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1); // ids outside [0, E) get no row
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)e * nchunks + c] = cnt[e];
 }
@@ -151,8 +155,12 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter(
   const long p0 = (long)c * kPermChunk;
   for (int sub = 0; sub < kPermChunk; sub += kPermThreads) {
     const long p = p0 + sub + threadIdx.x;
-    const bool valid = p < R;
-    const int key = valid ? idx[p] : E;
+    const bool in = p < R;
+    const int raw = in ? idx[p] : E;
+    // a pair routed outside [0, E) takes the "no pair" key E and gets no row
+    const bool valid = in && (unsigned)raw < (unsigned)E;
+    const int key = valid ? raw : E;
+    if (in && !valid) pair_to_row[p] = -1;
     // lanes of this wavefront holding the same key
     unsigned long long same = ~0ull;
     for (int b = 0; b < nbits; ++b) {

@@ -115,3 +115,22 @@ def ternary_bits(shape, seed, dtype="bf16", p_zero=1 / 3):
     v = g.choice(np.array([-1.0, 0.0, 1.0], np.float32), size=shape,
                  p=[(1 - p_zero) / 2, p_zero, (1 - p_zero) / 2])
     return bf16_bits(v) if dtype == "bf16" else fp16_bits(v)
+
+
+def sparse_ternary_bits(shape, seed, density, dtype="bf16"):
+    """Entries in {-1, 0, +1}, each non-zero with probability `density`
+    (rounded to a multiple of 1/128), +1 and -1 equally likely; uint16 bits.
+    One byte drawn per entry and mapped through a table, so full-size weight
+    tensors are quick to make.  Sparse enough, every product of such
+    matrices stays a small integer: exact in fp32 in any summation order and
+    exactly representable after the 16-bit store."""
+    t = int(round(128 * density))
+    if not 0 <= t <= 128:
+        raise ValueError("density must be in [0, 1]")
+    one = bf16_bits if dtype == "bf16" else fp16_bits
+    pos, neg = (int(v) for v in one(np.array([1.0, -1.0], np.float32)))
+    lut = np.zeros(256, np.uint16)
+    lut[:t] = pos
+    lut[256 - t:] = neg
+    u = np.random.default_rng(seed).integers(0, 256, size=shape, dtype=np.uint8)
+    return lut[u]

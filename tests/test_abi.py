@@ -28,9 +28,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 17, names
-    for n in ["moe_route", "moe_router", "moe_permute", "grouped_gemm", "moe_combine", "moe_finalize", "moe_layer",
-              "moe_layer_ex", "moe_pack_gate_up"]:
+    assert len(names) == 19, names
+    for n in ["moe_route", "moe_router", "moe_permute", "grouped_gemm", "grouped_gemm_tuned", "moe_combine",
+              "moe_finalize", "moe_layer", "moe_layer_ex", "moe_pack_gate_up", "moe_layer_workspace_size_ex"]:
         assert n in names
     for n in names:
         assert hasattr(lib, n), "missing export " + n
@@ -66,6 +66,10 @@ def test_layer_workspace_layout(lib):
     assert lay["total"] - lay["out_acc"] >= T * H * 4
     assert lib.moe_layer_workspace_size(T, H, E, k, I) == lay["total"]
     assert lib.moe_layer_workspace_size(T, H, E, 65, I) == 0  # k > E
+    # the gather combine needs no fp32 token-row accumulator, which comes last
+    assert lib.moe_layer_workspace_size_ex(T, H, E, k, I, 0) == lay["out_acc"]
+    assert lib.moe_layer_workspace_size_ex(T, H, E, k, I, 1) == lay["total"]
+    assert lib.moe_layer_workspace_size_ex(T, H, E, k, I, 2) == 0
 
 
 FAKE = ctypes.c_void_p(4096)       # aligned non-null; never dereferenced
@@ -162,6 +166,28 @@ def test_grouped_gemm_validation(lib):
     assert lib.grouped_gemm_workspace_size(0) == 0
 
 
+def test_grouped_gemm_tuned_validation(lib):
+    # the explicit launch shape of tests and sweeps: an instantiated tile that
+    # fits the shape, or MOE_ERR_UNSUPPORTED (never a silent fallback)
+    def call(tile=None, grid=0, N=512, K=256, epi=0, lay=0, B2=NULL, wsb=1 << 20):
+        t = None if tile is None else (ctypes.c_int32 * 6)(*tile)
+        return lib.grouped_gemm_tuned(0, N, K, 256, FAKE, NULL, 1, FAKE, B2, lay, FAKE, FAKE, epi, NULL,
+                                      NULL, 0, FAKE, t, grid, FAKE, wsb, NULL)
+    assert call(tile=(256, 32, 3, 6, 1, 8)) == moe.MOE_ERR_DEVICE      # valid; no GPU here
+    assert call(tile=(256, 32, 3, 6, 1, 8), grid=8) == moe.MOE_ERR_DEVICE
+    assert call(grid=-1) == moe.MOE_ERR_INVALID
+    assert call(grid=65536) == moe.MOE_ERR_INVALID
+    assert call(tile=(256, 32, 3, 7, 1, 4)) == moe.MOE_ERR_UNSUPPORTED  # not instantiated
+    assert call(tile=(256, 64, 3, 6, 1, 4)) == moe.MOE_ERR_UNSUPPORTED  # 64-deep slices: not built
+    assert call(tile=(256, 32, 3, 6, 1, 4), N=384) == moe.MOE_ERR_UNSUPPORTED  # 256 does not divide N
+    assert call(tile=(256, 32, 3, 6, 1, 4), K=64) == moe.MOE_ERR_UNSUPPORTED  # ring unsafe for 2 slices
+    assert call(tile=(256, 32, 3, 6, 0, 4)) == moe.MOE_ERR_UNSUPPORTED  # no row tasks per super-block
+    assert call(tile=(128, 32, 3, 6, 1, 8), epi=1, B2=FAKE) == moe.MOE_ERR_DEVICE
+    assert call(tile=(256, 32, 3, 6, 1, 8), epi=1, B2=FAKE) == moe.MOE_ERR_UNSUPPORTED  # SiLU*up: 128 max
+    assert call(tile=(64, 32, 3, 10, 1, 4), epi=1, lay=2) == moe.MOE_ERR_DEVICE
+    assert call(wsb=8) == moe.MOE_ERR_WORKSPACE
+
+
 def test_pack_gate_up_validation(lib):
     assert lib.moe_pack_gate_up(NULL, FAKE, 2, 64, 128, FAKE, NULL) == moe.MOE_ERR_INVALID
     assert lib.moe_pack_gate_up(FAKE, FAKE, 2, 64, 128, NULL, NULL) == moe.MOE_ERR_INVALID
@@ -190,7 +216,10 @@ def test_combine_and_layer_validation(lib):
     assert call(H=96) == moe.MOE_ERR_UNSUPPORTED
     assert call(I=80) == moe.MOE_ERR_UNSUPPORTED
     assert call(k=9) == moe.MOE_ERR_INVALID
-    assert call(wsb=ws - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(wsb=ws - 1) == moe.MOE_ERR_DEVICE               # the gather combine: no out_acc
+    gather_ws = lib.moe_layer_workspace_size_ex(T, H, E, k, I, 0)
+    assert call(wsb=gather_ws) == moe.MOE_ERR_DEVICE            # valid; no GPU here
+    assert call(wsb=gather_ws - 1) == moe.MOE_ERR_WORKSPACE
 
     def call_ex(combine, wsb=ws, x=FAKE):
         return lib.moe_layer_ex(x, FAKE, NULL, NULL, FAKE, FAKE, FAKE, T, H, E, k, I, FAKE, combine,

@@ -24,15 +24,21 @@ def _groups(nblk, G, seed, neg_tail=0):
     return bg
 
 
+def _tile(spec):
+    """"bn,bk,na,nb[,group rows[,wavefronts]]" -> the 6-entry tile of grouped_gemm_tuned."""
+    v = [int(x) for x in spec.split(",")]
+    return tuple(v + [1, 4][len(v) - 4:])
+
+
 def _run(A_bits, B_bits, bg, *, N, K, cap, m_rows, dtype, layout="kn", src=None, div=1, B2_bits=None,
-         epi="store"):
+         epi="store", tile=None):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
     out = torch.full((cap, N), float("nan"), dtype=tdt, device="cuda")
     D = moe.grouped_gemm(dev16(A_bits, tdt), dev16(B_bits, tdt), torch.from_numpy(bg).cuda(),
                          torch.tensor([m_rows], dtype=torch.int32, device="cuda"), N=N, K=K, cap=cap,
                          a_src_row=None if src is None else torch.from_numpy(src).cuda(), a_src_div=div,
                          B2=None if B2_bits is None else dev16(B2_bits, tdt), b_layout=layout,
-                         epilogue=epi, out=out)
+                         epilogue=epi, out=out, tile=tile)
     torch.cuda.synchronize()
     return D
 
@@ -141,12 +147,12 @@ TILES = [("store", "256,32,3,6"), ("store", "256,32,4,4,2"), ("store", "128,32,3
 
 
 @pytest.mark.parametrize("epi,tile", TILES, ids=["%s-%s" % t for t in TILES])
-def test_tile_configurations_integer_exact(epi, tile, monkeypatch):
+def test_tile_configurations_integer_exact(epi, tile):
     # every instantiated tile shape / ring depths / task order gives the
     # exact result; K = 64 and 128 have fewer slices than the B ring has
-    # stages (a configuration whose table ring is unsafe for them falls back
-    # to shallower rings)
-    monkeypatch.setenv("MOE_GG_TILE", tile)
+    # stages: a configuration whose table ring is unsafe for them is refused
+    # (MOE_ERR_UNSUPPORTED), never run
+    t = _tile(tile)
     G, N = 4, 512
     cap = 11 * 128
     bg = _groups(cap // 128, G, 17)
@@ -156,7 +162,12 @@ def test_tile_configurations_integer_exact(epi, tile, monkeypatch):
         B2 = syn.ternary_bits((G, K, N), 10) if epi == "silu_mul" else None
         m_rows = 9 * 128
         say("gemm tile", epi, tile, "K", K)
-        D = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16", B2_bits=B2, epi=epi)
+        if 2 * (K // t[1]) < t[3] - 1:
+            with pytest.raises(moe.MoeError) as ex:
+                _run(A, B, bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16", B2_bits=B2, epi=epi, tile=t)
+            assert ex.value.status == moe.MOE_ERR_UNSUPPORTED
+            continue
+        D = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16", B2_bits=B2, epi=epi, tile=t)
         ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, B2_bits=B2, epilogue=epi,
                                   rows=np.arange(m_rows, dtype=np.int32))
         got = to_f64(D)
@@ -169,11 +180,10 @@ def test_tile_configurations_integer_exact(epi, tile, monkeypatch):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("layout", ["kn", "nk"])
-def test_eight_wavefronts_integer_exact(dtype, layout, monkeypatch):
+def test_eight_wavefronts_integer_exact(dtype, layout):
     # the eight-wavefront workgroups (two per SIMD, a 128-row x 64-column
     # share of a 256 x 256 task each) on both B layouts, gathered rows, a
     # ragged group table and a block without a group
-    monkeypatch.setenv("MOE_GG_TILE", "256,32,3,6,1,8")
     G, N, K = 3, 768, 384
     cap = 9 * 128
     bg = np.array([0, 0, 0, 2, -1, 1, 1, 2, 2], np.int32)
@@ -182,7 +192,8 @@ def test_eight_wavefronts_integer_exact(dtype, layout, monkeypatch):
     B = syn.ternary_bits((G, K, N) if layout == "kn" else (G, N, K), 32, dtype)
     src = np.random.default_rng(3).integers(0, T * 2, size=cap).astype(np.int32)
     say("gemm eight wavefronts", dtype, layout)
-    D = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=cap, dtype=dtype, layout=layout, src=src, div=2)
+    D = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=cap, dtype=dtype, layout=layout, src=src, div=2,
+             tile=(256, 32, 3, 6, 1, 8))
     ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, is_fp16=dtype == "fp16", b_layout=layout,
                               a_src_row=src, a_src_div=2)
     got = to_f64(D)
@@ -349,13 +360,13 @@ def _scatter_case(T, k, E, K, N, seed, dtype="bf16"):
     return P, A, B, w
 
 
-def _run_scatter(P, A, B, w, *, N, K, dtype="bf16", out=None):
+def _run_scatter(P, A, B, w, *, N, K, dtype="bf16", out=None, tile=None):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
     return moe.grouped_gemm(dev16(A, tdt), dev16(B, tdt), torch.from_numpy(P["block_expert"]).cuda(),
                             torch.tensor([P["m_pad"]], dtype=torch.int32, device="cuda"), N=N, K=K,
                             cap=P["cap"], epilogue="weighted_scatter",
                             row_pair=torch.from_numpy(P["row_to_pair"]).cuda(),
-                            pair_w=torch.from_numpy(w).cuda(), out=out)
+                            pair_w=torch.from_numpy(w).cuda(), out=out, tile=tile)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
@@ -404,7 +415,7 @@ def test_weighted_scatter_integer_exact(dtype, T, k, E, K, N):
     assert np.array_equal(got.cpu().numpy().astype(np.float64), ref)
 
 
-def test_weighted_scatter_accumulates_and_tiles(monkeypatch):
+def test_weighted_scatter_accumulates_and_tiles():
     # `out` is accumulated into (the caller zeroes it); every tile shape gives
     # the exact result
     T, k, E, K, N = 260, 2, 6, 512, 256
@@ -412,10 +423,9 @@ def test_weighted_scatter_accumulates_and_tiles(monkeypatch):
     Y = oracle.grouped_gemm(A, B, P["block_expert"], N=N, K=K)
     ref = oracle.weighted_scatter(Y, P["row_to_pair"], w, k, T)
     for tile in ["256,32,3,6", "256,32,4,4,2", "128,32,3,10", "64,32,4,8"]:
-        monkeypatch.setenv("MOE_GG_TILE", tile)
         say("scatter tile", tile)
         base = torch.full((T, N), 3.0, dtype=torch.float32, device="cuda")
-        got = _run_scatter(P, A, B, w, N=N, K=K, out=base)
+        got = _run_scatter(P, A, B, w, N=N, K=K, out=base, tile=_tile(tile))
         torch.cuda.synchronize()
         assert np.array_equal(got.cpu().numpy().astype(np.float64), ref + 3.0), tile
 
@@ -470,11 +480,11 @@ def test_pack_gate_up_bit_exact(dtype):
 
 
 @pytest.mark.parametrize("tile", [None, "128,32,4,4,2", "64,32,3,10"])
-def test_gate_up_interleaved_layout(tile, monkeypatch):
+def test_gate_up_interleaved_layout(tile):
     # the interleaved weights give the same bits as the two separate matrices,
     # and the integer-exact result of the oracle, in every SiLU*up tile shape
-    if tile:
-        monkeypatch.setenv("MOE_GG_TILE_GU", tile)
+    # (a tile whose rings are unsafe for the K is refused on both layouts)
+    t = _tile(tile) if tile else None
     G, cap = 4, 11 * 128
     m_rows = 9 * 128
     bg = _groups(cap // 128, G, 23)
@@ -483,9 +493,16 @@ def test_gate_up_interleaved_layout(tile, monkeypatch):
         B = syn.ternary_bits((G, K, N), 12)
         B2 = syn.ternary_bits((G, K, N), 13)
         say("gemm gate/up interleaved", tile, N, K)
-        D0 = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16", B2_bits=B2, epi="silu_mul")
+        if t and 2 * (K // t[1]) < t[3] - 1:
+            for kw in (dict(B2_bits=B2), dict(layout="kn_gate_up")):
+                with pytest.raises(moe.MoeError):
+                    _run(A, B if "B2_bits" in kw else _interleave(B, B2), bg, N=N, K=K, cap=cap,
+                         m_rows=m_rows, dtype="bf16", epi="silu_mul", tile=t, **kw)
+            continue
+        D0 = _run(A, B, bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16", B2_bits=B2, epi="silu_mul",
+                  tile=t)
         D1 = _run(A, _interleave(B, B2), bg, N=N, K=K, cap=cap, m_rows=m_rows, dtype="bf16",
-                  layout="kn_gate_up", epi="silu_mul")
+                  layout="kn_gate_up", epi="silu_mul", tile=t)
         assert torch.equal(D0[:m_rows].view(torch.int16), D1[:m_rows].view(torch.int16))
         ref = oracle.grouped_gemm(A, B, bg, N=N, K=K, B2_bits=B2, epilogue="silu_mul",
                                   rows=np.arange(m_rows, dtype=np.int32))

@@ -90,7 +90,9 @@ def test_layer_tiny_steps_match_layer():
     href = oracle.grouped_gemm(d["x"], d["wg"], Po["block_expert"], N=I, K=H, a_src_row=Po["row_to_pair"],
                                a_src_div=k, B2_bits=d["wu"], epilogue="silu_mul", M=Po["m_pad"])
     real = Po["row_to_pair"][:Po["m_pad"]] >= 0
-    assert_close(to_f64(h)[:Po["m_pad"]][real], href[real], "h")
+    # only the real rows leave the device: padding rows of h are never written
+    h_real = h[:Po["m_pad"]][torch.from_numpy(real).cuda()]
+    assert_close(to_f64(h_real), href[real], "h")
     # combine against the oracle's combine of the GPU's own y (only the reduction differs)
     cref = oracle.combine(host16(y), Po["pair_to_row"], w.cpu().numpy())
     assert_close(to_f64(out2), cref, "combine", max_frac=8e-3, rel_fro=3e-3)
@@ -123,10 +125,33 @@ def _sample(T, n, seed=0):
     return np.sort(np.concatenate([s, [0, T - 1]])).astype(np.int32)
 
 
+def _check_h_rows_per_block(d, ws, what):
+    """One real row of every 128-row block of the layer's h (its gate/up
+    GEMM with SiLU*up, in the workspace) against the oracle's grouped GEMM on
+    the oracle's own permutation (bit-exact with the layer's, checked
+    before): every row task of the persistent schedule is sampled."""
+    T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
+    idx, _ = _routing(d)
+    P = oracle.permute(idx, E)
+    r2p, m_pad = P["row_to_pair"], P["m_pad"]
+    rows = []
+    for b in range(m_pad // 128):
+        real = np.nonzero(r2p[b * 128:(b + 1) * 128] >= 0)[0]
+        rows.append(b * 128 + real[(b * 37) % len(real)])
+    rows = np.array(rows, np.int32)
+    h = moe.workspace_view(ws, T, H, E, k, I, "h")
+    got = to_f64(h[torch.from_numpy(rows).long().cuda()])
+    ref = oracle.grouped_gemm(d["x"], d["wg"], P["block_expert"], N=I, K=H, a_src_row=r2p, a_src_div=k,
+                              B2_bits=d["wu"], epilogue="silu_mul", rows=rows)
+    r = assert_close(got, ref, what + " h rows")
+    say("layer", what, "h: %d rows (one per block) max|err|/max|ref| %.2e  relFro %.2e" % ((len(rows),) + r))
+
+
 @pytest.mark.parametrize("name,n", [("tp_share", 96), ("ep_skew", 96), ("ep_skew_small", 128), ("prefill", 40)])
 def test_layer_full_size(name, n):
     d = syn.make_config(name)
-    _check_layer(d, tokens=_sample(d["T"], min(n, d["T"] - 2)), what=name)
+    _, ws, _ = _check_layer(d, tokens=_sample(d["T"], min(n, d["T"] - 2)), what=name)
+    _check_h_rows_per_block(d, ws, name)
 
 
 # ---------------------------------------------------------------- weighted-scatter combine

@@ -209,16 +209,18 @@ def test_layer_routing_permutation_and_plan(T, E, k):
     assert np.array_equal(plan[:used], plan_ref[:used])
 
 
-def test_permute_skips_invalid_ids():
+@pytest.mark.parametrize("T,k,E", [(700, 3, 8), (5000, 4, 37), (9000, 8, 64)])
+def test_permute_skips_invalid_ids(T, k, E):
     # expert ids outside [0, E) get no row; the valid pairs are still a stable
-    # counting sort (checked by its defining properties)
+    # counting sort (checked by its defining properties).  Up to 16384 pairs
+    # take the one-launch kernel, more the three-pass counting sort.
     g = np.random.default_rng(21)
-    T, k, E = 700, 3, 8
     idx = g.integers(0, E, size=(T, k)).astype(np.int32)
     idx[::7, 0] = -3
-    idx[::11, 2] = E
+    idx[::11, k - 1] = E
     idx[5, 1] = 1 << 20
-    say("permute invalid ids")
+    idx[T - 1, :] = -(1 << 30)
+    say("permute invalid ids", T, k, E)
     P = moe.permute(torch.from_numpy(idx).cuda(), E)
     torch.cuda.synchronize()
     flat = idx.ravel()
