@@ -44,6 +44,10 @@ def parse():
     p.add_argument("--config", default="tp_share")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    p.add_argument("--cpu-seconds-other", type=float, default=4.0,
+                   help="the same for each of the other workloads")
+    p.add_argument("--others", default="dense,ep_skew,ep_skew_small,prefill",
+                   help="other workloads measured in the same run (comma list; '' for none)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="instead of the layer, run a plain device copy of MIB MiB a few times "
                         "(reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -68,26 +72,54 @@ def main():
               "(collectives and sharding are out of scope); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
-    import moe_expert_grouped_amd as moe
     from moe_expert_grouped_amd import synthetic as syn
 
     torch.cuda.set_device(0)
     if a.calibrate_copy:
         calibrate_copy(a.calibrate_copy)
         return
-    cfg = syn.CONFIGS[a.config]
-    if cfg["kind"] == "dense":
-        bench_dense(a)
-        return
-    d = syn.make_config(a.config)
+    meta = run_meta(torch)
+    if syn.CONFIGS[a.config]["kind"] == "dense":
+        rec = bench_dense(a, headline=True)
+    else:
+        rec = bench_moe(a, a.config, headline=True)
+    others = [c for c in (a.others.split(",") if a.others else []) if c and c != a.config]
+    if others:
+        # every other workload, in the same run: layer (or GEMM) time, per-kernel
+        # times, the roofline of its dominant kernel and the oracle beside it
+        rec["configs"] = {}
+        for name in others:
+            print("[bench] %s" % name, file=sys.stderr, flush=True)
+            if syn.CONFIGS[name]["kind"] == "dense":
+                rec["configs"][name] = bench_dense(a, headline=False)
+            else:
+                rec["configs"][name] = bench_moe(a, name, headline=False)
+            torch.cuda.empty_cache()
+    meta["clocks_after"] = gpu_clocks()
+    rec["meta"] = meta
+    print(json.dumps(rec), flush=True)
+
+
+def bench_moe(a, name, headline):
+    """One MoE layer share: the whole step (moe_layer) timed, its kernels one
+    by one, the roofline of the gate/up GEMM and the oracle beside it.  The
+    headline workload also times the weighted-scatter combine, the graph-
+    replayed step, the plain weight layout and the short HBM-bound steps in
+    graph-captured batches."""
+    import torch
+    import moe_expert_grouped_amd as moe
+    from moe_expert_grouped_amd import synthetic as syn
+    cfg = syn.CONFIGS[name]
+    d = syn.make_config(name)
     T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
+    sha = input_sha256(d)
     dev16 = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
     x, wg, wu, wd = dev16(d["x"]), dev16(d["wg"]), dev16(d["wu"]), dev16(d["wd"])
     given = "logits" not in d
     logits = None if given else torch.from_numpy(d["logits"]).cuda()
     tidx = torch.from_numpy(d["topk_idx"]).cuda() if given else None
     tw = torch.from_numpy(d["topk_w"]).cuda() if given else None
-    ws = moe.layer_workspace(T, H, E, k, I)
+    ws = moe.layer_workspace(T, H, E, k, I, combine="scatter" if headline else "gather")
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     # gate and up weights interleaved in 128-column blocks, once, before any
     # timing (a weight-load transform: the gate/up GEMM then streams each k row
@@ -104,7 +136,7 @@ def main():
         moe.layer(x, wgu, wu_arg, wd, k, logits=logits, topk_idx=tidx, topk_w=tw, workspace=ws,
                   out=out)
 
-    settle_steps = settle(step, a.settle_ms)
+    settle_steps = settle(step, a.settle_ms if headline else a.settle_ms / 2)
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -115,6 +147,136 @@ def main():
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / a.steps
     stats = step_stats(step, a.steps)
+
+    # ---- per-kernel durations: HIP events on the launch stream around each
+    # kernel of the same path called step by step.  The GEMMs run on a plan
+    # built once beforehand (plan_ready), as inside moe_layer, where the
+    # permutation kernel writes it: each pair of events brackets one kernel.
+    stream = torch.cuda.current_stream()
+    names = ["route", "permute", "gate_up", "down", "combine"]
+    R = T * k
+    idx_t, w_t = (tidx, tw) if given else moe.route(logits, k)
+    P = moe.permute(idx_t, E)
+    gws = torch.empty(moe.load_library().grouped_gemm_workspace_size(P.cap), dtype=torch.uint8,
+                      device="cuda")
+    gu_kw = dict(N=I, K=H, cap=P.cap, a_src_row=P.row_to_pair, a_src_div=k, B2=wu_arg,
+                 epilogue="silu_mul", b_layout="kn_gate_up" if packed else "kn", b_stream=stream_w,
+                 workspace=gws)
+    dn_kw = dict(N=H, K=I, cap=P.cap, row_pair=P.row_to_pair, b_stream=stream_w, workspace=gws)
+    h = moe.grouped_gemm(x, wgu, P.block_expert, P.num_padded_rows, **gu_kw)  # builds the plan
+    y = moe.grouped_gemm(h, wd, P.block_expert, P.num_padded_rows, plan_ready=True, **dn_kw)
+    timed = []
+    for it in range(a.warmup + a.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        e[0].record(stream)
+        if not given:
+            moe.route(logits, k)
+        e[1].record(stream)
+        moe.permute(idx_t, E)
+        e[2].record(stream)
+        moe.grouped_gemm(x, wgu, P.block_expert, P.num_padded_rows, out=h, plan_ready=True, **gu_kw)
+        e[3].record(stream)
+        moe.grouped_gemm(h, wd, P.block_expert, P.num_padded_rows, out=y, plan_ready=True, **dn_kw)
+        e[4].record(stream)
+        moe.combine(y, P.pair_to_row, w_t, out=out)
+        e[5].record(stream)
+        if it >= a.warmup:
+            timed.append(e)
+    torch.cuda.synchronize()
+    per = {n: np.array([es[i].elapsed_time(es[i + 1]) for es in timed]) * 1e3
+           for i, n in enumerate(names)}
+    # medians (a stalled host iteration would otherwise move the mean) and means
+    dur = {n: float(np.median(v)) for n, v in per.items()}
+    mean = {n: float(np.mean(v)) for n, v in per.items()}
+    m_pad = int(P.num_padded_rows.item())
+    counts = P.counts.cpu().numpy()
+    e_act = int((counts > 0).sum())
+
+    # ---- algorithmic work
+    gemm_flops = 6.0 * R * H * I
+    gu_flops = 4.0 * R * H * I
+    gu_bytes = 4.0 * e_act * H * I + 2.0 * T * H + 2.0 * R * I      # weights, x, h
+    dn_bytes = 2.0 * e_act * I * H + 2.0 * R * I + 2.0 * R * H      # weights, h, y
+    comb_bytes = 2.0 * R * H + 2.0 * T * H                          # y rows read, out written
+    layer_s = ms * 1e-3
+    gemm_s = (dur["gate_up"] + dur["down"]) * 1e-6
+    # the roofline of the dominant kernel, the gate/up GEMM: HBM-bound where
+    # its FLOPs per byte stay under the ridge (peak FLOP/s / peak bytes/s)
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    gu_us = mean["gate_up"]
+    if gu_flops / gu_bytes < ridge:
+        roof = {"bound": "hbm", "achieved": round(gu_bytes / (gu_us * 1e-6) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "algorithmic_bytes": gu_bytes}
+    else:
+        roof = {"bound": "mfma", "achieved": round(gu_flops / (gu_us * 1e-6) / 1e12, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "algorithmic_flops": gu_flops}
+    roof = {"kernel": "grouped_gemm gate/up (SiLU*up epilogue), the GEMM kernel alone", **roof,
+            "frac": round(roof["achieved"] / roof["peak"], 4),
+            "duration_us": round(gu_us, 2), "duration_median_us": round(dur["gate_up"], 2),
+            "launches": len(timed),
+            "traffic": recorded_traffic("grouped_gemm_gate_up_%s" % name)}
+
+    rec = {
+        "metric": "MoE layer us + grouped-GEMM TFLOP/s (% bf16 MFMA peak), T=2048 H=4096 E=64",
+        "value": round(gemm_flops / layer_s / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup, "settle_steps": settle_steps,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s MoE layer share" % name, "T": T, "H": H, "E": E, "top_k": k,
+                   "I": I, "routing": cfg.get("routing"), "m_pad": m_pad, "active_experts": e_act,
+                   "gate_up_weights": ("interleaved in 128-column blocks (moe_pack_gate_up, once "
+                                       "before timing)") if packed else "separate [E][H][I]",
+                   "weight_loads": "non-temporal" if stream_w else "default"},
+        "layer_us": round(ms * 1e3, 2),
+        "gemm_tflops": round(gemm_flops / gemm_s / 1e12, 2),
+        "gemm_mfma_peak_frac": round(gemm_flops / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernel_us": {n: round(v, 2) for n, v in dur.items()},
+        "kernel_us_mean": {n: round(v, 2) for n, v in mean.items()},
+        "layer_us_per_step": stats,
+        "roofline": roof,
+        "input_sha256": sha,
+    }
+    hbm = [("gate_up", dur["gate_up"], gu_bytes), ("down", dur["down"], dn_bytes),
+           ("combine", dur["combine"], comb_bytes)]
+    if headline:
+        rec.update(moe_headline_legs(a, d, locals()))
+        hbm = [hbm[0], hbm[1], ("combine", rec["kernel_us_batched"]["combine"], comb_bytes),
+               ("gather", rec["kernel_us_batched"]["gather"], 2.0 * T * H + 2.0 * m_pad * H),
+               ("router", rec["kernel_us_batched"]["router"], 2.0 * T * H + 2.0 * E * H + 8.0 * T * k)]
+    rec["hbm_gbs"] = {
+        n: {"us": round(us, 2), "algorithmic_bytes": b, "gbs": round(b / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)} for n, us, b in hbm}
+    wr_bits = rec.pop("_wr_bits", None)
+    if a.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(d, a.cpu_seconds if headline else a.cpu_seconds_other)
+        if wr_bits is not None:
+            rec["cpu_baseline_router"] = cpu_router_baseline(d["x"], wr_bits, k)
+    if not headline:
+        for key in ("metric", "n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline",
+                    "data"):
+            rec.pop(key)
+    return rec
+
+
+def moe_headline_legs(a, d, v):
+    """The extra legs of the headline workload: the weighted-scatter combine,
+    the graph-replayed step, the plain gate/up weight layout, and the combine,
+    permutation, row gather and router front end in graph-captured batches."""
+    import torch
+    import moe_expert_grouped_amd as moe
+    from moe_expert_grouped_amd import synthetic as syn
+    T, H, E, k = d["T"], d["H"], d["E"], d["k"]
+    x, wg, wu, wd, wgu, wu_arg = v["x"], v["wg"], v["wu"], v["wd"], v["wgu"], v["wu_arg"]
+    logits, tidx, tw, ws, out, step = v["logits"], v["tidx"], v["tw"], v["ws"], v["out"], v["step"]
+    P, h, y, idx_t, w_t, dn_kw = v["P"], v["h"], v["y"], v["idx_t"], v["w_t"], v["dn_kw"]
+    stream = torch.cuda.current_stream()
 
     def step_scatter():
         moe.layer(x, wgu, wu_arg, wd, k, logits=logits, topk_idx=tidx, topk_w=tw, workspace=ws,
@@ -138,6 +300,7 @@ def main():
     for _ in range(a.warmup):
         graph.replay()
     stats_graph = step_stats(graph.replay, a.steps, cold=False)
+    del graph
 
     def step_unpacked():
         moe.layer(x, wg, wu, wd, k, logits=logits, topk_idx=tidx, topk_w=tw, workspace=ws, out=out)
@@ -146,40 +309,7 @@ def main():
         step_unpacked()
     stats_unpacked = step_stats(step_unpacked, a.steps, cold=False)
 
-    # ---- per-kernel durations: HIP events on the launch stream, same path step by step
-    stream = torch.cuda.current_stream()
-    names = ["route", "permute", "gate_up", "down", "combine", "permute_gather"]
-    timed = []
-    R = T * k
-    idx_t, w_t = (tidx, tw) if given else (None, None)
-    for it in range(a.warmup + a.steps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
-        e[0].record(stream)
-        if not given:
-            idx_t, w_t = moe.route(logits, k)
-        e[1].record(stream)
-        P = moe.permute(idx_t, E)
-        e[2].record(stream)
-        h = moe.grouped_gemm(x, wgu, P.block_expert, P.num_padded_rows, N=I, K=H, cap=P.cap,
-                             a_src_row=P.row_to_pair, a_src_div=k, B2=wu_arg, epilogue="silu_mul",
-                             b_layout="kn_gate_up" if packed else "kn", b_stream=stream_w)
-        e[3].record(stream)
-        y = moe.grouped_gemm(h, wd, P.block_expert, P.num_padded_rows, N=H, K=I, cap=P.cap,
-                             row_pair=P.row_to_pair, b_stream=stream_w)
-        e[4].record(stream)
-        moe.combine(y, P.pair_to_row, w_t, out=out)
-        e[5].record(stream)
-        # the permutation with the optional row gather (x_perm), HBM-bound
-        moe.permute(idx_t, E, x=x)
-        e[6].record(stream)
-        if it >= a.warmup:
-            timed.append(e)
-    torch.cuda.synchronize()
-    # medians: a stalled host iteration (the GPU idles waiting for a launch)
-    # would otherwise move the mean
-    dur = {n: float(np.median([es[i].elapsed_time(es[i + 1]) for es in timed]))
-           for i, n in enumerate(names)}
-    # the weighted-scatter down GEMM and its finalize, same inputs
+    # the weighted-scatter down GEMM (alone, on the plan built before) and its finalize
     acc = torch.empty((T, H), dtype=torch.float32, device="cuda")
     sc = []
     for it in range(a.warmup + a.steps):
@@ -187,9 +317,8 @@ def main():
         e[0].record(stream)
         acc.zero_()
         e[1].record(stream)
-        moe.grouped_gemm(h, wd, P.block_expert, P.num_padded_rows, N=H, K=I, cap=P.cap,
-                         epilogue="weighted_scatter", row_pair=P.row_to_pair, pair_w=w_t, out=acc,
-                         b_stream=stream_w)
+        moe.grouped_gemm(h, wd, P.block_expert, P.num_padded_rows, epilogue="weighted_scatter",
+                         pair_w=w_t, out=acc, plan_ready=True, **dn_kw)
         e[2].record(stream)
         moe.finalize(acc, out=out)
         e[3].record(stream)
@@ -198,12 +327,11 @@ def main():
     torch.cuda.synchronize()
     dur_sc = {n: float(np.median([es[i].elapsed_time(es[i + 1]) for es in sc]))
               for i, n in enumerate(["zero", "down_scatter", "finalize"])}
-    # the short HBM-bound entry points once more, without the event packets
-    # between kernels that the step-by-step medians above include: a.steps
-    # calls captured back to back in one HIP graph, replayed between two HIP
-    # events.  The combine's y and the gather's x_perm rotate over enough
-    # buffers (400 MB, 308 MB) that none is still in the 256 MB Infinity Cache
-    # when it is read or rewritten, so the rates are HBM rates.
+    # the short HBM-bound entry points without event packets between kernels:
+    # a.steps calls captured back to back in one HIP graph, replayed between
+    # two HIP events.  The combine's y and the gather's x_perm rotate over
+    # enough buffers (400 MB, 308 MB) that none is still in the 256 MB
+    # Infinity Cache when it is read or rewritten, so the rates are HBM rates.
     out_b = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ys = [y.clone() for _ in range(4)]
     xps = [torch.empty((P.cap, H), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
@@ -232,87 +360,26 @@ def main():
     batched["router"] = graph_batch_us(lambda: moe.router(x, wr, k, workspace=rws), a.steps)
     # the row gather alone: the permutation with it minus the permutation
     batched["gather"] = batched["permute_with_gather"] - batched["permute"]
-    m_pad = int(P.num_padded_rows.item())
-    counts = P.counts.cpu().numpy()
-    e_act = int((counts > 0).sum())
-
-    # ---- algorithmic work
-    gemm_flops = 6.0 * R * H * I
-    gu_bytes = 4.0 * e_act * H * I + 2.0 * T * H + 2.0 * R * I      # weights, x, h
-    comb_bytes = 2.0 * R * H + 2.0 * T * H                          # y rows read, out written
-    gath_bytes = 2.0 * T * H + 2.0 * m_pad * H                      # x read once, x_perm written
-    router_bytes = 2.0 * T * H + 2.0 * E * H + 8.0 * T * k          # x, W_r, the routing
-    dn_bytes = 2.0 * e_act * I * H + 2.0 * R * I + 2.0 * R * H      # weights, h, y
-    layer_s = ms * 1e-3
-    gemm_s = (dur["gate_up"] + dur["down"]) * 1e-3
-    gu_s = dur["gate_up"] * 1e-3
-    achieved_gbs = gu_bytes / gu_s / 1e9
-
-    traffic = recorded_traffic("grouped_gemm_gate_up_%s" % a.config)
-
-    rec = {
-        "metric": "MoE layer us + grouped-GEMM TFLOP/s (% bf16 MFMA peak), T=2048 H=4096 E=64",
-        "value": round(gemm_flops / layer_s / 1e12, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup, "settle_steps": settle_steps,
-        "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "%s MoE layer share" % a.config, "T": T, "H": H, "E": E, "top_k": k,
-                   "I": I, "routing": cfg.get("routing"), "m_pad": m_pad, "active_experts": e_act,
-                   "gate_up_weights": ("interleaved in 128-column blocks (moe_pack_gate_up, once "
-                                       "before timing)") if packed else "separate [E][H][I]",
-                   "weight_loads": "non-temporal" if stream_w else "default"},
-        "layer_us": round(ms * 1e3, 2),
-        "gemm_tflops": round(gemm_flops / gemm_s / 1e12, 2),
-        "gemm_mfma_peak_frac": round(gemm_flops / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "kernel_us": {n: round(v * 1e3, 2) for n, v in dur.items()},
-        "kernel_us_batched": {n: round(v, 2) for n, v in batched.items()},
-        "hbm_gbs": {
-            n: {"us": round(us, 2), "algorithmic_bytes": b,
-                "gbs": round(b / (us * 1e-6) / 1e9, 1),
-                "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-            for n, us, b in (("gate_up", dur["gate_up"] * 1e3, gu_bytes),
-                             ("down", dur["down"] * 1e3, dn_bytes),
-                             ("combine", batched["combine"], comb_bytes),
-                             ("gather", batched["gather"], gath_bytes),
-                             ("router", batched["router"], router_bytes))},
-        "layer_us_per_step": stats,
+    del ys, xps
+    return {
+        "kernel_us_batched": {n: round(t, 2) for n, t in batched.items()},
         "hip_graph": {"layer_us_per_step": stats_graph},
         "unpacked_gate_up_weights": {"layer_us_per_step": stats_unpacked},
         "scatter_combine": {"layer_us_per_step": stats_scatter,
-                            "kernel_us": {n: round(v * 1e3, 2) for n, v in dur_sc.items()}},
+                            "kernel_us": {n: round(t * 1e3, 2) for n, t in dur_sc.items()}},
         "measured_peaks": measured_peaks(),
-        "roofline": {
-            "kernel": "grouped_gemm gate/up (SiLU*up epilogue)",
-            "bound": "hbm",
-            "achieved": round(achieved_gbs, 1),
-            "duration_us": round(dur["gate_up"] * 1e3, 2),
-            "algorithmic_bytes": gu_bytes,
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
-            "traffic": traffic,
-        },
+        "_wr_bits": wr_bits,
     }
-    if a.cpu_seconds > 0:
-        rec["cpu_baseline"] = cpu_baseline(d, a.cpu_seconds)
-        rec["cpu_baseline_router"] = cpu_router_baseline(d["x"], wr_bits, k)
-    print(json.dumps(rec), flush=True)
 
 
-def bench_dense(a):
+def bench_dense(a, headline):
     """The degenerate one-group case: D = A . B^T, fp16 4096^3 (B stored [N][K])."""
     import torch
     import moe_expert_grouped_amd as moe
     from moe_expert_grouped_amd import synthetic as syn
     d = syn.make_config("dense")
     M, N, K = d["M"], d["N"], d["K"]
+    sha = input_sha256(d)
     dev16 = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.float16).cuda()
     A, B = dev16(d["A"]), dev16(d["B"])
     bg = torch.zeros(M // 128, dtype=torch.int32, device="cuda")
@@ -323,34 +390,93 @@ def bench_dense(a):
     def step():
         moe.grouped_gemm(A, B, bg, nr, N=N, K=K, cap=M, b_layout="nk", out=D, workspace=ws)
 
-    settle_steps = settle(step, a.settle_ms)
+    settle_steps = settle(step, a.settle_ms if headline else a.settle_ms / 2)
     for _ in range(a.warmup):
         step()
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record(stream)
     for _ in range(a.steps):
         step()
-    e1.record(stream)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / a.steps
-    kern_ms = e0.elapsed_time(e1) / a.steps
+    # the GEMM kernel alone (its plan built by the calls above), per launch
+    ev = []
+    for it in range(a.warmup + a.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        moe.grouped_gemm(A, B, bg, nr, N=N, K=K, cap=M, b_layout="nk", out=D, workspace=ws,
+                         plan_ready=True)
+        e1.record(stream)
+        if it >= a.warmup:
+            ev.append((e0, e1))
+    torch.cuda.synchronize()
+    us = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e3
+    kern_us = float(np.mean(us))
     flops = 2.0 * M * N * K
-    tf = flops / (kern_ms * 1e-3) / 1e12
-    print(json.dumps({
+    tf = flops / (kern_us * 1e-6) / 1e12
+    rec = {
         "metric": "dense fp16 GEMM D = A.B^T (one-group grouped_gemm)", "value": round(tf, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "settle_steps": settle_steps,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp16", "data": "synthetic",
         "config": {"workload": "dense fp16 GEMM M=N=K=4096, D = A.B^T, fp32 accumulate"},
-        "kernel_us": round(kern_ms * 1e3, 2),
-        "roofline": {"kernel": "grouped_gemm (one group, B [N][K], fp16)", "bound": "mfma",
-                     "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
-        **({"cpu_baseline": cpu_dense_baseline(d, a.cpu_seconds)} if a.cpu_seconds > 0 else {}),
-    }), flush=True)
+        "step_us": round(ms * 1e3, 2),
+        "kernel_us": round(kern_us, 2), "kernel_us_median": round(float(np.median(us)), 2),
+        "roofline": {"kernel": "grouped_gemm (one group, B [N][K], fp16), the GEMM kernel alone",
+                     "bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "duration_us": round(kern_us, 2), "algorithmic_flops": flops, "launches": len(us),
+                     "traffic": None},
+        "input_sha256": sha,
+    }
+    if a.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_dense_baseline(d, a.cpu_seconds if headline else a.cpu_seconds_other)
+    if not headline:
+        for key in ("metric", "n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline",
+                    "data"):
+            rec.pop(key)
+    return rec
+
+
+def input_sha256(d):
+    """SHA-256 of every input array of a workload (numpy does not promise the
+    same Generator streams across versions: the hashes name the bits)."""
+    import hashlib
+    out = {}
+    for n, v in d.items():
+        if isinstance(v, np.ndarray):
+            out[n] = hashlib.sha256(memoryview(np.ascontiguousarray(v)).cast("B")).hexdigest()
+    return out
+
+
+def gpu_clocks():
+    """Current clock levels and power of the GPU as rocm-smi reports them
+    (the clocks are recorded, not locked); None where the tool is missing."""
+    import subprocess
+    cmd = ["rocm-smi", "--showclocks", "--showpower", "--showmaxpower", "--json"]
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    if r.returncode != 0 or not r.stdout.strip():
+        return None
+    try:
+        js = json.loads(r.stdout)
+    except ValueError:
+        return None
+    cards = sorted(c for c in js if c.startswith("card"))
+    return {"tool": "rocm-smi", "card": cards[0] if cards else None,
+            "values": js[cards[0]] if cards else js}
+
+
+def run_meta(torch):
+    import platform
+    p = torch.cuda.get_device_properties(0)
+    return {"numpy": np.__version__, "torch": torch.__version__, "hip": torch.version.hip,
+            "device": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
+            "host_cpu": platform.processor() or platform.machine(),
+            "host_threads": len(os.sched_getaffinity(0)), "clocks_before": gpu_clocks()}
 
 
 CSRC = os.path.join(ROOT, "moe_expert_grouped_amd", "csrc")

@@ -254,14 +254,20 @@ int grouped_gemm(int dtype, int N, int K, int cap, const void *A,
  *   grid  persistent workgroups, 0 = one per compute unit (the product
  *         choice); a smaller grid gives each workgroup more tasks, which
  *         the result does not depend on.  0 <= grid <= 65535.
+ *   flags MOE_TUNED_PLAN_READY: the workspace already holds the row-task
+ *         plan of this block_group and num_rows, built by an earlier
+ *         grouped_gemm call ordered before this one (the plan depends on
+ *         nothing else); only the GEMM kernel is launched, so it can be
+ *         timed alone.  0 otherwise.
  * ---------------------------------------------------------------------- */
+#define MOE_TUNED_PLAN_READY 1
 int grouped_gemm_tuned(int dtype, int N, int K, int cap, const void *A,
                        const int32_t *a_src_row, int a_src_div, const void *B,
                        const void *B2, int b_layout, const int32_t *block_group,
                        const int32_t *num_rows, int epilogue,
                        const int32_t *epi_row_pair, const float *pair_w, int k,
-                       void *D, const int32_t *tile, int grid, void *workspace,
-                       size_t ws_bytes, void *stream);
+                       void *D, const int32_t *tile, int grid, int flags,
+                       void *workspace, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * moe_combine -- top-k weighted reduction back to token order.    [P2 s.4]

@@ -71,8 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "moe_permute": ([P, I, I, I, P, I, P, P, P, P, P, P, P, I, P, Z, P], I),
             "grouped_gemm_workspace_size": ([I], Z),
             "grouped_gemm": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P, I, P, P, Z, P], I),
-            "grouped_gemm_tuned": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P, I, P, P, I, P, Z, P],
-                                   I),
+            "grouped_gemm_tuned": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P, I, P, P, I, I, P, Z,
+                                    P], I),
             "moe_combine": ([P, I, P, P, I, I, P, P], I),
             "moe_finalize": ([P, Z, P, P], I),
             "moe_pack_gate_up": ([P, P, I, I, I, P, P], I),
@@ -222,7 +222,7 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
                  row_pair: torch.Tensor | None = None, pair_w: torch.Tensor | None = None,
                  T: int | None = None, out: torch.Tensor | None = None,
                  workspace: torch.Tensor | None = None, b_stream: bool = False,
-                 tile: tuple | None = None, grid: int = 0) -> torch.Tensor:
+                 tile: tuple | None = None, grid: int = 0, plan_ready: bool = False) -> torch.Tensor:
     """D[r] = A[a(r)] . B[block_group[r // 128]] for r < min(num_rows, cap),
     or SiLU(A.B) * (A.B2) with epilogue="silu_mul".  Returns D [cap, N].
 
@@ -246,7 +246,9 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
     (columns per task, k per slice, A ring depth, B ring depth, row tasks per
     super-block, wavefronts) of an instantiated configuration, grid the
     number of persistent workgroups (0: one per compute unit).  The defaults
-    are the library's own choice."""
+    are the library's own choice.  plan_ready=True: `workspace` already
+    holds the row-task plan of this block_group / num_rows from an earlier
+    call on the stream, so only the GEMM kernel runs (to time it alone)."""
     _need(A, "A", (torch.bfloat16, torch.float16))
     _need(B, "B", A.dtype)
     _need(block_group, "block_group", torch.int32)
@@ -281,7 +283,7 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
             _LAYOUTS[b_layout] | (MOE_B_STREAM if b_stream else 0), _ptr(block_group),
             _ptr(num_rows), _EPIS[epilogue], _ptr(row_pair), _ptr(pair_w), k, _ptr(out))
     ws = (_ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
-    if tile is None and not grid:
+    if tile is None and not grid and not plan_ready:
         _check("grouped_gemm", lib.grouped_gemm(*args, *ws))
     else:
         t = None
@@ -289,7 +291,8 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
             if len(tile) != 6:
                 raise ValueError("tile must have 6 entries")
             t = (ctypes.c_int32 * 6)(*[int(v) for v in tile])
-        _check("grouped_gemm_tuned", lib.grouped_gemm_tuned(*args, t, int(grid), *ws))
+        _check("grouped_gemm_tuned",
+               lib.grouped_gemm_tuned(*args, t, int(grid), 1 if plan_ready else 0, *ws))
     return out
 
 

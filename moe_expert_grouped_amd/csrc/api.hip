@@ -202,8 +202,8 @@ int gemm_enqueue(int dtype, int N, int K, int cap, const void *A, const int32_t 
                  int a_src_div, const void *B, const void *B2, int b_layout, bool b_stream,
                  const int32_t *block_group, const int32_t *num_rows, int epilogue,
                  const int32_t *epi_row_pair, const float *pair_w, int k, void *D, int32_t *plan,
-                 const int32_t *tile, int grid, hipStream_t s) {
-  if (moe::launch_gg_plan(block_group, num_rows, cap, plan, s) != hipSuccess)
+                 const int32_t *tile, int grid, hipStream_t s, bool plan_ready = false) {
+  if (!plan_ready && moe::launch_gg_plan(block_group, num_rows, cap, plan, s) != hipSuccess)
     return MOE_ERR_DEVICE;
   return launch_status(moe::launch_grouped_gemm(
       dtype, N, K, (const uint16_t *)A, a_src_row, a_src_div, (const uint16_t *)B,
@@ -222,20 +222,21 @@ int grouped_gemm(int dtype, int N, int K, int cap, const void *A, const int32_t 
                  void *workspace, size_t ws_bytes, void *stream) {
   return grouped_gemm_tuned(dtype, N, K, cap, A, a_src_row, a_src_div, B, B2, b_layout,
                             block_group, num_rows, epilogue, epi_row_pair, pair_w, k, D, nullptr,
-                            0, workspace, ws_bytes, stream);
+                            0, 0, workspace, ws_bytes, stream);
 }
 
 int grouped_gemm_tuned(int dtype, int N, int K, int cap, const void *A, const int32_t *a_src_row,
                        int a_src_div, const void *B, const void *B2, int b_layout,
                        const int32_t *block_group, const int32_t *num_rows, int epilogue,
                        const int32_t *epi_row_pair, const float *pair_w, int k, void *D,
-                       const int32_t *tile, int grid, void *workspace, size_t ws_bytes,
-                       void *stream) {
+                       const int32_t *tile, int grid, int flags, void *workspace,
+                       size_t ws_bytes, void *stream) {
   bool b_stream = false;
   int st = check_gemm(dtype, N, K, cap, A, a_src_row, a_src_div, B, B2, b_layout, b_stream,
                       block_group, num_rows, epilogue, epi_row_pair, pair_w, k, D);
   if (st != MOE_OK) return st;
   if (grid < 0 || grid > 65535) return MOE_ERR_INVALID;
+  if (flags & ~MOE_TUNED_PLAN_READY) return MOE_ERR_INVALID;
   if (tile) {
     if (!moe::gg_tile_usable(tile, epilogue, N, K)) return MOE_ERR_UNSUPPORTED;
     // the interleaved gate/up layout needs column tiles inside 128-column blocks
@@ -248,7 +249,8 @@ int grouped_gemm_tuned(int dtype, int N, int K, int cap, const void *A, const in
   if (cus == 0) return MOE_ERR_DEVICE;
   return gemm_enqueue(dtype, N, K, cap, A, a_src_row, a_src_div, B, B2, b_layout, b_stream,
                       block_group, num_rows, epilogue, epi_row_pair, pair_w, k, D,
-                      (int32_t *)workspace, tile, grid > 0 ? grid : cus, (hipStream_t)stream);
+                      (int32_t *)workspace, tile, grid > 0 ? grid : cus, (hipStream_t)stream,
+                      (flags & MOE_TUNED_PLAN_READY) != 0);
 }
 
 int moe_pack_gate_up(const void *w_gate, const void *w_up, int E, int K, int N, void *out,

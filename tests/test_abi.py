@@ -169,10 +169,12 @@ def test_grouped_gemm_validation(lib):
 def test_grouped_gemm_tuned_validation(lib):
     # the explicit launch shape of tests and sweeps: an instantiated tile that
     # fits the shape, or MOE_ERR_UNSUPPORTED (never a silent fallback)
-    def call(tile=None, grid=0, N=512, K=256, epi=0, lay=0, B2=NULL, wsb=1 << 20):
+    def call(tile=None, grid=0, N=512, K=256, epi=0, lay=0, B2=NULL, wsb=1 << 20, flags=0):
         t = None if tile is None else (ctypes.c_int32 * 6)(*tile)
         return lib.grouped_gemm_tuned(0, N, K, 256, FAKE, NULL, 1, FAKE, B2, lay, FAKE, FAKE, epi, NULL,
-                                      NULL, 0, FAKE, t, grid, FAKE, wsb, NULL)
+                                      NULL, 0, FAKE, t, grid, flags, FAKE, wsb, NULL)
+    assert call(flags=1) == moe.MOE_ERR_DEVICE                          # plan ready; no GPU here
+    assert call(flags=2) == moe.MOE_ERR_INVALID
     assert call(tile=(256, 32, 3, 6, 1, 8)) == moe.MOE_ERR_DEVICE      # valid; no GPU here
     assert call(tile=(256, 32, 3, 6, 1, 8), grid=8) == moe.MOE_ERR_DEVICE
     assert call(grid=-1) == moe.MOE_ERR_INVALID
