@@ -222,6 +222,29 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, const void *x,
 size_t grouped_gemm_workspace_size(int cap);
 
 /* ------------------------------------------------------------------------
+ * grouped_gemm_noalloc -- grouped_gemm without a workspace, for callers that
+ * cannot allocate device memory or pass scratch: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same operation, arguments, limits and results as grouped_gemm; the
+ * row-task plan it builds goes to a fixed array the library holds on each
+ * GPU it runs on (about 64 KiB, kept until the process ends) instead of a
+ * workspace.  It calls no allocating routine.
+ *   cap <= MOE_NOALLOC_MAX_CAP rows (MOE_ERR_WORKSPACE otherwise).
+ * Every call on one GPU uses that GPU's one array: calls that may overlap
+ * on one GPU (different streams, without ordering between them) race and
+ * must not be made; calls ordered on one stream are safe.  The array keeps
+ * the last call's plan; each call rewrites every entry it reads, so nothing
+ * needs clearing between calls.
+ * ---------------------------------------------------------------------- */
+#define MOE_NOALLOC_MAX_CAP (1 << 20)
+int grouped_gemm_noalloc(int dtype, int N, int K, int cap, const void *A,
+                         const int32_t *a_src_row, int a_src_div,
+                         const void *B, const void *B2, int b_layout,
+                         const int32_t *block_group, const int32_t *num_rows,
+                         int epilogue, const int32_t *epi_row_pair,
+                         const float *pair_w, int k, void *D, void *stream);
+
+/* ------------------------------------------------------------------------
  * moe_pack_gate_up -- the MOE_B_KN_GATE_UP weight layout from separate gate
  * and up weights (a one-time weight transform, like loading a checkpoint
  * into the layout the GEMM streams best; no arithmetic).

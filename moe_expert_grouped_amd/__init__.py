@@ -73,6 +73,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "grouped_gemm": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P, I, P, P, Z, P], I),
             "grouped_gemm_tuned": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P, I, P, P, I, I, P, Z,
                                     P], I),
+            "grouped_gemm_noalloc": ([I, I, I, I, P, P, I, P, P, I, P, P, I, P, P, I, P, P], I),
             "moe_combine": ([P, I, P, P, I, I, P, P], I),
             "moe_finalize": ([P, Z, P, P], I),
             "moe_pack_gate_up": ([P, P, I, I, I, P, P], I),
@@ -221,7 +222,7 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
                  B2: torch.Tensor | None = None, b_layout: str = "kn", epilogue: str = "store",
                  row_pair: torch.Tensor | None = None, pair_w: torch.Tensor | None = None,
                  T: int | None = None, out: torch.Tensor | None = None,
-                 workspace: torch.Tensor | None = None, b_stream: bool = False,
+                 workspace: torch.Tensor | str | None = None, b_stream: bool = False,
                  tile: tuple | None = None, grid: int = 0, plan_ready: bool = False) -> torch.Tensor:
     """D[r] = A[a(r)] . B[block_group[r // 128]] for r < min(num_rows, cap),
     or SiLU(A.B) * (A.B2) with epilogue="silu_mul".  Returns D [cap, N].
@@ -279,9 +280,16 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, block_group: torch.Tensor,
     lib = load_library()
     if workspace is None:
         workspace = gemm_workspace(cap, A.device)
+    # workspace="none": grouped_gemm_noalloc, the plan in the library's own
+    # per-GPU array (no scratch from the caller)
     args = (_DTYPES[A.dtype], N, K, cap, _ptr(A), _ptr(a_src_row), a_src_div, _ptr(B), _ptr(B2),
             _LAYOUTS[b_layout] | (MOE_B_STREAM if b_stream else 0), _ptr(block_group),
             _ptr(num_rows), _EPIS[epilogue], _ptr(row_pair), _ptr(pair_w), k, _ptr(out))
+    if isinstance(workspace, str):
+        if workspace != "none" or tile is not None or grid or plan_ready:
+            raise ValueError('workspace="none" takes the default launch shape')
+        _check("grouped_gemm_noalloc", lib.grouped_gemm_noalloc(*args, _stream()))
+        return out
     ws = (_ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
     if tile is None and not grid and not plan_ready:
         _check("grouped_gemm", lib.grouped_gemm(*args, *ws))

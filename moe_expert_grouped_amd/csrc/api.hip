@@ -59,6 +59,27 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
+// The row-task plan of grouped_gemm_noalloc lives here instead of in a
+// caller workspace: one copy per GPU, held until the process ends, shared by
+// every call on that GPU.  In host code `scratch` names a host-side stand-in,
+// not device memory: kernels get the device address looked up below.
+__device__ __align__(256) int32_t scratch[2 + 2 * (MOE_NOALLOC_MAX_CAP / MOE_ROW_BLOCK)];
+int32_t *g_scratch[kMaxDevices]; // device address of `scratch`, per device
+
+// Device address of this device's `scratch`, looked up once per device with
+// that device current; NULL if the lookup fails.
+int32_t *scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = (int32_t *)p;
+  }
+  return g_scratch[dev];
+}
+
 int check_route(const float *logits, int T, int E, int k, const int32_t *idx, const float *w) {
   if (!logits || !idx || !w) return MOE_ERR_INVALID;
   if (T <= 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID;
@@ -251,6 +272,27 @@ int grouped_gemm_tuned(int dtype, int N, int K, int cap, const void *A, const in
                       block_group, num_rows, epilogue, epi_row_pair, pair_w, k, D,
                       (int32_t *)workspace, tile, grid > 0 ? grid : cus, (hipStream_t)stream,
                       (flags & MOE_TUNED_PLAN_READY) != 0);
+}
+
+int grouped_gemm_noalloc(int dtype, int N, int K, int cap, const void *A,
+                         const int32_t *a_src_row, int a_src_div, const void *B, const void *B2,
+                         int b_layout, const int32_t *block_group, const int32_t *num_rows,
+                         int epilogue, const int32_t *epi_row_pair, const float *pair_w, int k,
+                         void *D, void *stream) {
+  bool b_stream = false;
+  int st = check_gemm(dtype, N, K, cap, A, a_src_row, a_src_div, B, B2, b_layout, b_stream,
+                      block_group, num_rows, epilogue, epi_row_pair, pair_w, k, D);
+  if (st != MOE_OK) return st;
+  if (cap > MOE_NOALLOC_MAX_CAP) return MOE_ERR_WORKSPACE;
+  const int cus = device_cus();
+  if (cus == 0) return MOE_ERR_DEVICE;
+  int32_t *plan = scratch_ptr();
+  if (!plan) return MOE_ERR_DEVICE;
+  // the plan kernel writes every plan entry the GEMM reads: nothing left by
+  // an earlier call needs clearing
+  return gemm_enqueue(dtype, N, K, cap, A, a_src_row, a_src_div, B, B2, b_layout, b_stream,
+                      block_group, num_rows, epilogue, epi_row_pair, pair_w, k, D, plan, nullptr,
+                      cus, (hipStream_t)stream);
 }
 
 int moe_pack_gate_up(const void *w_gate, const void *w_up, int E, int K, int N, void *out,

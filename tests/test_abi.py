@@ -28,9 +28,10 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in ["moe_route", "moe_router", "moe_permute", "grouped_gemm", "grouped_gemm_tuned", "moe_combine",
-              "moe_finalize", "moe_layer", "moe_layer_ex", "moe_pack_gate_up", "moe_layer_workspace_size_ex"]:
+              "moe_finalize", "moe_layer", "moe_layer_ex", "moe_pack_gate_up", "moe_layer_workspace_size_ex",
+              "grouped_gemm_noalloc"]:
         assert n in names
     for n in names:
         assert hasattr(lib, n), "missing export " + n
@@ -188,6 +189,20 @@ def test_grouped_gemm_tuned_validation(lib):
     assert call(tile=(256, 32, 3, 6, 1, 8), epi=1, B2=FAKE) == moe.MOE_ERR_UNSUPPORTED  # SiLU*up: 128 max
     assert call(tile=(64, 32, 3, 10, 1, 4), epi=1, lay=2) == moe.MOE_ERR_DEVICE
     assert call(wsb=8) == moe.MOE_ERR_WORKSPACE
+
+
+def test_grouped_gemm_noalloc_validation(lib):
+    # the same checks as grouped_gemm, no workspace; the plan array holds up
+    # to MOE_NOALLOC_MAX_CAP rows
+    def call(cap=256, A=FAKE, epi=0, B2=NULL, lay=0):
+        return lib.grouped_gemm_noalloc(0, 128, 128, cap, A, NULL, 1, FAKE, B2, lay, FAKE, FAKE, epi, NULL,
+                                        NULL, 0, FAKE, NULL)
+    assert call() == moe.MOE_ERR_DEVICE                      # valid; no GPU here
+    assert call(cap=1 << 20) == moe.MOE_ERR_DEVICE
+    assert call(cap=(1 << 20) + 128) == moe.MOE_ERR_WORKSPACE
+    assert call(A=NULL) == moe.MOE_ERR_INVALID
+    assert call(epi=1) == moe.MOE_ERR_INVALID               # SiLU*up needs B2
+    assert call(lay=1 | moe.MOE_B_STREAM) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_pack_gate_up_validation(lib):
