@@ -357,7 +357,20 @@ def moe_headline_legs(a, d, v):
     wr = torch.from_numpy(wr_bits.view(np.int16)).view(torch.bfloat16).cuda()
     rws = torch.empty(max(moe.load_library().moe_router_workspace_size(T, H, E), 256),
                       dtype=torch.uint8, device="cuda")
-    batched["router"] = graph_batch_us(lambda: moe.router(x, wr, k, workspace=rws), a.steps)
+    # one launch: logits, top-k, softmax and the per-expert counts
+    batched["router"] = graph_batch_us(lambda: moe.router(x, wr, k, workspace=rws, with_counts=True),
+                                       a.steps)
+    # the whole layer from x and W_r (moe_layer_router: the router front end,
+    # then the permutation on its counts, the GEMMs and the combine)
+    lws = torch.empty(moe.load_library().moe_layer_router_workspace_size(T, H, E, k, d["I"], 0),
+                      dtype=torch.uint8, device="cuda")
+
+    def step_router():
+        moe.layer_router(x, wr, wgu, wu_arg, wd, k, workspace=lws, out=out)
+
+    for _ in range(a.warmup):
+        step_router()
+    stats_router = step_stats(step_router, a.steps, cold=False)
     # the row gather alone: the permutation with it minus the permutation
     batched["gather"] = batched["permute_with_gather"] - batched["permute"]
     del ys, xps
@@ -365,6 +378,7 @@ def moe_headline_legs(a, d, v):
         "kernel_us_batched": {n: round(t, 2) for n, t in batched.items()},
         "hip_graph": {"layer_us_per_step": stats_graph},
         "unpacked_gate_up_weights": {"layer_us_per_step": stats_unpacked},
+        "layer_with_router_front_end": {"layer_us_per_step": stats_router},
         "scatter_combine": {"layer_us_per_step": stats_scatter,
                             "kernel_us": {n: round(t * 1e3, 2) for n, t in dur_sc.items()}},
         "measured_peaks": measured_peaks(),

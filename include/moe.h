@@ -117,8 +117,11 @@ int moe_route(const float *logits, int T, int E, int k, int32_t *topk_idx,
 
 /* ------------------------------------------------------------------------
  * moe_router -- the router front end: the logits of the linear router,
- * then exactly moe_route on them (one launch; two when the hidden dimension
- * is sliced, the second adding the slices and routing).
+ * then exactly moe_route on them, and the per-expert count of the chosen
+ * (token, slot) pairs that the permutation starts from (one launch; two
+ * when the hidden dimension is sliced, the second adding the slices,
+ * routing and counting; with expert_counts and an unsliced hidden
+ * dimension, a one-workgroup launch clears the counts first).
  *                                                       [P2 s.4, the route]
  * The pages take the logits as given; the step before them is read as the
  * plain linear router without bias:
@@ -133,13 +136,17 @@ int moe_route(const float *logits, int T, int E, int k, int32_t *topk_idx,
  *            aligned
  *   logits   [T][E] fp32 out, or NULL (not written)
  *   topk_idx [T][k] int32 out;  topk_w [T][k] fp32 out
+ *   expert_counts [E] int32 out, or NULL: how many (token, slot) pairs chose
+ *            each expert
  * Requires 1 <= k <= E, k <= 16, E <= 128, H % 64 == 0
  * (MOE_ERR_UNSUPPORTED otherwise).  workspace: moe_router_workspace_size
- * bytes, 16-byte aligned (MOE_ERR_WORKSPACE if short).
+ * bytes, 16-byte aligned (MOE_ERR_WORKSPACE if short; NULL when that size
+ * is 0); its contents need no initialization.
  * ---------------------------------------------------------------------- */
 int moe_router(const void *x, const void *w_router, int T, int H, int E, int k,
-               float *logits, int32_t *topk_idx, float *topk_w, void *workspace,
-               size_t ws_bytes, void *stream);
+               float *logits, int32_t *topk_idx, float *topk_w,
+               int32_t *expert_counts, void *workspace, size_t ws_bytes,
+               void *stream);
 
 /* Workspace bytes of moe_router (0: none needed, workspace may be NULL; 0
  * also for unsupported sizes).  Fewer than 8161 tokens cut the hidden
@@ -359,6 +366,24 @@ int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
               const float *topk_w_in, const void *w_gate, const void *w_up,
               const void *w_down, int T, int H, int E, int k, int I, void *out,
               void *workspace, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_layer_router -- the whole share starting from the token rows and the
+ * router weights:                                      [P2 s.1, s.4; P1 s.4]
+ *   moe_router (logits, top-k, softmax and expert counts)
+ *   -> moe_permute (taking the router's counts) -> the two grouped GEMMs
+ *   -> the combine chosen by `combine` (MOE_COMBINE_GATHER / _SCATTER).
+ *   w_router [E][H] bf16; the other arguments and results as moe_layer_ex.
+ * Requires the limits of moe_router (E <= 128) and of moe_layer.
+ * Workspace: moe_layer_router_workspace_size bytes, 256-byte aligned: the
+ * moe_layer_workspace_layout regions, then the router's scratch.
+ * ---------------------------------------------------------------------- */
+size_t moe_layer_router_workspace_size(int T, int H, int E, int k, int I,
+                                       int combine);
+int moe_layer_router(const void *x, const void *w_router, const void *w_gate,
+                     const void *w_up, const void *w_down, int T, int H, int E,
+                     int k, int I, void *out, int combine, void *workspace,
+                     size_t ws_bytes, void *stream);
 
 /* moe_layer with a choice of combine ([P2 s.4], MoE layer1 row: the top-k
  * weighted reduction either after the down GEMM or inside its epilogue):

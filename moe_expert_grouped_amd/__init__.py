@@ -65,7 +65,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "moe_version": ([], ctypes.c_char_p),
             "moe_padded_capacity": ([I, I, I], I),
             "moe_route": ([P, I, I, I, P, P, P], I),
-            "moe_router": ([P, P, I, I, I, I, P, P, P, P, Z, P], I),
+            "moe_router": ([P, P, I, I, I, I, P, P, P, P, P, Z, P], I),
             "moe_router_workspace_size": ([I, I, I], Z),
             "moe_permute_workspace_size": ([I, I, I], Z),
             "moe_permute": ([P, I, I, I, P, I, P, P, P, P, P, P, P, I, P, Z, P], I),
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "moe_layer_workspace_layout": ([I, I, I, I, I, ctypes.POINTER(Z)], I),
             "moe_layer": ([P, P, P, P, P, P, P, I, I, I, I, I, P, P, Z, P], I),
             "moe_layer_ex": ([P, P, P, P, P, P, P, I, I, I, I, I, P, I, P, Z, P], I),
+            "moe_layer_router_workspace_size": ([I, I, I, I, I, I], Z),
+            "moe_layer_router": ([P, P, P, P, P, I, I, I, I, I, P, I, P, Z, P], I),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -135,11 +137,12 @@ def route(logits: torch.Tensor, k: int):
 
 
 def router(x: torch.Tensor, w_router: torch.Tensor, k: int, with_logits: bool = False,
-           workspace: torch.Tensor | None = None):
+           workspace: torch.Tensor | None = None, with_counts: bool = False):
     """The linear router and the routing in one launch: logits = x . w_router^T
     (x [T,H] bf16, w_router [E,H] bf16, fp32 accumulation), then the top-k and
-    softmax of `route` on those logits.  Returns (idx int32 [T,k], w fp32 [T,k],
-    logits fp32 [T,E] or None)."""
+    softmax of `route` on those logits, and the per-expert count of the
+    chosen pairs.  Returns (idx int32 [T,k], w fp32 [T,k], logits fp32 [T,E]
+    or None), plus counts int32 [E] with with_counts=True."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w_router, "w_router", torch.bfloat16, 2)
     T, H = x.shape
@@ -150,14 +153,15 @@ def router(x: torch.Tensor, w_router: torch.Tensor, k: int, with_logits: bool = 
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     lg = torch.empty((T, E), dtype=torch.float32, device=dev) if with_logits else None
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if with_counts else None
     lib = load_library()
     need = lib.moe_router_workspace_size(T, H, E)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _check("moe_router", lib.moe_router(_ptr(x), _ptr(w_router), T, H, E, k, _ptr(lg), _ptr(idx),
-                                        _ptr(w), _ptr(workspace),
-                                        0 if workspace is None else workspace.numel(), _stream()))
-    return idx, w, lg
+                                        _ptr(w), _ptr(counts), _ptr(workspace), workspace.numel(),
+                                        _stream()))
+    return (idx, w, lg, counts) if with_counts else (idx, w, lg)
 
 
 # ---------------------------------------------------------------- permute
@@ -430,6 +434,39 @@ def layer(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: tor
             _ptr(x), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
             _ptr(w_down), T, H, E, k, I, _ptr(out), _COMBINES[combine], _ptr(workspace),
             workspace.numel(), _stream()))
+    return out
+
+
+def layer_router(x: torch.Tensor, w_router: torch.Tensor, w_gate: torch.Tensor,
+                 w_up: torch.Tensor | None, w_down: torch.Tensor, k: int,
+                 workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                 combine: str = "gather") -> torch.Tensor:
+    """The MoE layer share from the token rows and the router weights: the
+    router front end (logits, top-k, softmax, expert counts in one launch),
+    then the permutation, the two grouped GEMMs and the combine.  The
+    workspace holds the moe_layer_workspace_layout regions first, then the
+    router's scratch."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_router, "w_router", torch.bfloat16, 2)
+    _need(w_gate, "w_gate", torch.bfloat16, 3)
+    if w_up is not None:
+        _need(w_up, "w_up", torch.bfloat16, 3)
+    _need(w_down, "w_down", torch.bfloat16, 3)
+    T, H = x.shape
+    E, _, I = w_gate.shape
+    if w_up is None:
+        I //= 2
+    lib = load_library()
+    if workspace is None:
+        n = lib.moe_layer_router_workspace_size(T, H, E, k, I, _COMBINES[combine])
+        if n == 0:
+            raise ValueError("unsupported layer sizes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _check("moe_layer_router", lib.moe_layer_router(
+        _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), T, H, E, k, I, _ptr(out),
+        _COMBINES[combine], _ptr(workspace), workspace.numel(), _stream()))
     return out
 
 

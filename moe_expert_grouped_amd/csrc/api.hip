@@ -11,12 +11,13 @@ hipError_t launch_route(const float *, int, int, int, int32_t *, float *, hipStr
 bool router_fits(int H, int E);
 size_t router_workspace_bytes(int T, int H, int E);
 hipError_t launch_router(const uint16_t *, const uint16_t *, int, int, int, int, float *,
-                         int32_t *, float *, void *, hipStream_t);
+                         int32_t *, float *, int32_t *, void *, hipStream_t);
 hipError_t launch_pack_gate_up(const uint16_t *, const uint16_t *, int, int, int, uint16_t *,
                                hipStream_t);
 bool permute_plan_fits(int T, int E, int k);
 hipError_t launch_permute_plan(const int32_t *, int, int, int, int, int32_t *, int32_t *,
-                               int32_t *, int32_t *, int32_t *, int32_t *, int32_t *, hipStream_t);
+                               int32_t *, int32_t *, int32_t *, int32_t *, int32_t *, hipStream_t,
+                               const int32_t *);
 size_t permute_workspace_bytes(long R, int E);
 hipError_t launch_permute(const int32_t *, int, int, int, const uint16_t *, int, int32_t *,
                           int32_t *, int32_t *, int32_t *, int32_t *, int32_t *, uint16_t *, int,
@@ -131,8 +132,8 @@ size_t moe_router_workspace_size(int T, int H, int E) {
 }
 
 int moe_router(const void *x, const void *w_router, int T, int H, int E, int k, float *logits,
-               int32_t *topk_idx, float *topk_w, void *workspace, size_t ws_bytes,
-               void *stream) {
+               int32_t *topk_idx, float *topk_w, int32_t *expert_counts, void *workspace,
+               size_t ws_bytes, void *stream) {
   if (!x || !w_router || !topk_idx || !topk_w) return MOE_ERR_INVALID;
   if (T <= 0 || H <= 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID;
   if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID;
@@ -142,8 +143,8 @@ int moe_router(const void *x, const void *w_router, int T, int H, int E, int k, 
   if (workspace && !aligned16(workspace)) return MOE_ERR_INVALID;
   if (device_cus() == 0) return MOE_ERR_DEVICE;
   return launch_status(moe::launch_router((const uint16_t *)x, (const uint16_t *)w_router, T, H,
-                                          E, k, logits, topk_idx, topk_w, workspace,
-                                          (hipStream_t)stream));
+                                          E, k, logits, topk_idx, topk_w, expert_counts,
+                                          workspace, (hipStream_t)stream));
 }
 
 size_t moe_permute_workspace_size(int T, int k, int E) {
@@ -374,13 +375,15 @@ int moe_layer(const void *x, const float *logits, const int32_t *topk_idx_in,
                       out, MOE_COMBINE_GATHER, workspace, ws_bytes, stream);
 }
 
-int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
-                 const float *topk_w_in, const void *w_gate, const void *w_up,
-                 const void *w_down, int T, int H, int E, int k, int I, void *out, int combine,
-                 void *workspace, size_t ws_bytes, void *stream) {
+} // extern "C"
+
+namespace {
+
+// Checks of the arguments every layer entry point shares.
+int check_layer(const void *x, const void *w_gate, const void *w_up, const void *w_down, int T,
+                int H, int E, int k, int I, const void *out, int combine, const void *workspace) {
   // w_up == NULL: w_gate holds gate and up interleaved (moe_pack_gate_up)
   if (!x || !w_gate || !w_down || !out || !workspace) return MOE_ERR_INVALID;
-  if (!logits && (!topk_idx_in || !topk_w_in)) return MOE_ERR_INVALID;
   if (T <= 0 || H <= 0 || E <= 0 || k <= 0 || I <= 0 || k > E) return MOE_ERR_INVALID;
   if (!aligned16(x) || !aligned16(w_gate) || (w_up && !aligned16(w_up)) || !aligned16(w_down) ||
       !aligned16(out) || !aligned16(workspace))
@@ -390,15 +393,22 @@ int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
   if (E > 1024 || k > 16) return MOE_ERR_UNSUPPORTED;
   if ((long)T * k > 0x7fffffffL / 2) return MOE_ERR_UNSUPPORTED;
   if (combine != MOE_COMBINE_GATHER && combine != MOE_COMBINE_SCATTER) return MOE_ERR_UNSUPPORTED;
-  size_t off[14];
-  moe_layer_workspace_layout(T, H, E, k, I, off);
-  // the fp32 token-row accumulator (last in the layout) only for the scatter
-  if (ws_bytes < (combine == MOE_COMBINE_SCATTER ? off[13] : off[12])) return MOE_ERR_WORKSPACE;
-  const int cus = device_cus();
-  if (cus == 0) return MOE_ERR_DEVICE;
+  return MOE_OK;
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  unsigned char *ws = (unsigned char *)workspace;
+// Bytes of the layer workspace before the router's scratch (the layout
+// through out_acc for the scatter combine, through y's region otherwise).
+size_t layer_core_bytes(const size_t off[14], int combine) {
+  return combine == MOE_COMBINE_SCATTER ? off[13] : off[12];
+}
+
+// The layer on arguments already checked: the routing from the router front
+// end (w_router), from the logits, or given; then permutation, the two
+// grouped GEMMs and the combine, all enqueued on `s`.
+int layer_run(const void *x, const void *w_router, const float *logits,
+              const int32_t *topk_idx_in, const float *topk_w_in, const void *w_gate,
+              const void *w_up, const void *w_down, int T, int H, int E, int k, int I, void *out,
+              int combine, unsigned char *ws, const size_t off[14], int cus, hipStream_t s) {
   int32_t *idx = (int32_t *)(ws + off[0]);
   float *w = (float *)(ws + off[1]);
   int32_t *counts = (int32_t *)(ws + off[2]);
@@ -416,8 +426,17 @@ int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
 
   const int32_t *ridx = topk_idx_in;
   const float *rw = topk_w_in;
+  const int32_t *counted = nullptr; // expert counts from the router front end
   hipError_t e;
-  if (logits) {
+  if (w_router) {
+    // logits, top-k, softmax and the expert histogram in one launch
+    e = moe::launch_router((const uint16_t *)x, (const uint16_t *)w_router, T, H, E, k, nullptr,
+                           idx, w, counts, ws + layer_core_bytes(off, combine), s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    ridx = idx;
+    rw = w;
+    counted = counts;
+  } else if (logits) {
     e = moe::launch_route(logits, T, E, k, idx, w, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     ridx = idx;
@@ -426,7 +445,7 @@ int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
   if (moe::permute_plan_fits(T, E, k)) {
     // permutation and the row-task plan in one launch
     e = moe::launch_permute_plan(ridx, T, E, k, cap, counts, offsets, p2r, r2p, bexp, mpad, plan,
-                                 s);
+                                 s, counted);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
   } else {
     e = moe::launch_permute(ridx, T, k, E, nullptr, 0, counts, offsets, p2r, r2p, bexp, mpad,
@@ -460,6 +479,52 @@ int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   e = moe::launch_combine(y, H, p2r, rw, T, k, (uint16_t *)out, s);
   return launch_status(e);
+}
+
+} // namespace
+
+extern "C" {
+
+int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
+                 const float *topk_w_in, const void *w_gate, const void *w_up,
+                 const void *w_down, int T, int H, int E, int k, int I, void *out, int combine,
+                 void *workspace, size_t ws_bytes, void *stream) {
+  int st = check_layer(x, w_gate, w_up, w_down, T, H, E, k, I, out, combine, workspace);
+  if (st != MOE_OK) return st;
+  if (!logits && (!topk_idx_in || !topk_w_in)) return MOE_ERR_INVALID;
+  size_t off[14];
+  moe_layer_workspace_layout(T, H, E, k, I, off);
+  // the fp32 token-row accumulator (last in the layout) only for the scatter
+  if (ws_bytes < layer_core_bytes(off, combine)) return MOE_ERR_WORKSPACE;
+  const int cus = device_cus();
+  if (cus == 0) return MOE_ERR_DEVICE;
+  return layer_run(x, nullptr, logits, topk_idx_in, topk_w_in, w_gate, w_up, w_down, T, H, E, k,
+                   I, out, combine, (unsigned char *)workspace, off, cus, (hipStream_t)stream);
+}
+
+size_t moe_layer_router_workspace_size(int T, int H, int E, int k, int I, int combine) {
+  size_t off[14];
+  if (moe_layer_workspace_layout(T, H, E, k, I, off) != MOE_OK) return 0;
+  if (combine != MOE_COMBINE_GATHER && combine != MOE_COMBINE_SCATTER) return 0;
+  if (!moe::router_fits(H, E)) return 0;
+  return layer_core_bytes(off, combine) + align256(moe::router_workspace_bytes(T, H, E));
+}
+
+int moe_layer_router(const void *x, const void *w_router, const void *w_gate, const void *w_up,
+                     const void *w_down, int T, int H, int E, int k, int I, void *out,
+                     int combine, void *workspace, size_t ws_bytes, void *stream) {
+  int st = check_layer(x, w_gate, w_up, w_down, T, H, E, k, I, out, combine, workspace);
+  if (st != MOE_OK) return st;
+  if (!w_router) return MOE_ERR_INVALID;
+  if (!aligned16(w_router)) return MOE_ERR_INVALID;
+  if (!moe::router_fits(H, E)) return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < moe_layer_router_workspace_size(T, H, E, k, I, combine)) return MOE_ERR_WORKSPACE;
+  size_t off[14];
+  moe_layer_workspace_layout(T, H, E, k, I, off);
+  const int cus = device_cus();
+  if (cus == 0) return MOE_ERR_DEVICE;
+  return layer_run(x, w_router, nullptr, nullptr, nullptr, w_gate, w_up, w_down, T, H, E, k, I,
+                   out, combine, (unsigned char *)workspace, off, cus, (hipStream_t)stream);
 }
 
 } // extern "C"

@@ -249,7 +249,7 @@ bool permute_plan_fits(int T, int E, int k);
 hipError_t launch_permute_plan(const int32_t *idx, int T, int E, int k, int cap, int32_t *counts,
                                int32_t *offsets, int32_t *pair_to_row, int32_t *row_to_pair,
                                int32_t *block_expert, int32_t *num_padded_rows, int32_t *plan,
-                               hipStream_t stream);
+                               hipStream_t stream, const int32_t *counts_in);
 
 size_t permute_workspace_bytes(long R, int E) {
   const long nchunks = (R + kPermChunk - 1) / kPermChunk;
@@ -265,7 +265,7 @@ hipError_t launch_permute(const int32_t *idx, int T, int k, int E, const uint16_
     // up to 16384 pairs: one launch (permute_plan.hip)
     const hipError_t e = launch_permute_plan(idx, T, E, k, cap, counts, offsets, pair_to_row,
                                              row_to_pair, block_expert, num_padded_rows, nullptr,
-                                             stream);
+                                             stream, nullptr);
     if (e != hipSuccess) return e;
   } else {
     const long R = (long)T * k;

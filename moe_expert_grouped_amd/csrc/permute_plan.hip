@@ -31,7 +31,8 @@ __host__ __device__ inline int hist_copies(int E) {
 }
 
 struct PPArgs {
-  const int32_t *idx; // [T*k] expert of each pair
+  const int32_t *idx;       // [T*k] expert of each pair
+  const int32_t *counts_in; // [E] pairs per expert, if already counted (the router's), or NULL
   int T, E, k, cap;
   int32_t *counts, *offsets, *pair_to_row, *row_to_pair, *block_expert, *num_padded_rows;
   int32_t *plan; // optional: the row-task plan
@@ -68,16 +69,21 @@ __global__ __launch_bounds__(kRPThreads) void permute_plan_kernel(PPArgs a) {
     key[u] = (e >= 0 && e < E) ? e : -1;
   }
   __syncthreads();
-  int *my_hist = hist + __builtin_amdgcn_readfirstlane(wave % copies) * E;
+  if (a.counts_in) {
+    // counted by the router front end in its launch
+    for (int e = tid; e < E; e += kRPThreads) cnt[e] = a.counts_in[e];
+  } else {
+    int *my_hist = hist + __builtin_amdgcn_readfirstlane(wave % copies) * E;
 #pragma unroll
-  for (int u = 0; u < NS; ++u)
-    if (key[u] >= 0) atomicAdd(&my_hist[key[u]], 1);
-  __syncthreads();
-  for (int e = tid; e < E; e += kRPThreads) {
-    int c = 0;
+    for (int u = 0; u < NS; ++u)
+      if (key[u] >= 0) atomicAdd(&my_hist[key[u]], 1);
+    __syncthreads();
+    for (int e = tid; e < E; e += kRPThreads) {
+      int c = 0;
 #pragma unroll
-    for (int w = 0; w < copies; ++w) c += hist[w * E + e];
-    cnt[e] = c;
+      for (int w = 0; w < copies; ++w) c += hist[w * E + e];
+      cnt[e] = c;
+    }
   }
   __syncthreads();
 
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(kRPThreads) void permute_plan_kernel(PPArgs a) {
   const int m_pad = off[E];
   if (blockIdx.x == 0) {
     for (int e = tid; e < E; e += kRPThreads) {
-      a.counts[e] = cnt[e];
+      if (a.counts != a.counts_in) a.counts[e] = cnt[e];
       a.offsets[e] = off[e];
     }
     if (tid == 0) {
@@ -177,12 +183,14 @@ bool permute_plan_fits(int T, int E, int k) {
 
 // The permutation maps, block experts and, with plan non-NULL, the row-task
 // plan of the routing idx.
+// counts_in: the pairs per expert if counted already (the router front end's
+// histogram; every id then lies in [0, E)), else NULL.
 hipError_t launch_permute_plan(const int32_t *idx, int T, int E, int k, int cap, int32_t *counts,
                                int32_t *offsets, int32_t *pair_to_row, int32_t *row_to_pair,
                                int32_t *block_expert, int32_t *num_padded_rows, int32_t *plan,
-                               hipStream_t stream) {
+                               hipStream_t stream, const int32_t *counts_in) {
   if (!permute_plan_fits(T, E, k)) return hipErrorInvalidValue;
-  PPArgs a{idx, T, E, k, cap, counts, offsets, pair_to_row, row_to_pair, block_expert,
+  PPArgs a{idx, counts_in, T, E, k, cap, counts, offsets, pair_to_row, row_to_pair, block_expert,
            num_padded_rows, plan};
   const int G = E; // one workgroup per expert
   const size_t hist_bytes = (size_t)hist_copies(E) * E * sizeof(int); // <= 16 KiB

@@ -25,7 +25,18 @@
 // slices' partial logits go to a workspace and a second launch adds them in
 // slice order and routes (one fixed rounding order either way).  (128-token
 // workgroups, which read half the W bytes per token, need 16 slices at
-// T = 2048, and their partials then cost as much as x.)
+// T = 2048, and their partials then cost as much as x.)  The kernel
+// boundary is the grid-wide step here: a one-launch form in which the last
+// of a token block's slices to arrive (a compare-and-swap on a per-block
+// word) adds the slices ran 24.0 us against 10.1 us for the two launches at
+// T = 2048, and a grid-wide last arriver for the histogram 67 us -- each
+// device-scope atomic round trip costs microseconds on this part.
+//
+// The routing kernel also counts the chosen experts (the histogram the
+// permutation starts from): a per-workgroup LDS histogram, then one
+// device-scope add per expert into expert_counts, issued without waiting
+// for a result.  The counts are cleared by the first launch when the hidden
+// dimension is sliced, else by a one-workgroup clearing launch before it.
 // Traffic: 2 T H (x, once) + 2 E H per workgroup (W, from L2) + 8 S T E
 // (partials, S > 1) + 4 T E (logits, if written) + 8 T k bytes.
 #include "topk.h"
@@ -67,7 +78,8 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t *__restrict_
                                                      int E, int k, int S, float *__restrict__ part_out,
                                                      float *__restrict__ logits,
                                                      int32_t *__restrict__ topk_idx,
-                                                     float *__restrict__ topk_w) {
+                                                     float *__restrict__ topk_w,
+                                                     int32_t *__restrict__ counts) {
   constexpr int EP = 32 * NT;                // expert columns computed
   constexpr int LD = EP + 1;                 // LDS row stride of the partial tiles, in floats
   constexpr int XB = kRouterTok * 128;       // x bytes of a stage: 32 rows x 128 bytes
@@ -75,6 +87,7 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t *__restrict_
   constexpr int NI = 1 + NT;                 // DMA instructions per wavefront per chunk
   static_assert(kRouterTok == 8 * kRouterWaves, "one x instruction per wavefront");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kRouterStages * SB];
+  __shared__ int32_t s_hist[32 * NT];
   // after the last chunk the ring holds the wavefronts' partial tiles
   static_assert(sizeof(float) * kRouterWaves * kRouterTok * LD <= kRouterStages * SB, "fits");
   float(*part)[kRouterTok][LD] = reinterpret_cast<float(*)[kRouterTok][LD]>(ring);
@@ -162,7 +175,14 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t *__restrict_
     part[0][tr][e] = s;
     if (dst && e < E && t0 + tr < T) dst[(size_t)(t0 + tr) * E + e] = s;
   }
-  if (S > 1) return; // router_select_kernel adds the slices and routes
+  if (S > 1) {
+    // router_select_kernel adds the slices, routes and counts; the counts
+    // start from zero (that launch follows this one)
+    if (counts && blockIdx.x == 0 && blockIdx.y == 0)
+      for (int e = threadIdx.x; e < E; e += blockDim.x) counts[e] = 0;
+    return;
+  }
+  for (int e = threadIdx.x; e < EP; e += blockDim.x) s_hist[e] = 0;
   __syncthreads();
 
   constexpr int EPL = (EP + 63) / 64;
@@ -176,21 +196,28 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t *__restrict_
       const int e = lane + 64 * i;
       v[i] = e < E ? part[0][tr][e] : 0.0f;
     }
-    topk_softmax<EPL>(v, E, k, lane, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+    const int chosen = topk_softmax<EPL>(v, E, k, lane, topk_idx + (size_t)t * k,
+                                         topk_w + (size_t)t * k);
+    if (counts && lane < k) atomicAdd(&s_hist[chosen], 1);
   }
+  if (!counts) return;
+  __syncthreads();
+  // cleared by the launch before this one
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    if (s_hist[e]) atomicAdd(&counts[e], s_hist[e]);
 }
 
 // One wavefront per token: the S slices' partial logits added in slice
 // order, written to logits if asked, then routed.
+// Token t of router_select_kernel (one wavefront): the S slices' partial
+// logits added in slice order, written to logits if asked, then routed;
+// with hist, its choices counted there.
 template <int EPL>
-__global__ __launch_bounds__(256) void router_select_kernel(const float *__restrict__ part, int T,
-                                                            int E, int k, int S,
-                                                            float *__restrict__ logits,
-                                                            int32_t *__restrict__ topk_idx,
-                                                            float *__restrict__ topk_w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (t >= T) return; // wavefront-uniform
+__device__ __forceinline__ void select_one(const float *__restrict__ part, int T, int E, int k,
+                                           int S, float *__restrict__ logits,
+                                           int32_t *__restrict__ topk_idx,
+                                           float *__restrict__ topk_w, int t, int lane,
+                                           int32_t *hist) {
   float v[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
@@ -203,36 +230,68 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float *__restr
     }
     v[i] = s;
   }
-  topk_softmax<EPL>(v, E, k, lane, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+  const int chosen = topk_softmax<EPL>(v, E, k, lane, topk_idx + (size_t)t * k,
+                                       topk_w + (size_t)t * k);
+  if (hist && lane < k) atomicAdd(&hist[chosen], 1);
+}
+
+// 16 tokens per 1024-thread workgroup, whose choices are counted in LDS and
+// added into counts (cleared by router_kernel).
+template <int EPL>
+__global__ __launch_bounds__(1024) void router_select_kernel(const float *__restrict__ part, int T,
+                                                             int E, int k, int S,
+                                                             float *__restrict__ logits,
+                                                             int32_t *__restrict__ topk_idx,
+                                                             float *__restrict__ topk_w,
+                                                             int32_t *__restrict__ counts) {
+  __shared__ int32_t s_hist[64 * EPL];
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  for (int e = threadIdx.x; e < 64 * EPL; e += blockDim.x) s_hist[e] = 0;
+  __syncthreads();
+  if (t < T) select_one<EPL>(part, T, E, k, S, logits, topk_idx, topk_w, t, lane,
+                             counts ? s_hist : nullptr);
+  if (!counts) return;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    if (s_hist[e]) atomicAdd(&counts[e], s_hist[e]);
 }
 
 bool router_fits(int H, int E) { return H % 64 == 0 && E >= 1 && E <= 128; }
 
+// Clears expert_counts before a routing kernel that adds into it.
+__global__ void router_clear_counts(int32_t *__restrict__ counts, int E) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) counts[e] = 0;
+}
+
 hipError_t launch_router(const uint16_t *x, const uint16_t *w, int T, int H, int E, int k,
-                         float *logits, int32_t *topk_idx, float *topk_w, void *ws,
-                         hipStream_t stream) {
+                         float *logits, int32_t *topk_idx, float *topk_w, int32_t *counts,
+                         void *ws, hipStream_t stream) {
   const int S = router_splits(T, H);
   float *part = S > 1 ? static_cast<float *>(ws) : nullptr;
+  if (counts && S == 1) router_clear_counts<<<1, 256, 0, stream>>>(counts, E);
   const dim3 grid((T + kRouterTok - 1) / kRouterTok, S), block(64 * kRouterWaves);
   const int nt = (E + 31) / 32;
   if (nt <= 1)
     router_kernel<1><<<grid, block, 0, stream>>>(x, w, T, H, E, k, S, part, logits, topk_idx,
-                                                 topk_w);
+                                                 topk_w, counts);
   else if (nt == 2)
     router_kernel<2><<<grid, block, 0, stream>>>(x, w, T, H, E, k, S, part, logits, topk_idx,
-                                                 topk_w);
+                                                 topk_w, counts);
   else if (nt == 3)
     router_kernel<3><<<grid, block, 0, stream>>>(x, w, T, H, E, k, S, part, logits, topk_idx,
-                                                 topk_w);
+                                                 topk_w, counts);
   else
     router_kernel<4><<<grid, block, 0, stream>>>(x, w, T, H, E, k, S, part, logits, topk_idx,
-                                                 topk_w);
+                                                 topk_w, counts);
   if (S > 1) {
-    const dim3 g2((T + 3) / 4);
+    const dim3 g2((T + 15) / 16);
     if (E <= 64)
-      router_select_kernel<1><<<g2, 256, 0, stream>>>(part, T, E, k, S, logits, topk_idx, topk_w);
+      router_select_kernel<1><<<g2, 1024, 0, stream>>>(part, T, E, k, S, logits, topk_idx, topk_w,
+                                                       counts);
     else
-      router_select_kernel<2><<<g2, 256, 0, stream>>>(part, T, E, k, S, logits, topk_idx, topk_w);
+      router_select_kernel<2><<<g2, 1024, 0, stream>>>(part, T, E, k, S, logits, topk_idx, topk_w,
+                                                       counts);
   }
   return hipGetLastError();
 }

@@ -60,9 +60,10 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
 // fp32 logit, then lower id), so the selection matches any correct
 // implementation bit for bit.  Slot 0 holds the largest logit; the weights
 // are the fp32 softmax over the k selected logits, their exponentials summed
-// in slot order.  Lane j < k writes slot j of idx_row / w_row.
+// in slot order.  Lane j < k writes slot j of idx_row / w_row, and returns
+// the expert it wrote (other lanes return 0).
 template <int EPL>
-__device__ __forceinline__ void topk_softmax(const float (&v)[EPL], int E, int k, int lane,
+__device__ __forceinline__ int topk_softmax(const float (&v)[EPL], int E, int k, int lane,
                                              int32_t *__restrict__ idx_row,
                                              float *__restrict__ w_row) {
   uint64_t key[EPL];
@@ -94,6 +95,7 @@ __device__ __forceinline__ void topk_softmax(const float (&v)[EPL], int E, int k
     idx_row[lane] = sel_e;
     w_row[lane] = sel_ex / sum;
   }
+  return sel_e;
 }
 
 } // namespace moe

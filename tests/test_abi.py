@@ -28,10 +28,10 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     for n in ["moe_route", "moe_router", "moe_permute", "grouped_gemm", "grouped_gemm_tuned", "moe_combine",
               "moe_finalize", "moe_layer", "moe_layer_ex", "moe_pack_gate_up", "moe_layer_workspace_size_ex",
-              "grouped_gemm_noalloc"]:
+              "grouped_gemm_noalloc", "moe_layer_router", "moe_layer_router_workspace_size"]:
         assert n in names
     for n in names:
         assert hasattr(lib, n), "missing export " + n
@@ -79,8 +79,9 @@ NULL = None
 
 
 def test_router_validation(lib):
-    def call(x=FAKE, w=FAKE, T=4, H=256, E=8, k=2, lg=NULL, idx=FAKE, wo=FAKE, ws=FAKE, wsb=1 << 20):
-        return lib.moe_router(x, w, T, H, E, k, lg, idx, wo, ws, wsb, NULL)
+    def call(x=FAKE, w=FAKE, T=4, H=256, E=8, k=2, lg=NULL, idx=FAKE, wo=FAKE, ws=FAKE, wsb=1 << 20,
+             counts=NULL):
+        return lib.moe_router(x, w, T, H, E, k, lg, idx, wo, counts, ws, wsb, NULL)
     assert call(x=NULL) == moe.MOE_ERR_INVALID
     assert call(w=NULL) == moe.MOE_ERR_INVALID
     assert call(idx=NULL) == moe.MOE_ERR_INVALID
@@ -96,6 +97,7 @@ def test_router_validation(lib):
     assert call(wsb=16) == moe.MOE_ERR_WORKSPACE
     assert call(ws=MISALIGNED) == moe.MOE_ERR_INVALID
     assert call(lg=FAKE) == moe.MOE_ERR_DEVICE       # valid arguments; no GPU here
+    assert call(counts=FAKE) == moe.MOE_ERR_DEVICE
     # the slices: only a short routing needs the workspace, which holds S partial [T][E] tiles
     assert lib.moe_router_workspace_size(2048, 4096, 64) == 4 * 2048 * 64 * 4
     assert lib.moe_router_workspace_size(8192, 4096, 64) == 0
@@ -250,6 +252,28 @@ def test_combine_and_layer_validation(lib):
                          NULL) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_layer(FAKE, FAKE, NULL, NULL, NULL, NULL, FAKE, T, H, E, k, I, FAKE, FAKE, ws,
                          NULL) == moe.MOE_ERR_INVALID
+
+
+def test_layer_router_validation(lib):
+    T, H, E, k, I = 64, 128, 8, 2, 64
+    ws = lib.moe_layer_router_workspace_size(T, H, E, k, I, 0)
+    lay = moe.layer_workspace_layout(T, H, E, k, I)
+    # the layer's regions (without the scatter's accumulator), then the router's scratch
+    assert ws == lay["out_acc"] + lib.moe_router_workspace_size(T, H, E)
+    assert lib.moe_layer_router_workspace_size(T, H, E, k, I, 1) == \
+        lay["total"] + lib.moe_router_workspace_size(T, H, E)
+    assert lib.moe_layer_router_workspace_size(T, H, 200, k, I, 0) == 0   # E > 128: no router
+
+    def call(x=FAKE, wr=FAKE, E=E, wsb=ws, combine=0):
+        return lib.moe_layer_router(x, wr, FAKE, FAKE, FAKE, T, H, E, k, I, FAKE, combine, FAKE, wsb, NULL)
+    assert call() == moe.MOE_ERR_DEVICE                 # valid; no GPU here
+    assert call(wr=NULL) == moe.MOE_ERR_INVALID
+    assert call(wr=MISALIGNED) == moe.MOE_ERR_INVALID
+    assert call(x=NULL) == moe.MOE_ERR_INVALID
+    assert call(E=200) == moe.MOE_ERR_UNSUPPORTED
+    assert call(wsb=ws - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(combine=1) == moe.MOE_ERR_WORKSPACE      # the scatter needs its accumulator too
+    assert call(combine=3) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_valid_call_without_device_reports_device_error(lib):

@@ -196,7 +196,7 @@ def test_layer_packed_gate_up_same_bits(name):
             assert_close(to_f64(b), to_f64(a), name + " scatter", max_frac=1e-2, rel_fro=2e-3)
 
 
-@pytest.mark.parametrize("combine", ["gather", "scatter"])
+@pytest.mark.parametrize("combine", ["gather", "scatter", "router"])
 def test_layer_hip_graph_replays(combine):
     # the whole layer captured in one HIP graph (it launches kernels only: no
     # memset node, no host synchronization, no allocation inside) replays to
@@ -207,26 +207,37 @@ def test_layer_hip_graph_replays(combine):
     D = _inputs_dev(d)
     wgu = moe.pack_gate_up(D["wg"], D["wu"])
     logits = torch.from_numpy(d["logits"]).cuda()
-    ws = moe.layer_workspace(T, H, E, k, I)
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     say("layer graph", combine)
-    eager = moe.layer(D["x"], wgu, None, D["wd"], k, logits=logits, workspace=ws, combine=combine).clone()
+    if combine == "router":
+        # the router front end inside the graph (its expert counts cleared and
+        # added by the replayed kernels themselves)
+        wr = dev16(syn.bf16_bits((np.random.default_rng(3).standard_normal((E, H)) / np.sqrt(H))
+                                 .astype(np.float32)))
+        ws = torch.empty(moe.load_library().moe_layer_router_workspace_size(T, H, E, k, I, 0), dtype=torch.uint8,
+                         device="cuda")
+        run = lambda o=None: moe.layer_router(D["x"], wr, wgu, None, D["wd"], k, workspace=ws, out=o)
+    else:
+        ws = moe.layer_workspace(T, H, E, k, I)
+        run = lambda o=None: moe.layer(D["x"], wgu, None, D["wd"], k, logits=logits, workspace=ws, out=o,
+                                       combine=combine)
+    eager = run().clone()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):  # warm the path on the capture stream
-        moe.layer(D["x"], wgu, None, D["wd"], k, logits=logits, workspace=ws, out=out, combine=combine)
+        run(out)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        moe.layer(D["x"], wgu, None, D["wd"], k, logits=logits, workspace=ws, out=out, combine=combine)
+        run(out)
     for rep in range(4):
         out.fill_(float("nan"))
         ws[:4096].zero_()  # eager work on the buffers the graph reads and writes
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        if combine == "gather":
+        if combine != "scatter":
             assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), rep
         else:
             assert_close(to_f64(out), to_f64(eager), "graph scatter %d" % rep, max_frac=1e-2, rel_fro=2e-3)

@@ -138,15 +138,20 @@ def _small_layer_inputs(T, H, E, k, I, seed):
 # tp_share router shape
 @pytest.mark.parametrize("T,H,E,k", [(2048, 4096, 64, 4), (77, 256, 5, 2), (300, 192, 128, 16),
                                      (33, 64, 33, 3), (1, 512, 1, 1), (1000, 1024, 96, 8),
-                                     (512, 4096, 16, 1)])
+                                     (512, 4096, 16, 1), (8192, 512, 64, 8)])
 def test_router_matches_oracle(T, H, E, k):
     g = np.random.default_rng(T + H + E + k)
     x = syn.bf16_bits(g.standard_normal((T, H)).astype(np.float32))
     W = syn.bf16_bits((g.standard_normal((E, H)) / np.sqrt(H)).astype(np.float32))
     say("router", "T", T, "H", H, "E", E, "k", k)
-    idx, w, lg = moe.router(dev16(x), dev16(W), k, with_logits=True)
+    # a workspace of garbage: its contents need no clearing
+    ws = torch.full((max(256, moe.load_library().moe_router_workspace_size(T, H, E)),), 0xA5,
+                    dtype=torch.uint8, device="cuda")
+    idx, w, lg, counts = moe.router(dev16(x), dev16(W), k, with_logits=True, workspace=ws, with_counts=True)
     torch.cuda.synchronize()
-    idx, w, lg = idx.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy()
+    idx, w, lg, counts = idx.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy(), counts.cpu().numpy()
+    # the expert histogram of the launch: exactly the count of the routing it wrote
+    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=E))
     # logits: within the fp32 summation bound of the exact sum (bf16 products
     # are exact in fp32; H additions at most, each off by half an ulp)
     ref = oracle.router_logits(x, W)
@@ -165,6 +170,85 @@ def test_router_matches_oracle(T, H, E, k):
         pairs = [(e, f) for e in a - b for f in b - a] or list(zip(idx[t], oidx[t]))
         for e, f in pairs:
             assert abs(ref[t, e] - ref[t, f]) <= 2 * (bound[t, e] + bound[t, f]), (t, e, f)
+
+
+@pytest.mark.parametrize("T,H,E,k", [(2048, 4096, 64, 4), (8192, 256, 16, 2)])
+def test_router_repeats_and_graph_replays(T, H, E, k):
+    # one workspace across calls, and the call captured in a HIP graph and
+    # replayed with eager work between replays: the same bits every time
+    # (the slices are added in a fixed order; the counts are cleared by the
+    # call itself)
+    g = np.random.default_rng(5)
+    x = dev16(syn.bf16_bits(g.standard_normal((T, H)).astype(np.float32)))
+    W = dev16(syn.bf16_bits((g.standard_normal((E, H)) / np.sqrt(H)).astype(np.float32)))
+    ws = torch.zeros(max(256, moe.load_library().moe_router_workspace_size(T, H, E)), dtype=torch.uint8,
+                     device="cuda")
+    say("router repeats and graph", T, H, E, k)
+    ref = moe.router(x, W, k, with_logits=True, workspace=ws, with_counts=True)
+    ref = [t.clone() for t in ref]
+    for _ in range(3):
+        again = moe.router(x, W, k, with_logits=True, workspace=ws, with_counts=True)
+        for a, b in zip(ref, again):
+            assert torch.equal(a, b)
+    outs = [torch.empty_like(t) for t in ref]
+    lib = moe.load_library()
+
+    def call():
+        st = lib.moe_router(moe._ptr(x), moe._ptr(W), T, H, E, k, moe._ptr(outs[2]), moe._ptr(outs[0]),
+                            moe._ptr(outs[1]), moe._ptr(outs[3]), moe._ptr(ws), ws.numel(), moe._stream())
+        assert st == moe.MOE_OK
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(4):
+        for t in outs:
+            t.zero_()
+        moe.router(x, W, k, workspace=ws)  # an eager call between the replays, same workspace
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, outs):
+            assert torch.equal(a, b), rep
+
+
+@pytest.mark.parametrize("name,combine", [("tiny", "gather"), ("tp_share", "gather"), ("tp_share", "scatter")])
+def test_layer_router_matches_oracle(name, combine):
+    # the layer from x and the router weights: its routing is the routing
+    # rule on the router's own fp32 logits (bit for bit), its permutation the
+    # oracle's of that routing, its output the layer's definition
+    d = syn.make_config(name)
+    T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
+    Wr = syn.bf16_bits((np.random.default_rng(11).standard_normal((E, H)) / np.sqrt(H)).astype(np.float32))
+    x, wr = dev16(d["x"]), dev16(Wr)
+    wg, wu, wd = dev16(d["wg"]), dev16(d["wu"]), dev16(d["wd"])
+    lib = moe.load_library()
+    ws = torch.full((lib.moe_layer_router_workspace_size(T, H, E, k, I, 0 if combine == "gather" else 1),),
+                    0x3C, dtype=torch.uint8, device="cuda")
+    say("layer router", name, combine)
+    out = moe.layer_router(x, wr, moe.pack_gate_up(wg, wu), None, wd, k, workspace=ws, combine=combine)
+    _, _, lg = moe.router(x, wr, k, with_logits=True)
+    torch.cuda.synchronize()
+    idx, w = oracle.route(lg.cpu().numpy(), k)
+    view = lambda n: moe.workspace_view(ws, T, H, E, k, I, n).cpu().numpy()
+    assert np.array_equal(view("topk_idx"), idx)
+    assert np.max(np.abs(view("topk_w") - w) / w) <= 1e-6
+    P = oracle.permute(idx, E)
+    for n_ws, n_or in [("expert_counts", "counts"), ("expert_offsets", "offsets"),
+                       ("pair_to_row", "pair_to_row"), ("row_to_pair", "row_to_pair"),
+                       ("block_expert", "block_expert")]:
+        assert np.array_equal(view(n_ws), P[n_or]), n_ws
+    tokens = np.arange(T, dtype=np.int32) if T <= 256 else np.sort(
+        np.random.default_rng(0).choice(T, 96, replace=False)).astype(np.int32)
+    ref = oracle.moe_tokens(d["x"], idx, w, d["wg"], d["wu"], d["wd"], tokens=tokens)
+    from _util import assert_close, to_f64
+    r = assert_close(to_f64(out)[tokens], ref, "layer router " + name)
+    say("layer router", name, "max|err|/max|ref| %.2e  relFro %.2e" % r)
 
 
 # shapes of every variant of the one-launch routing + permutation + plan
