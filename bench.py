@@ -309,6 +309,20 @@ def moe_headline_legs(a, d, v):
         step_unpacked()
     stats_unpacked = step_stats(step_unpacked, a.steps, cold=False)
 
+    # the permutation as its own launch instead of inside the gate/up GEMM's
+    # prologue (the layer's default where the shape allows), interleaved
+    # with the default so both see the same clocks
+    def step_separate():
+        moe.layer(x, wgu, wu_arg, wd, k, logits=logits, topk_idx=tidx, topk_w=tw, workspace=ws,
+                  out=out, separate_permute=True)
+
+    for _ in range(a.warmup):
+        step_separate()
+    ab = {"fused": [], "separate": []}
+    for _ in range(5):
+        ab["fused"].append(step_stats(step, max(a.steps // 5, 4), cold=False)["warm"]["median"])
+        ab["separate"].append(step_stats(step_separate, max(a.steps // 5, 4), cold=False)["warm"]["median"])
+
     # the weighted-scatter down GEMM (alone, on the plan built before) and its finalize
     acc = torch.empty((T, H), dtype=torch.float32, device="cuda")
     sc = []
@@ -378,6 +392,10 @@ def moe_headline_legs(a, d, v):
         "kernel_us_batched": {n: round(t, 2) for n, t in batched.items()},
         "hip_graph": {"layer_us_per_step": stats_graph},
         "unpacked_gate_up_weights": {"layer_us_per_step": stats_unpacked},
+        "front_end_ab": {"what": "layer step medians (us), 5 interleaved rounds: the reorder by route "
+                                 "inside the gate/up GEMM prologue (fused, the default) against the "
+                                 "permutation as its own launch (separate)",
+                         "fused": ab["fused"], "separate": ab["separate"]},
         "layer_with_router_front_end": {"layer_us_per_step": stats_router},
         "scatter_combine": {"layer_us_per_step": stats_scatter,
                             "kernel_us": {n: round(t * 1e3, 2) for n, t in dur_sc.items()}},

@@ -87,6 +87,14 @@ extern "C" {
 /* How moe_layer_ex returns expert outputs to token order. */
 #define MOE_COMBINE_GATHER 0  /* y stored per row, then moe_combine (deterministic) */
 #define MOE_COMBINE_SCATTER 1 /* down GEMM scatters w*y into fp32 rows, moe_finalize */
+/* Flag OR-ed into the combine of moe_layer_ex / moe_layer_router: run the
+ * permutation as its own launch before the gate/up GEMM.  Without it the
+ * layer fuses the reorder by route into the gate/up GEMM's prologue
+ * ([P2 s.4], MoE layer0 = prologue + reorder by route; [P1 s.4], the gate
+ * hook before a row block is loaded) wherever the shape allows: at most
+ * 16384 (token, slot) pairs, at most 256 experts, I % 128 == 0, and a
+ * bounded number of tasks per workgroup.  Same results either way. */
+#define MOE_LAYER_SEPARATE_PERMUTE 0x100
 
 #define MOE_ROW_BLOCK 128 /* rows per task and per-expert alignment unit [P1 s.4] */
 
@@ -355,7 +363,8 @@ size_t moe_layer_workspace_size(int T, int H, int E, int k, int I);
 int moe_layer_workspace_layout(int T, int H, int E, int k, int I,
                                size_t off[14]);
 
-/* Workspace bytes of moe_layer_ex with the given combine: off[12] of the
+/* Workspace bytes of moe_layer_ex with the given combine (the
+ * MOE_LAYER_SEPARATE_PERMUTE flag changes nothing here): off[12] of the
  * layout for MOE_COMBINE_GATHER (no out_acc), off[13] for
  * MOE_COMBINE_SCATTER; 0 for invalid sizes or an unknown combine.
  * moe_layer_workspace_size is the larger of the two. */

@@ -36,6 +36,7 @@ ROW_BLOCK = 128
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 MOE_B_STREAM = 0x100  # flag on a [K][N] b_layout: non-temporal weight loads
+MOE_LAYER_SEPARATE_PERMUTE = 0x100  # flag on a layer's combine: the permutation as its own launch
 _DTYPES = {torch.bfloat16: 0, torch.float16: 1}
 _LAYOUTS = {"kn": 0, "nk": 1, "kn_gate_up": 2}
 _EPIS = {"store": 0, "silu_mul": 1, "weighted_scatter": 2}
@@ -401,12 +402,15 @@ def layer_workspace(T, H, E, k, I, device="cuda", combine: str = "scatter") -> t
 def layer(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, k: int,
           logits: torch.Tensor | None = None, topk_idx: torch.Tensor | None = None,
           topk_w: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-          out: torch.Tensor | None = None, combine: str = "gather") -> torch.Tensor:
+          out: torch.Tensor | None = None, combine: str = "gather",
+          separate_permute: bool = False) -> torch.Tensor:
     """The MoE layer share: route (or the given routing) -> permute -> gate/up
     grouped GEMM with SiLU*up -> down grouped GEMM -> top-k weighted combine.
     w_up=None: w_gate is the interleaved [E][H][2I] tensor of pack_gate_up.
     combine="gather" (deterministic) stores y and runs the combine kernel;
-    "scatter" folds the weighted sum into the down GEMM's epilogue."""
+    "scatter" folds the weighted sum into the down GEMM's epilogue.  The
+    permutation runs inside the gate/up GEMM's prologue where the shape
+    allows; separate_permute=True gives it its own launch (same results)."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w_gate, "w_gate", torch.bfloat16, 3)
     if w_up is not None:
@@ -425,27 +429,28 @@ def layer(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: tor
         workspace = layer_workspace(T, H, E, k, I, x.device, combine)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
-    if combine == "gather":
+    if combine == "gather" and not separate_permute:
         _check("moe_layer", load_library().moe_layer(
             _ptr(x), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
             _ptr(w_down), T, H, E, k, I, _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
     else:
         _check("moe_layer_ex", load_library().moe_layer_ex(
             _ptr(x), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
-            _ptr(w_down), T, H, E, k, I, _ptr(out), _COMBINES[combine], _ptr(workspace),
-            workspace.numel(), _stream()))
+            _ptr(w_down), T, H, E, k, I, _ptr(out),
+            _COMBINES[combine] | (MOE_LAYER_SEPARATE_PERMUTE if separate_permute else 0),
+            _ptr(workspace), workspace.numel(), _stream()))
     return out
 
 
 def layer_router(x: torch.Tensor, w_router: torch.Tensor, w_gate: torch.Tensor,
                  w_up: torch.Tensor | None, w_down: torch.Tensor, k: int,
                  workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                 combine: str = "gather") -> torch.Tensor:
+                 combine: str = "gather", separate_permute: bool = False) -> torch.Tensor:
     """The MoE layer share from the token rows and the router weights: the
-    router front end (logits, top-k, softmax, expert counts in one launch),
-    then the permutation, the two grouped GEMMs and the combine.  The
-    workspace holds the moe_layer_workspace_layout regions first, then the
-    router's scratch."""
+    router front end (logits, top-k, softmax; the expert counts too when the
+    permutation runs separately), then the permutation, the two grouped GEMMs
+    and the combine.  The workspace holds the moe_layer_workspace_layout
+    regions first, then the router's scratch."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w_router, "w_router", torch.bfloat16, 2)
     _need(w_gate, "w_gate", torch.bfloat16, 3)
@@ -466,7 +471,8 @@ def layer_router(x: torch.Tensor, w_router: torch.Tensor, w_gate: torch.Tensor,
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     _check("moe_layer_router", lib.moe_layer_router(
         _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), T, H, E, k, I, _ptr(out),
-        _COMBINES[combine], _ptr(workspace), workspace.numel(), _stream()))
+        _COMBINES[combine] | (MOE_LAYER_SEPARATE_PERMUTE if separate_permute else 0), _ptr(workspace),
+        workspace.numel(), _stream()))
     return out
 
 

@@ -40,9 +40,12 @@ FLAGS = [
 # and dtypes, the weighted scatter for [K][N] weights.
 # (epilogue, [K][N] B, fp16, non-temporal B): the non-temporal weight loads
 # exist for the [K][N] layouts only
-GG_VARIANTS = [(e, kn, f, 0) for e in (0, 1) for kn in (1, 0) for f in (0, 1)] + \
-              [(2, 1, 0, 0), (2, 1, 1, 0)] + \
-              [(e, 1, f, 1) for e in (0, 1, 2) for f in (0, 1)]
+# (.., 1): the fused gate/up form (the permutation inside the kernel), bf16
+# [K][N] weights, both cache policies
+GG_VARIANTS = [(e, kn, f, 0, 0) for e in (0, 1) for kn in (1, 0) for f in (0, 1)] + \
+              [(2, 1, 0, 0, 0), (2, 1, 1, 0, 0)] + \
+              [(e, 1, f, 1, 0) for e in (0, 1, 2) for f in (0, 1)] + \
+              [(1, 1, 0, nt, 1) for nt in (0, 1)]
 
 
 def _compile(job) -> str:
@@ -63,8 +66,8 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
         if os.path.basename(src) == "gg_inst.hip":
-            jobs += [(src, (("GG_EPI", e), ("GG_KN", kn), ("GG_FP16", f), ("GG_NT", nt)))
-                     for e, kn, f, nt in GG_VARIANTS]
+            jobs += [(src, (("GG_EPI", e), ("GG_KN", kn), ("GG_FP16", f), ("GG_NT", nt), ("GG_LP", lp)))
+                     for e, kn, f, nt, lp in GG_VARIANTS]
         else:
             jobs.append((src, ()))
     # the instantiations are the slow ones: start them first

@@ -28,6 +28,11 @@ hipError_t launch_grouped_gemm(int, int, int, const uint16_t *, const int32_t *,
                                hipStream_t, const int32_t *tile = nullptr);
 bool gg_tile_usable(const int32_t *tile, int epilogue, int N, int K);
 hipError_t launch_gg_plan(const int32_t *, const int32_t *, int, int32_t *, hipStream_t);
+bool gg_fused_fits(int N, int K, int R, int E, int grid);
+hipError_t launch_gate_up_fused(const uint16_t *, const int32_t *, int, int, int, int,
+                                const uint16_t *, const uint16_t *, bool, int, int, uint16_t *,
+                                int32_t *, int32_t *, int32_t *, int32_t *, int32_t *, int32_t *,
+                                int32_t *, int, bool, hipStream_t);
 size_t gg_plan_bytes(int cap);
 hipError_t launch_combine(const uint16_t *, int, const int32_t *, const float *, int, int,
                           uint16_t *, hipStream_t);
@@ -363,6 +368,7 @@ size_t moe_layer_workspace_size(int T, int H, int E, int k, int I) {
 size_t moe_layer_workspace_size_ex(int T, int H, int E, int k, int I, int combine) {
   size_t off[14];
   if (moe_layer_workspace_layout(T, H, E, k, I, off) != MOE_OK) return 0;
+  combine &= ~MOE_LAYER_SEPARATE_PERMUTE;
   if (combine == MOE_COMBINE_GATHER) return off[12]; // out_acc, last, is the scatter's only
   return combine == MOE_COMBINE_SCATTER ? off[13] : 0;
 }
@@ -392,14 +398,16 @@ int check_layer(const void *x, const void *w_gate, const void *w_up, const void 
   if (!w_up && I % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (E > 1024 || k > 16) return MOE_ERR_UNSUPPORTED;
   if ((long)T * k > 0x7fffffffL / 2) return MOE_ERR_UNSUPPORTED;
-  if (combine != MOE_COMBINE_GATHER && combine != MOE_COMBINE_SCATTER) return MOE_ERR_UNSUPPORTED;
+  if ((combine & ~MOE_LAYER_SEPARATE_PERMUTE) != MOE_COMBINE_GATHER &&
+      (combine & ~MOE_LAYER_SEPARATE_PERMUTE) != MOE_COMBINE_SCATTER)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
 // Bytes of the layer workspace before the router's scratch (the layout
 // through out_acc for the scatter combine, through y's region otherwise).
 size_t layer_core_bytes(const size_t off[14], int combine) {
-  return combine == MOE_COMBINE_SCATTER ? off[13] : off[12];
+  return (combine & ~MOE_LAYER_SEPARATE_PERMUTE) == MOE_COMBINE_SCATTER ? off[13] : off[12];
 }
 
 // The layer on arguments already checked: the routing from the router front
@@ -409,6 +417,12 @@ int layer_run(const void *x, const void *w_router, const float *logits,
               const int32_t *topk_idx_in, const float *topk_w_in, const void *w_gate,
               const void *w_up, const void *w_down, int T, int H, int E, int k, int I, void *out,
               int combine, unsigned char *ws, const size_t off[14], int cus, hipStream_t s) {
+  // the reorder by route inside the gate/up GEMM's prologue (one launch
+  // fewer) where the shape allows, unless the caller asks for the separate
+  // permutation launch
+  const bool fused = !(combine & MOE_LAYER_SEPARATE_PERMUTE) &&
+                     moe::gg_fused_fits(I, H, T * k, E, cus);
+  combine &= ~MOE_LAYER_SEPARATE_PERMUTE;
   int32_t *idx = (int32_t *)(ws + off[0]);
   float *w = (float *)(ws + off[1]);
   int32_t *counts = (int32_t *)(ws + off[2]);
@@ -429,20 +443,33 @@ int layer_run(const void *x, const void *w_router, const float *logits,
   const int32_t *counted = nullptr; // expert counts from the router front end
   hipError_t e;
   if (w_router) {
-    // logits, top-k, softmax and the expert histogram in one launch
+    // logits, top-k, softmax and (for a separate permutation) the expert
+    // histogram it starts from
     e = moe::launch_router((const uint16_t *)x, (const uint16_t *)w_router, T, H, E, k, nullptr,
-                           idx, w, counts, ws + layer_core_bytes(off, combine), s);
+                           idx, w, fused ? nullptr : counts, ws + layer_core_bytes(off, combine),
+                           s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     ridx = idx;
     rw = w;
-    counted = counts;
+    counted = fused ? nullptr : counts;
   } else if (logits) {
     e = moe::launch_route(logits, T, E, k, idx, w, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     ridx = idx;
     rw = w;
   }
-  if (moe::permute_plan_fits(T, E, k)) {
+  // weights streamed (non-temporal loads) when the experts average at most
+  // two 128-row blocks: each weight tile is then read by about one row task
+  const bool stream_w = (long)T * k <= 2L * MOE_ROW_BLOCK * E;
+  if (fused) {
+    // the gate/up GEMM computes the permutation from the routing and writes
+    // it out (counts, offsets, row maps, block experts, M_pad, plan)
+    e = moe::launch_gate_up_fused((const uint16_t *)x, ridx, T, k, E, cap,
+                                  (const uint16_t *)w_gate, (const uint16_t *)w_up, !w_up, I, H,
+                                  h, counts, offsets, p2r, r2p, bexp, mpad, plan, cus, stream_w,
+                                  s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+  } else if (moe::permute_plan_fits(T, E, k)) {
     // permutation and the row-task plan in one launch
     e = moe::launch_permute_plan(ridx, T, E, k, cap, counts, offsets, p2r, r2p, bexp, mpad, plan,
                                  s, counted);
@@ -455,14 +482,13 @@ int layer_run(const void *x, const void *w_router, const float *logits,
     e = moe::launch_gg_plan(bexp, mpad, cap, plan, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
   }
-  // weights streamed (non-temporal loads) when the experts average at most
-  // two 128-row blocks: each weight tile is then read by about one row task
-  const bool stream_w = (long)T * k <= 2L * MOE_ROW_BLOCK * E;
-  e = moe::launch_grouped_gemm(MOE_BF16, I, H, (const uint16_t *)x, r2p, k,
-                               (const uint16_t *)w_gate, (const uint16_t *)w_up,
-                               w_up ? MOE_B_KN : MOE_B_KN_GATE_UP, plan,
-                               MOE_EPI_SILU_MUL, nullptr, nullptr, 0, h, cus, stream_w, s);
-  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  if (!fused) {
+    e = moe::launch_grouped_gemm(MOE_BF16, I, H, (const uint16_t *)x, r2p, k,
+                                 (const uint16_t *)w_gate, (const uint16_t *)w_up,
+                                 w_up ? MOE_B_KN : MOE_B_KN_GATE_UP, plan,
+                                 MOE_EPI_SILU_MUL, nullptr, nullptr, 0, h, cus, stream_w, s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+  }
   if (combine == MOE_COMBINE_SCATTER) {
     e = moe::launch_zero(oacc, (long)T * H, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
@@ -505,6 +531,7 @@ int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
 size_t moe_layer_router_workspace_size(int T, int H, int E, int k, int I, int combine) {
   size_t off[14];
   if (moe_layer_workspace_layout(T, H, E, k, I, off) != MOE_OK) return 0;
+  combine &= ~MOE_LAYER_SEPARATE_PERMUTE;
   if (combine != MOE_COMBINE_GATHER && combine != MOE_COMBINE_SCATTER) return 0;
   if (!moe::router_fits(H, E)) return 0;
   return layer_core_bytes(off, combine) + align256(moe::router_workspace_bytes(T, H, E));

@@ -107,7 +107,77 @@ struct GGArgs {
   int group_rows; // row tasks per super-block of the task order (>= 1)
   int ldb;        // [K][N] weights: elements per k row (N, or 2N interleaved)
   int b_il;       // gate/up interleaved in 128-column blocks in B (B2 unused)
+  // The fused form (LP): the kernel computes the permutation itself from
+  // the routing, builds its own row-task plan and A-row tables in LDS, and
+  // writes the permutation for the steps after it.
+  const int32_t *route_idx = nullptr; // [R] expert of each (token, slot) pair
+  int lp_R = 0, lp_E = 0, lp_cap = 0; // pairs, experts, row capacity
+  int32_t *o_counts = nullptr, *o_offsets = nullptr, *o_p2r = nullptr, *o_r2p = nullptr,
+          *o_bexp = nullptr, *o_mpad = nullptr, *o_plan = nullptr;
 };
+
+// Limits of the fused form: experts (one LDS scan over them) and pairs (the
+// routing staged in the 48 KiB A ring, which the A stream fills only after
+// the tables are built).
+constexpr int kLpMaxExperts = 256;
+constexpr int kLpMaxPairs = 12288;
+
+// Exclusive prefix sum of v over the NTH threads of the workgroup, in
+// thread order; `total` gets the sum.  wt: NTH / 64 ints of LDS.  Two
+// barriers, so wt is free again on return.
+template <int NTH>
+__device__ __forceinline__ int block_excl_scan(int v, int32_t *wt, int &total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) wt[wave] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NTH / 64; ++w) {
+    const int t = wt[w];
+    before += w < wave ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return before + incl - v;
+}
+
+// The routing staged in LDS: DMA of 64 ids per wavefront instruction (ids
+// past the last pair re-read the last one and are never used), one wait.
+template <int NTH>
+__device__ __forceinline__ void lp_stage(const int32_t *idx, int R, int32_t *ids) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // the LDS address is scalar
+  for (int c = wave * 64; c < R; c += NTH)
+    dma4(idx + min(c + lane, R - 1), lds_addr_of(ids + c));
+  wait_vmcnt<0>();
+  __syncthreads();
+}
+
+// The permutation's stable order by its definition: thread t takes pairs
+// t NS .. t NS + NS - 1 (NS = ceil(R / NTH) <= 32) as the bits of one mask
+// of matches, so a prefix sum over the threads of their match counts gives
+// each pair of expert e its rank among the pairs of e (ascending pair
+// index).  The thread reads its pairs rotated by its index, so the lanes of
+// a read spread over the banks.  f(p, rank) is called for every pair p of e.
+template <int NTH, class F>
+__device__ __forceinline__ void lp_each_of_expert(const int32_t *ids, int R, int e, int32_t *wt,
+                                                  F &&f) {
+  const int t = threadIdx.x;
+  const int NS = (R + NTH - 1) / NTH;
+  uint32_t mask = 0;
+  for (int u = 0; u < NS; ++u) {
+    const int j = (u + t) % NS, p = t * NS + j;
+    if (p < R && ids[p] == e) mask |= 1u << j;
+  }
+  int tot;
+  const int before = block_excl_scan<NTH>(__builtin_popcount(mask), wt, tot);
+  for (uint32_t m = mask; m; m &= m - 1) {
+    const int j = __builtin_ctz(m);
+    f(t * NS + j, before + __builtin_popcount(mask & ((1u << j) - 1u)));
+  }
+}
 
 // 16-byte-granule XOR swizzles of tiles stored with 64- or 128-byte rows
 // (A tiles and [N][K] B tiles: BK = 32 or 64 k of one row).  Both make the
@@ -293,7 +363,11 @@ __device__ __forceinline__ void scatter_tile(const f32x16 (&acc)[1][MI][NI], flo
 // (two per SIMD, 128 accumulators each: while one issues its fragment reads
 // and DMA, the other feeds the matrix pipe).  Each covers 128 rows and
 // BN / (WV / 2) columns of the task.
-template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR, bool BNT, int WV>
+// LP: the fused form -- the permutation is computed by the kernel from the
+// routing instead of read from a plan and row map built before it (see
+// GGArgs); SiLU*up on [K][N] weights with gathered A rows only.
+template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR, bool BNT, int WV,
+          bool LP = false>
 __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
   constexpr int NB = EPI == kEpiSiluMul ? 2 : 1; // B matrices
   constexpr int ARP = BK * 2;                    // bytes per A row (and [N][K] B row) per slice
@@ -344,15 +418,121 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
   const int wn = wave % WCOL;
   const int N = args.N, K = args.K;
   const int KT = K / BK;
-  const bool has_a = args.a_src_row != nullptr;
+  static_assert(!LP || (EPI == kEpiSiluMul && KN), "the fused form is the gate/up GEMM's");
+  const bool has_a = LP || args.a_src_row != nullptr;
   // the pair table `tab` holds a_src_row if given, else epi_row_pair; the
   // scatter's own epilogue table is needed only when both differ
   const int32_t *tab_src = has_a ? args.a_src_row : args.epi_row_pair;
-  const bool has_tab = tab_src != nullptr;
+  const bool has_tab = LP || tab_src != nullptr;
   const bool own_e = SCAT && has_a && args.epi_row_pair != args.a_src_row;
 
+  // ---------------- fused form: the permutation from the routing ----------------
+  // The routing is staged in the A ring and counted in LDS; the expert
+  // offsets and row-task offsets follow by two scans.  That fixes the task
+  // list, so the weight stream can start; the A-row tables of this
+  // workgroup's tasks are built while its first slices are in flight, and
+  // the permutation the later steps read is written after the main loop.
+  // (Compact loops throughout: this code runs once per workgroup, so its
+  // instruction fetch, not its arithmetic, is what it costs.)
+  constexpr int NTH = 64 * WV;
+  __shared__ int32_t lp_s[LP ? 3 * (kLpMaxExperts + 1) + 16 : 1];
+  int32_t *const lp_cnt = lp_s;
+  int32_t *const lp_off = lp_s + (kLpMaxExperts + 1);
+  int32_t *const lp_toff = lp_s + 2 * (kLpMaxExperts + 1);
+  int32_t *const lp_wt = lp_s + 3 * (kLpMaxExperts + 1);
+  int32_t *const lp_ids = reinterpret_cast<int32_t *>(aring);
+  int nrt, m_pad = 0;
+  if constexpr (LP) {
+    static_assert(!LP || NA * A_BYTES >= 4 * kLpMaxPairs, "the routing fits the A ring");
+    static_assert(!LP || kLpMaxPairs <= 32 * NTH, "a thread's pairs fit one mask");
+    const int R = args.lp_R, E = args.lp_E;
+    for (int e = tid; e < E; e += NTH) lp_cnt[e] = 0;
+    lp_stage<NTH>(args.route_idx, R, lp_ids);
+#pragma unroll 4
+    for (int p = tid; p < R; p += NTH) {
+      const int e = lp_ids[p];
+      if (e >= 0 && e < E) atomicAdd(&lp_cnt[e], 1);
+    }
+    __syncthreads();
+    // padded offsets and each expert's first row task (one thread per expert)
+    const int c = tid < E ? lp_cnt[tid] : 0;
+    const int padded = (c + kBM - 1) / kBM * kBM;
+    const int tasks = (padded / kBM + 1) / 2;
+    int mp, ntasks;
+    const int o = block_excl_scan<NTH>(padded, lp_wt, mp);
+    const int to = block_excl_scan<NTH>(tasks, lp_wt, ntasks);
+    if (tid < E) {
+      lp_off[tid] = o;
+      lp_toff[tid] = to;
+    }
+    if (tid == 0) {
+      lp_off[E] = mp;
+      lp_toff[E] = ntasks;
+    }
+    __syncthreads();
+    // the same in every lane (a value read from LDS is not known to be):
+    // the task addresses derived from it are wave-uniform scalars
+    nrt = __builtin_amdgcn_readfirstlane(ntasks);
+    m_pad = __builtin_amdgcn_readfirstlane(mp);
+  } else {
+    nrt = args.plan[0]; // read before any DMA is in flight
+  }
+
+  // The permutation the later steps read, written by the fused form at its
+  // end: the experts of this workgroup (their pairs' rows, padding rows,
+  // block experts, plan entries); workgroup 0 the counts, offsets, M_pad,
+  // the plan's head and the pairs routed outside [0, E); all of them,
+  // shared out, the rows and blocks past M_pad.  The routing is staged in
+  // the A ring again (every wavefront's DMA has landed and the rings are
+  // read).
+  auto lp_outputs = [&]() {
+    if constexpr (LP) {
+      const int R = args.lp_R, E = args.lp_E;
+      __syncthreads();
+      lp_stage<NTH>(args.route_idx, R, lp_ids);
+      // (the lambdas capture plain pointers: a reference to the kernel's
+      // argument block would move it to private memory, and every field read
+      // from there would no longer be known to be wave-uniform)
+      int32_t *const o_p2r = args.o_p2r, *const o_r2p = args.o_r2p;
+      for (int e = blockIdx.x; e < E; e += gridDim.x) {
+        const int r0 = lp_off[e], r1 = lp_off[e + 1];
+        lp_each_of_expert<NTH>(lp_ids, R, e, lp_wt, [=](int p, int rank) {
+          o_p2r[p] = r0 + rank;
+          o_r2p[r0 + rank] = p;
+        });
+        for (int r = r0 + lp_cnt[e] + tid; r < r1; r += NTH) o_r2p[r] = -1;
+        const int b0 = r0 / kBM, nbk = (r1 - r0) / kBM;
+        for (int b = tid; b < nbk; b += NTH) args.o_bexp[b0 + b] = e;
+        for (int q = tid; 2 * q < nbk; q += NTH) {
+          const int i = lp_toff[e] + q;
+          args.o_plan[kPlanHead + 2 * i] = (b0 + 2 * q) | (2 * q + 1 < nbk ? kPlanTwo : 0);
+          args.o_plan[kPlanHead + 2 * i + 1] = e;
+        }
+      }
+      if (blockIdx.x == 0) {
+        for (int e = tid; e < E; e += NTH) {
+          args.o_counts[e] = lp_cnt[e];
+          args.o_offsets[e] = lp_off[e];
+        }
+        if (tid == 0) {
+          args.o_offsets[E] = m_pad;
+          args.o_mpad[0] = m_pad;
+          args.o_plan[0] = nrt;
+          args.o_plan[1] = m_pad / kBM;
+        }
+      }
+      // (loops with the same trip count in every lane)
+      const int step = gridDim.x * NTH, cap = args.lp_cap;
+      for (int r0 = m_pad + (int)blockIdx.x * NTH; r0 < cap; r0 += step)
+        if (r0 + tid < cap) o_r2p[r0 + tid] = -1;
+      for (int b0 = m_pad / kBM + (int)blockIdx.x * NTH; b0 < cap / kBM; b0 += step)
+        if (b0 + tid < cap / kBM) args.o_bexp[b0 + tid] = -1;
+      for (int p0 = (int)blockIdx.x * NTH; p0 < R; p0 += step)
+        if (p0 + tid < R && (lp_ids[p0 + tid] < 0 || lp_ids[p0 + tid] >= E)) o_p2r[p0 + tid] = -1;
+    }
+  };
+
   // ---------------- schedule ----------------
-  const int nrt = args.plan[0]; // read before any DMA is in flight
   const int ncol = N / BN;
   const int ntask = nrt * ncol;
   const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
@@ -361,16 +541,49 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
   const int slot = blockIdx.x / nx;
   const int tx0 = (int)(((long)ntask * xcd) / nx);
   const int tx1 = (int)(((long)ntask * (xcd + 1)) / nx);
-  const int n_items = tx1 - tx0 > slot ? (tx1 - tx0 - slot + S - 1) / S : 0;
-  if (n_items == 0) return;
+  // the fused form builds the tables of at most kTabSlots items (the host
+  // bounds the task count so; more would not be computed)
+  const int n_items = min(tx1 - tx0 > slot ? (tx1 - tx0 - slot + S - 1) / S : 0,
+                          LP ? kTabSlots : 1 << 30);
+  if (n_items == 0) {
+    lp_outputs();
+    return;
+  }
   const int total = n_items * KT; // slices of this workgroup
   auto coords = [&](int i, int &rt, int &n0) {
     task_coords(tx0 + slot + i * S, args.group_rows, ncol, nrt, BN, rt, n0);
+    // wave-uniform: the weight stream addresses are scalar operands
+    rt = __builtin_amdgcn_readfirstlane(rt);
+    n0 = __builtin_amdgcn_readfirstlane(n0);
   };
-
+  if constexpr (LP) {
+    // the plan entries of this workgroup's items, from the offsets: row task
+    // rt is task rt - toff[e] of the expert e with toff[e] <= rt < toff[e+1]
+    // (each wavefront writes its own copy, as the DMA'd entries would be)
+    for (int i = 0; i < n_items; ++i) {
+      int rt, n0;
+      coords(i, rt, n0);
+      const int E = args.lp_E;
+      int lo = 0, hi = E - 1; // the last expert with toff <= rt (empty experts own no task)
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (lp_toff[mid] <= rt)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      const int q = rt - lp_toff[lo];
+      const int nbk = (lp_off[lo + 1] - lp_off[lo]) / kBM;
+      if (lane == 0) {
+        ptab[wave][i][0] = (lp_off[lo] / kBM + 2 * q) | (2 * q + 1 < nbk ? kPlanTwo : 0);
+        ptab[wave][i][1] = lo;
+      }
+    }
+  }
   // ---------------- per-task tables (DMA'd into small LDS rings) ----------------
   // DMA the plan entry of item i into this wavefront's slot (lanes 0, 1).
   auto fetch_plan = [&](int i) {
+    if constexpr (LP) return; // built in LDS above
     int rt, n0;
     coords(i, rt, n0);
     if (lane < 2)
@@ -386,7 +599,7 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
   // entry has landed).  Rows of the missing second block of a one-block
   // task repeat the first block's rows.
   auto fetch_tables = [&](int i) {
-    if (!has_tab) return;
+    if (LP || !has_tab) return; // LP: built in LDS above
     int b, nb, g;
     plan_of(i, b, nb, g);
     const int r = TR * wave + (lane % TR);
@@ -552,11 +765,36 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
   // s + LB - LA, the order of the main loop.  The tables were issued before
   // at least (LB - LA) B_LOADS DMA instructions (task starts may add more,
   // which only makes the wait stricter).
+  // The A-row tables of the fused form's items: table row r of item i is
+  // the pair of rank j0 + r among the pairs of its expert g (a one-block task
+  // repeats its 128 rows); ranks past the expert's count are padding (-1).
+  auto lp_tables = [&]() {
+    if constexpr (LP) {
+      for (int i = 0; i < n_items; ++i) {
+        int b, nb, g;
+        plan_of(i, b, nb, g);
+        const int j0 = b * kBM - lp_off[g];
+        for (int r = tid; r < kTM; r += NTH) tab[i][r] = -1;
+        __syncthreads();
+        int32_t *const trow = tab[i];
+        lp_each_of_expert<NTH>(lp_ids, args.lp_R, g, lp_wt, [=](int p, int rank) {
+          const int r = rank - j0;
+          if (r >= 0 && r < nb * kBM) {
+            trow[r] = p;
+            if (nb == 1) trow[r + kBM] = p;
+          }
+        });
+        __syncthreads();
+      }
+    }
+  };
+
   for (int j = 0; j < 4 && j < n_items; ++j) fetch_plan(j);
   wait_vmcnt<0>();
   for (int j = 0; j < 3 && j < n_items; ++j) fetch_tables(j);
   b_begin(0);
   for (int s = 0; s < LB - LA; ++s) b_issue();
+  lp_tables(); // the fused form: while the first weight slices are in flight
   wait_vmcnt<(LB - LA) * B_LOADS>();
   a_begin(0);
   for (int s = 0; s < LA; ++s) {
@@ -777,11 +1015,14 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
   }
   // drain any DMA still in flight before the workgroup retires its LDS
   wait_vmcnt<0>();
+  lp_outputs();
 }
 
-template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR, bool BNT, int WV = 4>
+template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR, bool BNT, int WV = 4,
+          bool LP = false>
 static hipError_t launch_one(const GGArgs &a, int grid, hipStream_t stream) {
-  grouped_gemm_kernel<BN, BK, EPI, KN, FP16, NA, NBR, BNT, WV><<<grid, 64 * WV, 0, stream>>>(a);
+  grouped_gemm_kernel<BN, BK, EPI, KN, FP16, NA, NBR, BNT, WV, LP>
+      <<<grid, 64 * WV, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -810,6 +1051,18 @@ inline bool tile_supported(int nbm, int bn, int bk, int na, int nb, int waves = 
 // Launch of one (epilogue, B layout, dtype, B cache policy) combination
 // with the tile shape c.  Explicitly instantiated in gg_inst.hip, one object
 // per combination; the dispatcher declares those instantiations extern.
+// The fused gate/up form (LP): bf16 [K][N] weights, the eight-wavefront
+// 128-column tile (shorter K, which takes the four-wavefront tiles, runs the
+// permutation as its own launch).
+inline bool lp_tile(const TileCfg &c) {
+  return c.bn == 128 && c.bk == 32 && c.waves == 8 && c.na == 3 && c.nb == 6;
+}
+template <bool BNT>
+hipError_t launch_lp(const GGArgs &a, const TileCfg &c, int grid, hipStream_t s) {
+  if (!lp_tile(c)) return hipErrorInvalidValue;
+  return launch_one<128, 32, kEpiSiluMul, true, false, 3, 6, BNT, 8, true>(a, grid, s);
+}
+
 template <int EPI, bool KN, bool FP16, bool BNT>
 hipError_t launch_bn(const GGArgs &a, const TileCfg &c, int grid, hipStream_t s) {
 #define MOE_GG_CASE(BNV, NAV, NBV)                                                            \

@@ -27,6 +27,8 @@ MOE_GG_EXTERN(kEpiSiluMul, true, true, true)
 MOE_GG_EXTERN(kEpiScatter, true, false, true)
 MOE_GG_EXTERN(kEpiScatter, true, true, true)
 #undef MOE_GG_EXTERN
+extern template hipError_t launch_lp<false>(const GGArgs &, const TileCfg &, int, hipStream_t);
+extern template hipError_t launch_lp<true>(const GGArgs &, const TileCfg &, int, hipStream_t);
 
 // Tile configurations: (BN, BK, A ring depth, B ring depth, super-block row
 // tasks, wavefronts).  Defaults: gate/up 128 gate + 128 up columns, down /
@@ -188,6 +190,54 @@ hipError_t launch_grouped_gemm(int dtype, int N, int K, const uint16_t *A,
                       : launch_bn<kEpiStore, true, false, false>(a, c, grid, stream);
   return fp16 ? launch_bn<kEpiStore, false, true, false>(a, c, grid, stream)
               : launch_bn<kEpiStore, false, false, false>(a, c, grid, stream);
+}
+
+// The fused gate/up GEMM (the reorder by route in its prologue): whether
+// this shape can take it.  The routing of R pairs to E experts is staged in
+// LDS (R <= kLpMaxPairs, E <= 256), the default SiLU*up tile must have a
+// fused instantiation, and no workgroup may get more than kTabSlots tasks:
+// with row tasks nrt = sum_e ceil(count_e / 256) <= R / 256 + min(E, R),
+// the task count is bounded before the routing is known.
+bool gg_fused_fits(int N, int K, int R, int E, int grid) {
+  if (E < 1 || E > kLpMaxExperts || R < 1 || R > kLpMaxPairs || N % 128 != 0 || grid < 1)
+    return false;
+  const TileCfg c = tile_config(kEpiSiluMul, N, K);
+  if (!lp_tile(c)) return false;
+  const long nrt_max = R / 256 + (E < R ? E : R);
+  const long ntask = nrt_max * (N / c.bn);
+  const int nx = grid % 8 == 0 ? 8 : 1;
+  const long S = grid / nx;
+  const long range = (ntask + nx - 1) / nx;
+  return (range + S - 1) / S <= kTabSlots;
+}
+
+// The fused gate/up GEMM: h = SiLU(x.Wg) * (x.Wu) over the permutation of
+// route_idx, which the kernel computes itself and writes out (counts,
+// offsets, pair_to_row, row_to_pair, block_expert, M_pad and the row-task
+// plan, as the permutation kernel would).  Gate and up weights interleaved
+// (il) or separate; x rows gathered as row_to_pair / k.
+hipError_t launch_gate_up_fused(const uint16_t *x, const int32_t *route_idx, int T, int k, int E,
+                                int cap, const uint16_t *B, const uint16_t *B2, bool il, int N,
+                                int K, uint16_t *h, int32_t *counts, int32_t *offsets,
+                                int32_t *p2r, int32_t *r2p, int32_t *bexp, int32_t *mpad,
+                                int32_t *plan, int grid, bool b_stream, hipStream_t stream) {
+  const int R = T * k;
+  if (!gg_fused_fits(N, K, R, E, grid)) return hipErrorInvalidValue;
+  const TileCfg c = tile_config(kEpiSiluMul, N, K);
+  GGArgs a{x, nullptr, k, B, il ? B : B2, nullptr, h, nullptr, nullptr, nullptr, 0, N, K, c.group,
+           il ? 2 * N : N, il ? 1 : 0};
+  a.route_idx = route_idx;
+  a.lp_R = R;
+  a.lp_E = E;
+  a.lp_cap = cap;
+  a.o_counts = counts;
+  a.o_offsets = offsets;
+  a.o_p2r = p2r;
+  a.o_r2p = r2p;
+  a.o_bexp = bexp;
+  a.o_mpad = mpad;
+  a.o_plan = plan;
+  return b_stream ? launch_lp<true>(a, c, grid, stream) : launch_lp<false>(a, c, grid, stream);
 }
 
 } // namespace moe

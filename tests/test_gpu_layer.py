@@ -241,3 +241,59 @@ def test_layer_hip_graph_replays(combine):
             assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), rep
         else:
             assert_close(to_f64(out), to_f64(eager), "graph scatter %d" % rep, max_frac=1e-2, rel_fro=2e-3)
+
+
+# ---------------------------------------------------------------- the fused front end
+
+def _fused_case(name):
+    if name in syn.CONFIGS:
+        return syn.make_config(name)
+    T, H, E, k, I, seed = name
+    d = syn.make_moe(T, H, E, k, I, seed=seed, routing="uniform_idx")
+    # a few pairs routed outside [0, E): they get no row and add nothing
+    d["topk_idx"][::37, 0] = -1
+    d["topk_idx"][5, k - 1] = E + 3
+    return d
+
+
+@pytest.mark.parametrize("name", ["tiny", "tp_share", "ep_skew", "ep_skew_small", (130, 64, 1, 1, 128, 3),
+                                  (40, 512, 3, 3, 256, 4), (1000, 256, 256, 8, 256, 5)],
+                         ids=lambda n: n if isinstance(n, str) else "T%d_H%d_E%d_k%d_I%d" % n[:5])
+def test_fused_front_end_same_bits(name):
+    # the reorder by route inside the gate/up GEMM's prologue against the
+    # separate permutation launch: the same permutation (every index array of
+    # the workspace, including the plan the down GEMM runs on), the same h on
+    # every real row, the same output bits
+    d = _fused_case(name)
+    T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
+    D = _inputs_dev(d)
+    wgu = moe.pack_gate_up(D["wg"], D["wu"])
+    kw = dict(logits=torch.from_numpy(d["logits"]).cuda()) if "logits" in d else dict(
+        topk_idx=torch.from_numpy(d["topk_idx"]).cuda(), topk_w=torch.from_numpy(d["topk_w"]).cuda())
+    say("fused front end", name)
+    res = []
+    for sep in (False, True):
+        ws = torch.full((moe.layer_workspace(T, H, E, k, I).numel(),), 0x7F, dtype=torch.uint8, device="cuda")
+        out = moe.layer(D["x"], wgu, None, D["wd"], k, workspace=ws, separate_permute=sep, **kw)
+        torch.cuda.synchronize()
+        res.append((out, ws))
+    (o1, w1), (o2, w2) = res
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    view = lambda ws, n: moe.workspace_view(ws, T, H, E, k, I, n)
+    for n in ["topk_idx", "expert_counts", "expert_offsets", "pair_to_row", "row_to_pair", "block_expert",
+              "num_padded_rows"]:
+        assert torch.equal(view(w1, n), view(w2, n)), n
+    lay = moe.layer_workspace_layout(T, H, E, k, I)
+    plan = lambda ws: ws[lay["gemm_scratch"]:lay["gemm_scratch"] + 8].view(torch.int32)
+    nrt = int(plan(w2)[0])
+    n = 4 * (2 + 2 * nrt)
+    assert torch.equal(w1[lay["gemm_scratch"]:lay["gemm_scratch"] + n], w2[lay["gemm_scratch"]:lay["gemm_scratch"] + n])
+    m_pad = int(view(w1, "num_padded_rows")[0])
+    real = view(w1, "row_to_pair")[:m_pad] >= 0
+    h1, h2 = view(w1, "h")[:m_pad][real], view(w2, "h")[:m_pad][real]
+    assert torch.equal(h1.view(torch.int16), h2.view(torch.int16))
+    if "logits" not in d:
+        # the given routing with ids outside [0, E): their pairs get no row
+        flat = d["topk_idx"].ravel()
+        bad = (flat < 0) | (flat >= E)
+        assert np.all(view(w1, "pair_to_row").cpu().numpy()[bad] == -1)

@@ -29,7 +29,9 @@ def _case(T, k, E, K, N, seed, epi, dense_values=True):
     Pm = oracle.permute(idx, E)
     cap = Pm["cap"]
     if dense_values:
-        A = syn.bf16_bits(g.standard_normal((T, K)).astype(np.float32))
+        # gate/up (epi 1) gathers A rows as row_to_pair / k: T rows; the store
+        # reads A row r for every row r below M_pad: cap rows
+        A = syn.bf16_bits(g.standard_normal((T if epi == 1 else cap, K)).astype(np.float32))
         B = syn.bf16_bits((g.standard_normal((E, K, N)) / np.sqrt(K)).astype(np.float32))
         B2 = syn.bf16_bits((g.standard_normal((E, K, N)) / np.sqrt(K)).astype(np.float32))
     else:  # integer values: the scatter's atomic sums are then unique
