@@ -95,7 +95,7 @@ def main():
             else:
                 rec["configs"][name] = bench_moe(a, name, headline=False)
             torch.cuda.empty_cache()
-    meta["clocks_after"] = gpu_clocks()
+    meta["clocks_after"] = gpu_clocks(getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None))
     rec["meta"] = meta
     print(json.dumps(rec), flush=True)
 
@@ -203,7 +203,11 @@ def bench_moe(a, name, headline):
     # the roofline of the dominant kernel, the gate/up GEMM: HBM-bound where
     # its FLOPs per byte stay under the ridge (peak FLOP/s / peak bytes/s)
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    gu_us = mean["gate_up"]
+    # the GEMM kernel alone on its prebuilt plan: 100 ms of it untimed, then
+    # launches back to back
+    n_roof = max(a.steps, 100)
+    gu_us = batch_us(lambda: moe.grouped_gemm(x, wgu, P.block_expert, P.num_padded_rows, out=h,
+                                              plan_ready=True, **gu_kw), n_roof)
     if gu_flops / gu_bytes < ridge:
         roof = {"bound": "hbm", "achieved": round(gu_bytes / (gu_us * 1e-6) / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "algorithmic_bytes": gu_bytes}
@@ -212,8 +216,9 @@ def bench_moe(a, name, headline):
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "algorithmic_flops": gu_flops}
     roof = {"kernel": "grouped_gemm gate/up (SiLU*up epilogue), the GEMM kernel alone", **roof,
             "frac": round(roof["achieved"] / roof["peak"], 4),
-            "duration_us": round(gu_us, 2), "duration_median_us": round(dur["gate_up"], 2),
-            "launches": len(timed),
+            "duration_us": round(gu_us, 2), "launches": n_roof,
+            "timing": "one HIP event pair around %d back-to-back launches, after 100 ms of the "
+                      "same untimed" % n_roof,
             "traffic": recorded_traffic("grouped_gemm_gate_up_%s" % name)}
 
     rec = {
@@ -425,25 +430,20 @@ def bench_dense(a, headline):
     settle_steps = settle(step, a.settle_ms if headline else a.settle_ms / 2)
     for _ in range(a.warmup):
         step()
-    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(a.steps):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / a.steps
-    # the GEMM kernel alone (its plan built by the calls above), per launch
-    ev = []
-    for it in range(a.warmup + a.steps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        moe.grouped_gemm(A, B, bg, nr, N=N, K=K, cap=M, b_layout="nk", out=D, workspace=ws,
-                         plan_ready=True)
-        e1.record(stream)
-        if it >= a.warmup:
-            ev.append((e0, e1))
-    torch.cuda.synchronize()
-    us = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e3
+    # the GEMM kernel alone (its plan built by the calls above), launches
+    # back to back after 100 ms of the same: five batches, the mean of their
+    # per-launch means
+    n_batch = max(a.steps // 5, 20)
+    us = np.array([batch_us(lambda: moe.grouped_gemm(A, B, bg, nr, N=N, K=K, cap=M, b_layout="nk",
+                                                     out=D, workspace=ws, plan_ready=True), n_batch,
+                            settle_ms=100.0 if i == 0 else 0.0)
+                   for i in range(5)])
     kern_us = float(np.mean(us))
     flops = 2.0 * M * N * K
     tf = flops / (kern_us * 1e-6) / 1e12
@@ -454,11 +454,12 @@ def bench_dense(a, headline):
         "dtype": "fp16", "data": "synthetic",
         "config": {"workload": "dense fp16 GEMM M=N=K=4096, D = A.B^T, fp32 accumulate"},
         "step_us": round(ms * 1e3, 2),
-        "kernel_us": round(kern_us, 2), "kernel_us_median": round(float(np.median(us)), 2),
+        "kernel_us": round(kern_us, 2), "kernel_us_batches": [round(float(u), 2) for u in us],
         "roofline": {"kernel": "grouped_gemm (one group, B [N][K], fp16), the GEMM kernel alone",
                      "bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                     "duration_us": round(kern_us, 2), "algorithmic_flops": flops, "launches": len(us),
+                     "duration_us": round(kern_us, 2), "algorithmic_flops": flops, "launches": 5 * n_batch,
+                     "timing": "five HIP event pairs, each around %d back-to-back launches" % n_batch,
                      "traffic": None},
         "input_sha256": sha,
     }
@@ -482,24 +483,38 @@ def input_sha256(d):
     return out
 
 
-def gpu_clocks():
-    """Current clock levels and power of the GPU as rocm-smi reports them
-    (the clocks are recorded, not locked); None where the tool is missing."""
-    import subprocess
-    cmd = ["rocm-smi", "--showclocks", "--showpower", "--showmaxpower", "--json"]
-    try:
-        r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
-    except (OSError, subprocess.SubprocessError):
+def gpu_clocks(pci_bus=None):
+    """Current shader and memory clock levels and the power figures of the
+    GPU, read from the amdgpu driver's sysfs files (the clocks are recorded,
+    not locked); None where they are not readable.  No tool is started, so
+    this also works under a profiler that preloads itself into children."""
+    import glob
+    devs = sorted(os.path.dirname(f) for f in glob.glob("/sys/class/drm/card[0-9]*/device/pp_dpm_sclk"))
+    if pci_bus is not None:
+        same = [d for d in devs if os.path.basename(os.path.realpath(d)).split(":")[1:2] == ["%02x" % pci_bus]]
+        devs = same or devs
+    if not devs:
         return None
-    if r.returncode != 0 or not r.stdout.strip():
-        return None
-    try:
-        js = json.loads(r.stdout)
-    except ValueError:
-        return None
-    cards = sorted(c for c in js if c.startswith("card"))
-    return {"tool": "rocm-smi", "card": cards[0] if cards else None,
-            "values": js[cards[0]] if cards else js}
+    dev = devs[0]
+
+    def read(path):
+        try:
+            with open(path) as f:
+                return f.read()
+        except OSError:
+            return None
+
+    out = {"card": os.path.basename(os.path.dirname(dev)), "pci": os.path.basename(os.path.realpath(dev))}
+    for key in ("sclk", "mclk"):
+        txt = read(os.path.join(dev, "pp_dpm_%s" % key)) or ""
+        cur = [ln.strip() for ln in txt.splitlines() if ln.rstrip().endswith("*")]
+        out[key] = cur[0] if cur else None
+    for hw in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))):
+        for name in ("power1_cap", "power1_average", "power1_input"):
+            v = read(os.path.join(hw, name))
+            if v is not None and v.strip().isdigit():
+                out[name + "_w"] = int(v) / 1e6
+    return out
 
 
 def run_meta(torch):
@@ -508,7 +523,8 @@ def run_meta(torch):
     return {"numpy": np.__version__, "torch": torch.__version__, "hip": torch.version.hip,
             "device": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
             "host_cpu": platform.processor() or platform.machine(),
-            "host_threads": len(os.sched_getaffinity(0)), "clocks_before": gpu_clocks()}
+            "host_threads": len(os.sched_getaffinity(0)),
+            "clocks_before": gpu_clocks(getattr(p, "pci_bus_id", None))}
 
 
 CSRC = os.path.join(ROOT, "moe_expert_grouped_amd", "csrc")
@@ -562,6 +578,28 @@ def graph_batch_us(fn, n):
     e1.record(stream)
     torch.cuda.synchronize()
     del graph
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def batch_us(fn, n, settle_ms=100.0, lead=4):
+    """Mean duration of one call of `fn` (one kernel launch): `n` calls
+    enqueued back to back between one pair of HIP events on the launch
+    stream.  The same call runs untimed for `settle_ms` first (from idle the
+    shader clock needs some tens of milliseconds of load to reach its
+    steady level), then `lead` more so the host is ahead of the GPU and the
+    queue never runs dry inside the timed region; one event pair per batch
+    keeps the marker packets' own few microseconds out of the figure."""
+    import torch
+    settle(fn, settle_ms)
+    stream = torch.cuda.current_stream()
+    for _ in range(lead):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / n
 
 
