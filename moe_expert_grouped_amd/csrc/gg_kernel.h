@@ -51,9 +51,9 @@
 //   * v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulators; with WV
 //     wavefronts, wavefront (wm, wn) owns rows [128 wm, 128 wm + 128) and
 //     columns [WC wn, WC wn + WC) of each B matrix, WC = BN / (WV / 2).  A
-//     one-block task loads its 128 rows twice; the second copy's products
-//     are not stored (they hide under the weight stream in the HBM-bound
-//     shapes, and keep one fixed register layout);
+//     one-block task loads its 128 rows twice (one fixed register layout);
+//     the second copy's products are not stored, and in the streamed-weight
+//     form neither they nor those of all-padding 32-row groups are computed;
 //   * the store epilogues convert pairs with one packed instruction and go
 //     through LDS (the stages of the slice just consumed) so each store
 //     writes whole row pieces; the weighted scatter adds with fp32 atomics.
@@ -866,10 +866,20 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
   };
   // matrix instruction t of a k step on buffer BUF (row group fastest)
   constexpr int NM = NB * NI * 4;
+  // Bit mi: this wavefront's 32-row group mi of the current item has a row
+  // whose product is used (wave-uniform, set at each item's start).  Only
+  // the streamed-weight form (BNT) skips the others: there each weight tile
+  // is read about once, the kernel waits on HBM and the skipped matrix work
+  // is pure saving (tp_share layer -4.6 %, ep_skew -5 %), while in the
+  // MFMA-bound shapes the predicate on every matrix instruction costs more
+  // than the little padding saves (dense +5 %, prefill +9 %).
+  uint32_t live = 0xF;
   auto mma = [&](auto T, auto BUF) {
     constexpr int t = decltype(T)::value;
     constexpr int buf = decltype(BUF)::value;
     constexpr int m = t / (4 * NI), j = (t / 4) % NI, mi = t % 4;
+    if constexpr (BNT)
+      if (!(live & (1u << mi))) return;
     // the weighted scatter keeps the row-major accumulator layout (its fp32
     // atomics then cover 32 contiguous columns per row); the stores take the
     // transposed one (weights as the first operand)
@@ -936,6 +946,25 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
     int rt, n0, b, nb, g;
     coords(i, rt, n0);
     plan_of(i, b, nb, g);
+    // Matrix instructions whose products nobody reads (BNT only): all of
+    // them for an item of no group, those of the second half of a one-block
+    // task (a copy of the first), and a 32-row group whose rows are all
+    // padding (pair < 0 in the item's table; the epilogues do not store or
+    // add such rows).  Their accumulators stay zero.
+    if (!BNT) {
+      live = 0xF;
+    } else if (g < 0 || (nb == 1 && wm == 1)) {
+      live = 0;
+    } else if (has_tab) {
+      const MOE_LDS int32_t *trow = (const MOE_LDS int32_t *)tab[i % kTabSlots] + wm * 128;
+      uint32_t lv = 0;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        lv |= (__builtin_amdgcn_ballot_w64(lane < 32 && trow[mi * 32 + lane] >= 0) != 0) << mi;
+      live = __builtin_amdgcn_readfirstlane(lv);
+    } else {
+      live = 0xF;
+    }
     for (int kt = 0; kt < KT; ++kt, ++c) {
       // k step 0 on buffer 0: its fragments (read during the previous
       // matrix instructions) are in -- said explicitly, so no LDS wait lands
