@@ -304,7 +304,10 @@ def moe_headline_legs(a, d, v):
         step()
     for _ in range(a.warmup):
         graph.replay()
-    stats_graph = step_stats(graph.replay, a.steps, cold=False)
+    # back-to-back replays between one event pair: an event pair around each
+    # replay would also hold the host's graph-launch time before the first
+    # kernel (the GPU is idle by then), not the step's
+    graph_us = batch_us(graph.replay, max(a.steps, 50), settle_ms=50.0)
     del graph
 
     def step_unpacked():
@@ -389,19 +392,29 @@ def moe_headline_legs(a, d, v):
 
     for _ in range(a.warmup):
         step_router()
-    stats_router = step_stats(step_router, a.steps, cold=False)
+    # interleaved with the layer from logits, so both see the same clocks;
+    # back-to-back steps between one event pair per round
+    n_r = max(a.steps // 5, 10)
+    ab_router = {"from_logits": [], "from_router": []}
+    for _ in range(5):
+        ab_router["from_logits"].append(round(batch_us(step, n_r, settle_ms=0.0), 2))
+        ab_router["from_router"].append(round(batch_us(step_router, n_r, settle_ms=0.0), 2))
     # the row gather alone: the permutation with it minus the permutation
     batched["gather"] = batched["permute_with_gather"] - batched["permute"]
     del ys, xps
     return {
         "kernel_us_batched": {n: round(t, 2) for n, t in batched.items()},
-        "hip_graph": {"layer_us_per_step": stats_graph},
+        "hip_graph": {"layer_us_per_step": round(graph_us, 2),
+                      "timing": "one HIP event pair around %d back-to-back replays" % max(a.steps, 50)},
         "unpacked_gate_up_weights": {"layer_us_per_step": stats_unpacked},
         "front_end_ab": {"what": "layer step medians (us), 5 interleaved rounds: the reorder by route "
                                  "inside the gate/up GEMM prologue (fused, the default) against the "
                                  "permutation as its own launch (separate)",
                          "fused": ab["fused"], "separate": ab["separate"]},
-        "layer_with_router_front_end": {"layer_us_per_step": stats_router},
+        "layer_with_router_front_end": {
+            "what": "layer us per step, 5 interleaved rounds of %d back-to-back steps: from the "
+                    "router logits (route kernel) against from x and W_r (moe_layer_router)" % n_r,
+            **ab_router},
         "scatter_combine": {"layer_us_per_step": stats_scatter,
                             "kernel_us": {n: round(t * 1e3, 2) for n, t in dur_sc.items()}},
         "measured_peaks": measured_peaks(),
