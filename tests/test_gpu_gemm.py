@@ -403,6 +403,65 @@ def test_streamed_weights_same_bits(dtype, epi, layout):
     assert torch.equal(plain.view(iv), streamed.view(iv))
 
 
+@pytest.mark.parametrize("epi,layout", [("store", "kn"), ("silu_mul", "kn_gate_up"), ("weighted_scatter", "kn")])
+def test_streamed_form_skips_only_dead_row_groups(epi, layout):
+    # The streamed-weight form skips the matrix instructions of the second
+    # half of a one-block task and of 32-row groups that are all padding.
+    # Expert sizes that make every case: an empty expert, one-block experts
+    # whose last 1, 2 or 3 groups are dead (1, 10, 33, 96 rows), a full block,
+    # two-block tasks whose second block holds 1 row or three live groups
+    # (129, 200 rows).  Every real row: the same bits as the plain form, and
+    # (store, scatter) the oracle's exact result.
+    counts = [1, 10, 33, 96, 97, 0, 129, 128, 200]
+    E, K = len(counts), 192
+    N = 128 if epi == "silu_mul" else 256
+    g = np.random.default_rng(91)
+    ids = g.permutation(np.repeat(np.arange(E, dtype=np.int32), counts)).reshape(-1, 1)
+    T = ids.shape[0]
+    P = oracle.permute(ids, E)
+    cap, m_pad, r2p = P["cap"], P["m_pad"], P["row_to_pair"]
+    assert list(P["counts"]) == counts
+    real = np.nonzero(r2p[:m_pad] >= 0)[0]
+    A = syn.ternary_bits((T if epi == "silu_mul" else cap, K), 92)
+    B = syn.ternary_bits((E, K, N), 93)
+    B2 = syn.ternary_bits((E, K, N), 94) if epi == "silu_mul" else None
+    w = g.choice(np.array([0.25, 0.5, 1.0, 2.0, -1.0], np.float32), size=(T, 1))
+    At, Bt = dev16(A), dev16(B)
+    B2t = dev16(B2) if B2 is not None else None
+    if layout == "kn_gate_up":
+        Bt, B2t = moe.pack_gate_up(Bt, B2t), None
+    bexp = torch.from_numpy(P["block_expert"]).cuda()
+    mpad = torch.tensor([m_pad], dtype=torch.int32, device="cuda")
+    r2pt = torch.from_numpy(r2p).cuda()
+    say("streamed skip", epi, layout, "rows", T, "m_pad", m_pad)
+
+    def run(stream):
+        if epi == "weighted_scatter":
+            return moe.grouped_gemm(At, Bt, bexp, mpad, N=N, K=K, cap=cap, epilogue=epi, row_pair=r2pt,
+                                    pair_w=torch.from_numpy(w).cuda(), b_stream=stream)
+        out = torch.full((cap, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        if epi == "silu_mul":
+            return moe.grouped_gemm(At, Bt, bexp, mpad, N=N, K=K, cap=cap, a_src_row=r2pt, a_src_div=1,
+                                    B2=B2t, b_layout=layout, epilogue=epi, out=out, b_stream=stream)
+        return moe.grouped_gemm(At, Bt, bexp, mpad, N=N, K=K, cap=cap, row_pair=r2pt, out=out,
+                                b_stream=stream)
+    plain, streamed = run(False), run(True)
+    torch.cuda.synchronize()
+    if epi == "weighted_scatter":
+        assert torch.equal(plain.view(torch.int32), streamed.view(torch.int32))
+        Y = oracle.grouped_gemm(A, B, P["block_expert"], N=N, K=K)
+        ref = oracle.weighted_scatter(Y, r2p, w, 1, T)
+        assert np.array_equal(streamed.cpu().numpy().astype(np.float64), ref)
+        return
+    rt = torch.from_numpy(real).cuda()
+    assert torch.equal(plain[rt].view(torch.int16), streamed[rt].view(torch.int16))
+    pad = np.nonzero(r2p[:m_pad] < 0)[0]
+    assert torch.isnan(streamed[torch.from_numpy(pad).cuda()]).all()   # padding rows not written
+    if epi == "store":
+        ref = oracle.grouped_gemm(A, B, P["block_expert"], N=N, K=K, rows=real)
+        assert np.array_equal(to_f64(streamed)[real], ref)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("T,k,E,K,N", [(150, 3, 4, 320, 256), (200, 1, 5, 64, 128), (90, 2, 3, 128, 192)])
 def test_weighted_scatter_integer_exact(dtype, T, k, E, K, N):
