@@ -1069,7 +1069,8 @@ struct TileCfg {
 inline bool tile_supported(int nbm, int bn, int bk, int na, int nb, int waves = 4) {
   if (bk != 32) return false;
   // eight wavefronts: the full-size rings of the default tiles, no scatter
-  if (waves == 8) return na == 3 && nb == 6 && ((nbm == 1 && bn == 256) || (nbm == 2 && bn == 128));
+  if (waves == 8)
+    return na == 3 && ((nbm == 1 && bn == 256 && nb == 6) || (nbm == 2 && bn == 128 && (nb == 6 || nb == 4)));
   if (waves != 4) return false;
   if (na == 4 && nb == 4) return bn == 64 || bn == 128 || (bn == 256 && nbm == 1);
   if (nbm == 2) return (bn == 128 && na == 3 && nb == 6) || (bn == 64 && na == 3 && nb == 10);
@@ -1084,12 +1085,12 @@ inline bool tile_supported(int nbm, int bn, int bk, int na, int nb, int waves = 
 // 128-column tile (shorter K, which takes the four-wavefront tiles, runs the
 // permutation as its own launch).
 inline bool lp_tile(const TileCfg &c) {
-  return c.bn == 128 && c.bk == 32 && c.waves == 8 && c.na == 3 && c.nb == 6;
+  return c.bn == 128 && c.bk == 32 && c.waves == 8 && c.na == 3 && c.nb == 4;
 }
 template <bool BNT>
 hipError_t launch_lp(const GGArgs &a, const TileCfg &c, int grid, hipStream_t s) {
   if (!lp_tile(c)) return hipErrorInvalidValue;
-  return launch_one<128, 32, kEpiSiluMul, true, false, 3, 6, BNT, 8, true>(a, grid, s);
+  return launch_one<128, 32, kEpiSiluMul, true, false, 3, 4, BNT, 8, true>(a, grid, s);
 }
 
 template <int EPI, bool KN, bool FP16, bool BNT>
@@ -1102,7 +1103,7 @@ hipError_t launch_bn(const GGArgs &a, const TileCfg &c, int grid, hipStream_t s)
     return launch_one<BNV, 32, EPI, KN, FP16, NAV, NBV, BNT, 8>(a, grid, s);
   if constexpr (EPI == kEpiSiluMul) {
     MOE_GG_CASE(128, 3, 6) MOE_GG_CASE(128, 4, 4) MOE_GG_CASE(64, 3, 10) MOE_GG_CASE(64, 4, 4)
-    MOE_GG_CASE8(128, 3, 6)
+    MOE_GG_CASE8(128, 3, 6) MOE_GG_CASE8(128, 3, 4)
   } else {
     MOE_GG_CASE(256, 3, 6) MOE_GG_CASE(256, 4, 4) MOE_GG_CASE(128, 3, 10) MOE_GG_CASE(128, 4, 4)
     MOE_GG_CASE(64, 4, 8) MOE_GG_CASE(64, 4, 4)

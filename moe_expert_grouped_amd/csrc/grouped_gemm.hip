@@ -34,7 +34,9 @@ extern template hipError_t launch_lp<true>(const GGArgs &, const TileCfg &, int,
 // tasks, wavefronts).  Defaults: gate/up 128 gate + 128 up columns, down /
 // dense 256 columns (128 when N is not a multiple of 256, 64 below that),
 // 32-deep slices, a 3-deep A ring and a 6-deep B ring (weights are most of
-// the bytes in flight); the 128 / 256-column tiles with eight wavefronts
+// the bytes in flight; gate/up takes a 4-deep one, which measured 2-5 %
+// faster where the weights stream and the same where they are re-read,
+// while down was faster with 6); the 128 / 256-column tiles with eight wavefronts
 // (two per SIMD: one's matrix instructions run while the other issues its
 // fragment reads and DMA), except for the weighted scatter.  A configuration
 // is used only if it is instantiated, divides N, and its B ring keeps the
@@ -55,7 +57,7 @@ static TileCfg tile_config(int epilogue, int N, int K) {
   // weighted scatter
   const int w = epilogue == kEpiScatter ? 4 : 8;
   if (epilogue == kEpiSiluMul)
-    c = N % 128 == 0 ? TileCfg{128, 32, 3, 6, 1, w} : TileCfg{64, 32, 3, 10, 1};
+    c = N % 128 == 0 ? TileCfg{128, 32, 3, w == 8 ? 4 : 6, 1, w} : TileCfg{64, 32, 3, 10, 1};
   else
     c = N % 256 == 0 ? TileCfg{256, 32, 3, 6, 1, w}
                      : (N % 128 == 0 ? TileCfg{128, 32, 3, 10, 1} : TileCfg{64, 32, 4, 8, 1});

@@ -193,7 +193,8 @@ def test_store_many_items_dtypes_layouts(dtype, layout, K):
     assert np.all(np.isnan(got[:c["m_rows"]][~real]))
 
 
-SILU_TILES = [(None, 128), ((128, 32, 3, 6, 1, 8), 320), ((128, 32, 3, 6, 1, 4), 128),
+SILU_TILES = [(None, 128), ((128, 32, 3, 6, 1, 8), 320), ((128, 32, 3, 4, 1, 8), 64),
+              ((128, 32, 3, 4, 1, 8), 320), ((128, 32, 3, 6, 1, 4), 128),
               ((128, 32, 4, 4, 1, 4), 64), ((128, 32, 4, 4, 2, 4), 128), ((64, 32, 3, 10, 1, 4), 320),
               ((64, 32, 4, 4, 1, 4), 64)]
 
