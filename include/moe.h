@@ -95,6 +95,23 @@ extern "C" {
  * 16384 (token, slot) pairs, at most 256 experts, I % 128 == 0, and a
  * bounded number of tasks per workgroup.  Same results either way. */
 #define MOE_LAYER_SEPARATE_PERMUTE 0x100
+/* Flag OR-ed into the combine of moe_layer_ex / moe_layer_router: split K
+ * ([P2 s.5]: with less than one wave of tasks the compute units stand idle).
+ * A GEMM of the layer whose tasks ((row task, column block) pairs; at most
+ * floor((T*k + 255*min(E, T*k)) / 256) row tasks) fit one wave of the
+ * compute units, and whose k range holds at least 2 x 512 values, runs each
+ * task's k range in 4 equal parts (2 when K holds fewer, or the workspace
+ * room does), each part a task of its own writing fp32 partial sums into
+ * the y region of the workspace; a reduction then adds the parts in part
+ * order and applies the epilogue (after gate/up: SiLU*up into h, the
+ * permutation then running as its own launch; after down, with
+ * MOE_COMBINE_GATHER: the weighted combine, y never stored).  Deterministic,
+ * but rounded differently from the unsplit sums.  It pays where few row
+ * tasks are actually routed -- measured on MI355X, T=16 tokens over 16
+ * experts (I=2048): 101 against 137 us -- and costs where the actual tasks
+ * nearly fill the CUs (T=128: 143 against 140 us), which the host cannot
+ * see before the routing runs on the device; so it is the caller's choice. */
+#define MOE_LAYER_SPLIT_K 0x200
 
 #define MOE_ROW_BLOCK 128 /* rows per task and per-expert alignment unit [P1 s.4] */
 

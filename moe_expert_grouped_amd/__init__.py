@@ -37,6 +37,7 @@ ROW_BLOCK = 128
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 MOE_B_STREAM = 0x100  # flag on a [K][N] b_layout: non-temporal weight loads
 MOE_LAYER_SEPARATE_PERMUTE = 0x100  # flag on a layer's combine: the permutation as its own launch
+MOE_LAYER_SPLIT_K = 0x200  # flag on a layer's combine: GEMMs below one wave of tasks split K
 _DTYPES = {torch.bfloat16: 0, torch.float16: 1}
 _LAYOUTS = {"kn": 0, "nk": 1, "kn_gate_up": 2}
 _EPIS = {"store": 0, "silu_mul": 1, "weighted_scatter": 2}
@@ -403,14 +404,16 @@ def layer(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: tor
           logits: torch.Tensor | None = None, topk_idx: torch.Tensor | None = None,
           topk_w: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
           out: torch.Tensor | None = None, combine: str = "gather",
-          separate_permute: bool = False) -> torch.Tensor:
+          separate_permute: bool = False, split_k: bool = False) -> torch.Tensor:
     """The MoE layer share: route (or the given routing) -> permute -> gate/up
     grouped GEMM with SiLU*up -> down grouped GEMM -> top-k weighted combine.
     w_up=None: w_gate is the interleaved [E][H][2I] tensor of pack_gate_up.
     combine="gather" (deterministic) stores y and runs the combine kernel;
     "scatter" folds the weighted sum into the down GEMM's epilogue.  The
     permutation runs inside the gate/up GEMM's prologue where the shape
-    allows; separate_permute=True gives it its own launch (same results)."""
+    allows; separate_permute=True gives it its own launch (same results).
+    split_k=True: a GEMM with at most one wave of tasks splits its k range
+    (fp32 partial sums, reduced in a fixed order; MOE_LAYER_SPLIT_K)."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w_gate, "w_gate", torch.bfloat16, 3)
     if w_up is not None:
@@ -429,28 +432,33 @@ def layer(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: tor
         workspace = layer_workspace(T, H, E, k, I, x.device, combine)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
-    if combine == "gather" and not separate_permute:
+    if combine == "gather" and not separate_permute and not split_k:
         _check("moe_layer", load_library().moe_layer(
             _ptr(x), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
             _ptr(w_down), T, H, E, k, I, _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
     else:
         _check("moe_layer_ex", load_library().moe_layer_ex(
             _ptr(x), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
-            _ptr(w_down), T, H, E, k, I, _ptr(out),
-            _COMBINES[combine] | (MOE_LAYER_SEPARATE_PERMUTE if separate_permute else 0),
+            _ptr(w_down), T, H, E, k, I, _ptr(out), _layer_flags(combine, separate_permute, split_k),
             _ptr(workspace), workspace.numel(), _stream()))
     return out
+
+
+def _layer_flags(combine, separate_permute, split_k):
+    return (_COMBINES[combine] | (MOE_LAYER_SEPARATE_PERMUTE if separate_permute else 0) |
+            (MOE_LAYER_SPLIT_K if split_k else 0))
 
 
 def layer_router(x: torch.Tensor, w_router: torch.Tensor, w_gate: torch.Tensor,
                  w_up: torch.Tensor | None, w_down: torch.Tensor, k: int,
                  workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                 combine: str = "gather", separate_permute: bool = False) -> torch.Tensor:
+                 combine: str = "gather", separate_permute: bool = False,
+                 split_k: bool = False) -> torch.Tensor:
     """The MoE layer share from the token rows and the router weights: the
     router front end (logits, top-k, softmax; the expert counts too when the
     permutation runs separately), then the permutation, the two grouped GEMMs
-    and the combine.  The workspace holds the moe_layer_workspace_layout
-    regions first, then the router's scratch."""
+    and the combine (split K as in layer()).  The workspace holds the
+    moe_layer_workspace_layout regions first, then the router's scratch."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w_router, "w_router", torch.bfloat16, 2)
     _need(w_gate, "w_gate", torch.bfloat16, 3)
@@ -471,8 +479,7 @@ def layer_router(x: torch.Tensor, w_router: torch.Tensor, w_gate: torch.Tensor,
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     _check("moe_layer_router", lib.moe_layer_router(
         _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), T, H, E, k, I, _ptr(out),
-        _COMBINES[combine] | (MOE_LAYER_SEPARATE_PERMUTE if separate_permute else 0), _ptr(workspace),
-        workspace.numel(), _stream()))
+        _layer_flags(combine, separate_permute, split_k), _ptr(workspace), workspace.numel(), _stream()))
     return out
 
 

@@ -25,7 +25,12 @@ hipError_t launch_permute(const int32_t *, int, int, int, const uint16_t *, int,
 hipError_t launch_grouped_gemm(int, int, int, const uint16_t *, const int32_t *, int,
                                const uint16_t *, const uint16_t *, int, const int32_t *, int,
                                const int32_t *, const float *, int, void *, int, bool,
-                               hipStream_t, const int32_t *tile = nullptr);
+                               hipStream_t, const int32_t *tile = nullptr, int ksplit = 1,
+                               float *Dpart = nullptr, int part_R = 0);
+hipError_t launch_splitk_silu(const float *, int, int, int, const int32_t *, uint16_t *,
+                              hipStream_t);
+hipError_t launch_splitk_combine(const float *, int, int, int, int, const int32_t *,
+                                 const float *, uint16_t *, hipStream_t);
 bool gg_tile_usable(const int32_t *tile, int epilogue, int N, int K);
 hipError_t launch_gg_plan(const int32_t *, const int32_t *, int, int32_t *, hipStream_t);
 bool gg_fused_fits(int N, int K, int R, int E, int grid);
@@ -44,6 +49,8 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 constexpr int kDefaultCus = 256; // sizing when no device is visible (MI355X)
+// flags a layer's combine argument may carry
+constexpr int kLayerFlags = MOE_LAYER_SEPARATE_PERMUTE | MOE_LAYER_SPLIT_K;
 std::mutex g_mu;
 int g_cus[kMaxDevices]; // 0 = not queried yet
 
@@ -368,7 +375,7 @@ size_t moe_layer_workspace_size(int T, int H, int E, int k, int I) {
 size_t moe_layer_workspace_size_ex(int T, int H, int E, int k, int I, int combine) {
   size_t off[14];
   if (moe_layer_workspace_layout(T, H, E, k, I, off) != MOE_OK) return 0;
-  combine &= ~MOE_LAYER_SEPARATE_PERMUTE;
+  combine &= ~kLayerFlags;
   if (combine == MOE_COMBINE_GATHER) return off[12]; // out_acc, last, is the scatter's only
   return combine == MOE_COMBINE_SCATTER ? off[13] : 0;
 }
@@ -398,8 +405,8 @@ int check_layer(const void *x, const void *w_gate, const void *w_up, const void 
   if (!w_up && I % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (E > 1024 || k > 16) return MOE_ERR_UNSUPPORTED;
   if ((long)T * k > 0x7fffffffL / 2) return MOE_ERR_UNSUPPORTED;
-  if ((combine & ~MOE_LAYER_SEPARATE_PERMUTE) != MOE_COMBINE_GATHER &&
-      (combine & ~MOE_LAYER_SEPARATE_PERMUTE) != MOE_COMBINE_SCATTER)
+  if ((combine & ~kLayerFlags) != MOE_COMBINE_GATHER &&
+      (combine & ~kLayerFlags) != MOE_COMBINE_SCATTER)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -407,7 +414,25 @@ int check_layer(const void *x, const void *w_gate, const void *w_up, const void 
 // Bytes of the layer workspace before the router's scratch (the layout
 // through out_acc for the scatter combine, through y's region otherwise).
 size_t layer_core_bytes(const size_t off[14], int combine) {
-  return (combine & ~MOE_LAYER_SEPARATE_PERMUTE) == MOE_COMBINE_SCATTER ? off[13] : off[12];
+  return (combine & ~kLayerFlags) == MOE_COMBINE_SCATTER ? off[13] : off[12];
+}
+
+// k parts of a layer GEMM of N columns in BN-column blocks over a k range
+// of K, when the caller asks for split K: 1 (no split) unless even the most
+// row tasks any routing can give (an expert of c rows has ceil(c / 256) of
+// them, so at most floor((R + 255 * min(E, R)) / 256) in all) fit one wave
+// ("Comm-compute fusion (1)", section 5); then 4 parts (2 if K is too
+// short), each at least 16 slices of 32 -- shorter parts would not hide the
+// pipeline's fill behind their weight stream -- and only if the fp32
+// partials, parts x R x NB x N, fit in `room` bytes.
+int splitk_parts(long R, int E, int N, int BN, int NB, int K, int cus, size_t room) {
+  const long rt = (R + 255L * (E < R ? E : R)) / 256;
+  if (N % BN != 0 || rt * (N / BN) > cus) return 1;
+  for (int parts = 4; parts >= 2; parts /= 2)
+    if (K % (32 * parts) == 0 && K / 32 / parts >= 16 &&
+        (size_t)parts * R * NB * N * 4 <= room)
+      return parts;
+  return 1;
 }
 
 // The layer on arguments already checked: the routing from the router front
@@ -417,12 +442,24 @@ int layer_run(const void *x, const void *w_router, const float *logits,
               const int32_t *topk_idx_in, const float *topk_w_in, const void *w_gate,
               const void *w_up, const void *w_down, int T, int H, int E, int k, int I, void *out,
               int combine, unsigned char *ws, const size_t off[14], int cus, hipStream_t s) {
+  // split K where a GEMM has less than one wave of tasks (its fp32 partials
+  // in y's region, free until the down GEMM: gate/up's are reduced into h
+  // before it, down's replace y); the down GEMM only with the gather combine
+  const long R = (long)T * k;
+  const size_t room = off[10] - off[9];
+  const bool may_split = (combine & MOE_LAYER_SPLIT_K) != 0;
+  const int ks_gu = may_split ? splitk_parts(R, E, I, 128, 2, H, cus, room) : 1;
+  const int ks_dn =
+      may_split && (combine & ~kLayerFlags) == MOE_COMBINE_GATHER
+          ? splitk_parts(R, E, H, 256, 1, I, cus, room)
+          : 1;
+  float *part = (float *)(ws + off[9]);
   // the reorder by route inside the gate/up GEMM's prologue (one launch
   // fewer) where the shape allows, unless the caller asks for the separate
-  // permutation launch
-  const bool fused = !(combine & MOE_LAYER_SEPARATE_PERMUTE) &&
+  // permutation launch or the gate/up GEMM splits K
+  const bool fused = !(combine & MOE_LAYER_SEPARATE_PERMUTE) && ks_gu == 1 &&
                      moe::gg_fused_fits(I, H, T * k, E, cus);
-  combine &= ~MOE_LAYER_SEPARATE_PERMUTE;
+  combine &= ~kLayerFlags;
   int32_t *idx = (int32_t *)(ws + off[0]);
   float *w = (float *)(ws + off[1]);
   int32_t *counts = (int32_t *)(ws + off[2]);
@@ -486,8 +523,13 @@ int layer_run(const void *x, const void *w_router, const float *logits,
     e = moe::launch_grouped_gemm(MOE_BF16, I, H, (const uint16_t *)x, r2p, k,
                                  (const uint16_t *)w_gate, (const uint16_t *)w_up,
                                  w_up ? MOE_B_KN : MOE_B_KN_GATE_UP, plan,
-                                 MOE_EPI_SILU_MUL, nullptr, nullptr, 0, h, cus, stream_w, s);
+                                 MOE_EPI_SILU_MUL, nullptr, nullptr, 0, h, cus, stream_w, s,
+                                 nullptr, ks_gu, part, (int)R);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
+    if (ks_gu > 1) {
+      e = moe::launch_splitk_silu(part, ks_gu, (int)R, I, p2r, h, s);
+      if (e != hipSuccess) return MOE_ERR_DEVICE;
+    }
   }
   if (combine == MOE_COMBINE_SCATTER) {
     e = moe::launch_zero(oacc, (long)T * H, s);
@@ -497,6 +539,14 @@ int layer_run(const void *x, const void *w_router, const float *logits,
                                  oacc, cus, stream_w, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     return launch_status(moe::launch_finalize(oacc, (long)T * H, (uint16_t *)out, s));
+  }
+  if (ks_dn > 1) {
+    e = moe::launch_grouped_gemm(MOE_BF16, H, I, h, nullptr, 1, (const uint16_t *)w_down,
+                                 nullptr, MOE_B_KN, plan, MOE_EPI_STORE, r2p, nullptr, 0, y, cus,
+                                 stream_w, s, nullptr, ks_dn, part, (int)R);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    return launch_status(
+        moe::launch_splitk_combine(part, ks_dn, T, k, H, p2r, rw, (uint16_t *)out, s));
   }
   // padding rows of y are never read: the down GEMM skips their stores
   e = moe::launch_grouped_gemm(MOE_BF16, H, I, h, nullptr, 1, (const uint16_t *)w_down, nullptr,
@@ -531,7 +581,7 @@ int moe_layer_ex(const void *x, const float *logits, const int32_t *topk_idx_in,
 size_t moe_layer_router_workspace_size(int T, int H, int E, int k, int I, int combine) {
   size_t off[14];
   if (moe_layer_workspace_layout(T, H, E, k, I, off) != MOE_OK) return 0;
-  combine &= ~MOE_LAYER_SEPARATE_PERMUTE;
+  combine &= ~kLayerFlags;
   if (combine != MOE_COMBINE_GATHER && combine != MOE_COMBINE_SCATTER) return 0;
   if (!moe::router_fits(H, E)) return 0;
   return layer_core_bytes(off, combine) + align256(moe::router_workspace_bytes(T, H, E));

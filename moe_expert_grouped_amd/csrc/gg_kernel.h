@@ -114,6 +114,15 @@ struct GGArgs {
   int lp_R = 0, lp_E = 0, lp_cap = 0; // pairs, experts, row capacity
   int32_t *o_counts = nullptr, *o_offsets = nullptr, *o_p2r = nullptr, *o_r2p = nullptr,
           *o_bexp = nullptr, *o_mpad = nullptr, *o_plan = nullptr;
+  // Split K (store and SiLU*up epilogues, not the fused form): each task's k
+  // range in `ksplit` equal parts, each part a task of its own whose fp32
+  // accumulators go, for the rows with a pair p >= 0 in the task's table,
+  // to Dpart[(part * part_R + p) * NB * N + m * N + column] (m: the B
+  // matrix) instead of the epilogue; a reduction kernel adds the parts in
+  // order and applies the epilogue.
+  int ksplit = 1;
+  float *Dpart = nullptr;
+  int part_R = 0;
 };
 
 // Limits of the fused form: experts (one LDS scan over them) and pairs (the
@@ -320,6 +329,38 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][MI][NI], uint
   }
 }
 
+// Split-K epilogue of one wavefront's share of a tile (the transposed
+// accumulator layout of the store epilogues: register 4 q + e of lane l
+// holds row l % 32, column 8 q + 4 (l / 32) + e of each 32 x 32 tile): the
+// raw fp32 sums of the rows whose pair is p >= 0, 16 bytes per lane and
+// store, at Dp[(p * NB + m) * N + col] (Dp: this k part's block).
+template <int NB, int MI, int NI>
+__device__ __forceinline__ void partial_tile(const f32x16 (&acc)[NB][MI][NI], float *Dp, int N,
+                                             const MOE_LDS int32_t *ptab, int lane, int row0,
+                                             int col) {
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int p = ptab[row0 + i * 32 + (lane & 31)];
+    if (p >= 0) {
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float4 v;
+            v.x = acc_read(acc[m][i][j][4 * q + 0]);
+            v.y = acc_read(acc[m][i][j][4 * q + 1]);
+            v.z = acc_read(acc[m][i][j][4 * q + 2]);
+            v.w = acc_read(acc[m][i][j][4 * q + 3]);
+            *reinterpret_cast<float4 *>(Dp + ((size_t)p * NB + m) * N + col + j * 32 + 8 * q +
+                                        4 * (lane >> 5)) = v;
+          }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Weighted-scatter epilogue of one wavefront's share of a tile: task row r
 // adds w_r * acc into the fp32 token row p_r / k of Dacc, with the pair p_r
 // and its weight w_r taken from the task's LDS tables (padding rows, p < 0,
@@ -366,8 +407,9 @@ __device__ __forceinline__ void scatter_tile(const f32x16 (&acc)[1][MI][NI], flo
 // LP: the fused form -- the permutation is computed by the kernel from the
 // routing instead of read from a plan and row map built before it (see
 // GGArgs); SiLU*up on [K][N] weights with gathered A rows only.
+// SK: the split-K form (see GGArgs::ksplit; store and SiLU*up only).
 template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR, bool BNT, int WV,
-          bool LP = false>
+          bool LP = false, bool SK = false>
 __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
   constexpr int NB = EPI == kEpiSiluMul ? 2 : 1; // B matrices
   constexpr int ARP = BK * 2;                    // bytes per A row (and [N][K] B row) per slice
@@ -417,7 +459,10 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
   const int wm = wave / WCOL;
   const int wn = wave % WCOL;
   const int N = args.N, K = args.K;
-  const int KT = K / BK;
+  static_assert(!SK || (!LP && EPI != kEpiScatter), "split K: store and SiLU*up only");
+  // k parts per task (split K) and slices per item
+  const int KS = SK ? args.ksplit : 1;
+  const int KT = K / BK / KS;
   static_assert(!LP || (EPI == kEpiSiluMul && KN), "the fused form is the gate/up GEMM's");
   const bool has_a = LP || args.a_src_row != nullptr;
   // the pair table `tab` holds a_src_row if given, else epi_row_pair; the
@@ -534,7 +579,7 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
 
   // ---------------- schedule ----------------
   const int ncol = N / BN;
-  const int ntask = nrt * ncol;
+  const int ntask = nrt * ncol * KS; // (row task, column block, k part)
   const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
   const int xcd = blockIdx.x % nx;
   const int S = gridDim.x / nx;
@@ -551,10 +596,16 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
   }
   const int total = n_items * KT; // slices of this workgroup
   auto coords = [&](int i, int &rt, int &n0) {
-    task_coords(tx0 + slot + i * S, args.group_rows, ncol, nrt, BN, rt, n0);
+    const int t = tx0 + slot + i * S;
+    task_coords(SK ? t / KS : t, args.group_rows, ncol, nrt, BN, rt, n0);
     // wave-uniform: the weight stream addresses are scalar operands
     rt = __builtin_amdgcn_readfirstlane(rt);
     n0 = __builtin_amdgcn_readfirstlane(n0);
+  };
+  // the k part of item i (the parts of one task are neighbouring items)
+  auto kpart = [&](int i) -> int {
+    if constexpr (!SK) return 0;
+    return __builtin_amdgcn_readfirstlane((tx0 + slot + i * S) % KS);
   };
   if constexpr (LP) {
     // the plan entries of this workgroup's items, from the offsets: row task
@@ -642,6 +693,7 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
     int b, nb, g;
     plan_of(i, b, nb, g);
     const MOE_LDS int32_t *ptbl = (const MOE_LDS int32_t *)tab[i % kTabSlots];
+    const size_t kb = (size_t)kpart(i) * KT * BK; // the item's first k (split K)
 #pragma unroll
     for (int q = 0; q < A_INSTR; ++q) {
       // instruction q covers task rows (wave*A_INSTR+q)*A_RPI .. +A_RPI
@@ -652,7 +704,7 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
         src = p < 0 ? 0 : p / args.a_src_div; // padding rows read a valid row
       }
       const int c = (lane % A_GPR) ^ swz_rows<BK>(row);
-      a_src[q] = reinterpret_cast<const unsigned char *>(args.A) + ((size_t)src * K + c * 8) * 2;
+      a_src[q] = reinterpret_cast<const unsigned char *>(args.A) + ((size_t)src * K + kb + c * 8) * 2;
     }
     fetch_weights(i);
     a_i = i;
@@ -717,6 +769,7 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
     coords(i, rt, n0);
     plan_of(i, b, nb, g);
     const int gg = g < 0 ? 0 : g;
+    const size_t kb = (size_t)kpart(i) * KT * BK; // the item's first k (split K)
 #pragma unroll
     for (int m = 0; m < NB; ++m) {
       // interleaved gate/up: block b of 128 columns holds gate then up
@@ -725,8 +778,8 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
           (size_t)gg * K * (KN ? args.ldb : N) * 2;
       const int col = args.b_il ? ((n0 >> 7) << 8) + (n0 & 127) + m * 128 : n0;
       // this wavefront's first k row (or n row) of every slice
-      b_base[m] = KN ? Bm + ((size_t)(wave * B_INSTR * RPI) * args.ldb + col) * 2
-                     : Bm + (size_t)(n0 + wave * B_INSTR * RPI) * K * 2;
+      b_base[m] = KN ? Bm + ((size_t)(kb + wave * B_INSTR * RPI) * args.ldb + col) * 2
+                     : Bm + ((size_t)(n0 + wave * B_INSTR * RPI) * K + kb) * 2;
     }
     b_i = i;
     b_k = 0;
@@ -1019,6 +1072,11 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
       if constexpr (SCAT) {
         scatter_tile<4, NI>(acc, args.Dacc, N, pair_table(s), (const MOE_LDS float *)wtab[s],
                             args.topk, lane, wm * 128, n0 + wn * WC);
+      } else if constexpr (SK) {
+        // split K: this part's raw sums of the rows with a pair (the host
+        // requires a table)
+        partial_tile<NB, 4, NI>(acc, args.Dpart + (size_t)kpart(i) * args.part_R * NB * N, N,
+                                pair_table(s), lane, wm * 128, n0 + wn * WC);
       } else {
         // staging: the stages of the slice just consumed, which every
         // wavefront finished reading at its barrier and which the next DMA
@@ -1038,8 +1096,8 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
       }
     }
     // every wavefront's staging is read back before any wavefront issues the
-    // next slice's DMA into those stages
-    if constexpr (!SCAT) block_barrier();
+    // next slice's DMA into those stages (the other epilogues stage nothing)
+    if constexpr (!SCAT && !SK) block_barrier();
     clear_acc();
   }
   // drain any DMA still in flight before the workgroup retires its LDS
@@ -1048,9 +1106,9 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
 }
 
 template <int BN, int BK, int EPI, bool KN, bool FP16, int NA, int NBR, bool BNT, int WV = 4,
-          bool LP = false>
+          bool LP = false, bool SK = false>
 static hipError_t launch_one(const GGArgs &a, int grid, hipStream_t stream) {
-  grouped_gemm_kernel<BN, BK, EPI, KN, FP16, NA, NBR, BNT, WV, LP>
+  grouped_gemm_kernel<BN, BK, EPI, KN, FP16, NA, NBR, BNT, WV, LP, SK>
       <<<grid, 64 * WV, 0, stream>>>(a);
   return hipGetLastError();
 }
@@ -1093,8 +1151,26 @@ hipError_t launch_lp(const GGArgs &a, const TileCfg &c, int grid, hipStream_t s)
   return launch_one<128, 32, kEpiSiluMul, true, false, 3, 4, BNT, 8, true>(a, grid, s);
 }
 
+// The split-K form exists for the streamed bf16 [K][N] store and SiLU*up
+// tiles of eight wavefronts (the shapes with fewer tasks than workgroups).
+inline bool splitk_tile(int epilogue, const TileCfg &c) {
+  return c.waves == 8 && c.bk == 32 && c.group >= 1 &&
+         ((epilogue == kEpiStore && c.bn == 256 && c.na == 3 && c.nb == 6) ||
+          (epilogue == kEpiSiluMul && c.bn == 128 && c.na == 3 && c.nb == 4));
+}
+
 template <int EPI, bool KN, bool FP16, bool BNT>
 hipError_t launch_bn(const GGArgs &a, const TileCfg &c, int grid, hipStream_t s) {
+  if (a.ksplit > 1) {
+    if constexpr (KN && !FP16 && BNT && EPI != kEpiScatter) {
+      if (!splitk_tile(EPI, c)) return hipErrorInvalidValue;
+      if constexpr (EPI == kEpiSiluMul)
+        return launch_one<128, 32, EPI, KN, FP16, 3, 4, BNT, 8, false, true>(a, grid, s);
+      else
+        return launch_one<256, 32, EPI, KN, FP16, 3, 6, BNT, 8, false, true>(a, grid, s);
+    }
+    return hipErrorInvalidValue;
+  }
 #define MOE_GG_CASE(BNV, NAV, NBV)                                                            \
   if (c.waves == 4 && c.bn == BNV && c.bk == 32 && c.na == NAV && c.nb == NBV)                \
     return launch_one<BNV, 32, EPI, KN, FP16, NAV, NBV, BNT>(a, grid, s);

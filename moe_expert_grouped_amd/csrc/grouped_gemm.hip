@@ -155,12 +155,18 @@ static hipError_t launch_kn_stream(const GGArgs &a, const TileCfg &c, int epilog
 // same stream.  grid: persistent workgroups (one per CU in the product
 // path; LDS holds one per CU, any count >= 1 computes the same result);
 // tile: NULL for the default configuration.
+// ksplit > 1 (split K, the layer's shapes with fewer tasks than workgroups):
+// the GEMM writes each k part's raw fp32 sums of the rows with a pair to
+// Dpart ([ksplit][part_R][NB][N], see GGArgs) instead of D, for a
+// reduction kernel (splitk.hip) to finish; streamed bf16 [K][N] weights, the
+// store or SiLU*up epilogue, a row table, the default tile, and K / 32 a
+// multiple of ksplit with at least 4 slices per part.
 hipError_t launch_grouped_gemm(int dtype, int N, int K, const uint16_t *A,
                                const int32_t *a_src_row, int a_src_div, const uint16_t *B,
                                const uint16_t *B2, int layout, const int32_t *plan, int epilogue,
                                const int32_t *epi_row_pair, const float *pair_w, int topk,
                                void *D, int grid, bool b_stream, hipStream_t stream,
-                               const int32_t *tile) {
+                               const int32_t *tile, int ksplit, float *Dpart, int part_R) {
   // the default configuration, or the explicit one of grouped_gemm_tuned
   // (checked by gg_tile_usable before the call)
   const TileCfg c =
@@ -175,6 +181,17 @@ hipError_t launch_grouped_gemm(int dtype, int N, int K, const uint16_t *A,
   const bool kn = layout == 0 || il;
   if (il && (epilogue != kEpiSiluMul || N % 128 != 0 || c.bn > 128 || 128 % c.bn != 0))
     return hipErrorInvalidValue;
+  if (ksplit > 1) {
+    const int kt = K / 32 / ksplit;
+    if (!b_stream || fp16 || !kn || scat || tile || !Dpart || part_R <= 0 ||
+        (ksplit != 2 && ksplit != 4) || K % (32 * ksplit) != 0 || kt < 4 ||
+        2 * kt < c.nb - 1 || !splitk_tile(epilogue, c) ||
+        !(a_src_row || epi_row_pair))
+      return hipErrorInvalidValue;
+    a.ksplit = ksplit;
+    a.Dpart = Dpart;
+    a.part_R = part_R;
+  }
   if (b_stream && !kn) return hipErrorInvalidValue;
   if (b_stream) return launch_kn_stream(a, c, epilogue, fp16, grid, stream);
   if (scat) {

@@ -245,6 +245,13 @@ def test_combine_and_layer_validation(lib):
                                 FAKE, wsb, NULL)
     assert call_ex(2) == moe.MOE_ERR_UNSUPPORTED
     assert call_ex(-1) == moe.MOE_ERR_UNSUPPORTED
+    assert call_ex(0x400) == moe.MOE_ERR_UNSUPPORTED           # an unknown flag
+    # the flags take no workspace of their own: valid, and no GPU here
+    for flags in (moe.MOE_LAYER_SEPARATE_PERMUTE, moe.MOE_LAYER_SPLIT_K,
+                  moe.MOE_LAYER_SEPARATE_PERMUTE | moe.MOE_LAYER_SPLIT_K):
+        assert call_ex(flags, wsb=gather_ws) == moe.MOE_ERR_DEVICE
+        assert call_ex(1 | flags) == moe.MOE_ERR_DEVICE
+        assert lib.moe_layer_workspace_size_ex(T, H, E, k, I, flags) == gather_ws
     assert call_ex(1, x=NULL) == moe.MOE_ERR_INVALID
     assert call_ex(1, wsb=ws - 1) == moe.MOE_ERR_WORKSPACE
     # w_up == NULL: packed gate/up weights, which need I % 128 == 0 (I = 64 here)
@@ -252,6 +259,17 @@ def test_combine_and_layer_validation(lib):
                          NULL) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_layer(FAKE, FAKE, NULL, NULL, NULL, NULL, FAKE, T, H, E, k, I, FAKE, FAKE, ws,
                          NULL) == moe.MOE_ERR_INVALID
+
+
+def test_binding_constants_match_header():
+    # the Python binding's status codes, enum values and layer flags are
+    # the header's
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"^#define\s+(MOE_[A-Z0-9_]+)\s+(0x[0-9a-fA-F]+|-?\d+)", text, re.M))
+    names = [n for n in defs if hasattr(moe, n)]
+    assert {"MOE_LAYER_SEPARATE_PERMUTE", "MOE_LAYER_SPLIT_K", "MOE_ERR_UNSUPPORTED"} <= set(names)
+    for n in names:
+        assert getattr(moe, n) == int(defs[n], 0), n
 
 
 def test_layer_router_validation(lib):
