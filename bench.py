@@ -248,6 +248,11 @@ def bench_moe(a, name, headline):
         "roofline": roof,
         "input_sha256": sha,
     }
+    if name == "ep_skew_small":
+        # the one workload with less than one wave of GEMM tasks: the layer
+        # with split K (MOE_LAYER_SPLIT_K) against without, interleaved, and
+        # a decode-sized share of the same experts
+        rec["split_k_ab"] = split_k_ab(a, d, step, dict(wgu=wgu, wu_arg=wu_arg, wd=wd, ws=ws, out=out))
     hbm = [("gate_up", dur["gate_up"], gu_bytes), ("down", dur["down"], dn_bytes),
            ("combine", dur["combine"], comb_bytes)]
     if headline:
@@ -268,6 +273,36 @@ def bench_moe(a, name, headline):
                     "data"):
             rec.pop(key)
     return rec
+
+
+def split_k_ab(a, d, step, v):
+    """Layer us per step, 5 interleaved rounds of back-to-back steps, without
+    and with split K: on this workload's share, and on the first 16 of its
+    tokens routed by the same recipe (a decode-sized batch, few row tasks)."""
+    import torch
+    import moe_expert_grouped_amd as moe
+    from moe_expert_grouped_amd import synthetic as syn
+    H, E, k, I = d["H"], d["E"], d["k"], d["I"]
+    res = {}
+    n = max(a.steps // 5, 20)
+    for T in (d["T"], 16):
+        s = d if T == d["T"] else syn.make_moe(T, H, E, k, I, routing="zipf", seed=0, with_weights=False)
+        x = torch.from_numpy(s["x"].view(np.int16)).view(torch.bfloat16).cuda()
+        kw = dict(topk_idx=torch.from_numpy(s["topk_idx"]).cuda(), topk_w=torch.from_numpy(s["topk_w"]).cuda())
+        out = v["out"][:T]
+
+        def run(split):
+            moe.layer(x, v["wgu"], v["wu_arg"], v["wd"], k, workspace=v["ws"], out=out, split_k=split, **kw)
+
+        r = {"unsplit": [], "split": [], "active_experts": int(np.unique(s["topk_idx"]).size)}
+        settle(lambda: run(False), 50.0)
+        for _ in range(5):
+            r["unsplit"].append(round(batch_us(lambda: run(False), n, settle_ms=0.0), 2))
+            r["split"].append(round(batch_us(lambda: run(True), n, settle_ms=0.0), 2))
+        res["T%d" % T] = r
+    return {"what": "layer us per step, 5 interleaved rounds of %d back-to-back steps, unsplit "
+                    "against split K (MOE_LAYER_SPLIT_K); T16: the first Zipf draw of 16 tokens "
+                    "over the same experts" % n, **res}
 
 
 def moe_headline_legs(a, d, v):

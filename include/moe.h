@@ -96,21 +96,26 @@ extern "C" {
  * bounded number of tasks per workgroup.  Same results either way. */
 #define MOE_LAYER_SEPARATE_PERMUTE 0x100
 /* Flag OR-ed into the combine of moe_layer_ex / moe_layer_router: split K
- * ([P2 s.5]: with less than one wave of tasks the compute units stand idle).
- * A GEMM of the layer whose tasks ((row task, column block) pairs; at most
- * floor((T*k + 255*min(E, T*k)) / 256) row tasks) fit one wave of the
- * compute units, and whose k range holds at least 2 x 512 values, runs each
- * task's k range in 4 equal parts (2 when K holds fewer, or the workspace
- * room does), each part a task of its own writing fp32 partial sums into
- * the y region of the workspace; a reduction then adds the parts in part
- * order and applies the epilogue (after gate/up: SiLU*up into h, the
- * permutation then running as its own launch; after down, with
- * MOE_COMBINE_GATHER: the weighted combine, y never stored).  Deterministic,
- * but rounded differently from the unsplit sums.  It pays where few row
- * tasks are actually routed -- measured on MI355X, T=16 tokens over 16
- * experts (I=2048): 101 against 137 us -- and costs where the actual tasks
- * nearly fill the CUs (T=128: 143 against 140 us), which the host cannot
- * see before the routing runs on the device; so it is the caller's choice. */
+ * below one wave ([P2 s.5]: with fewer tasks than compute units the rest
+ * stand idle).  A GEMM of the layer that may have at most one wave of (row
+ * task, column block) tasks -- at most floor((T*k + 255*min(E, T*k)) / 256)
+ * row tasks times its column blocks -- and whose k range holds at least
+ * 2 x 512 values is launched in its split-K form (the down GEMM with
+ * MOE_COMBINE_GATHER only).  Once the routing has run, it counts the row
+ * tasks on the device; where they leave at least a quarter of the compute
+ * units idle, it runs each task's k range in 2 or 4 equal parts (the count
+ * that gives the busiest workgroup the least work), each part a task of its
+ * own writing fp32 partial sums into the y region of the workspace, and a
+ * reduction adds the parts in part order and applies the epilogue (after
+ * gate/up: SiLU*up into h; after down: the weighted combine itself, y never
+ * stored); otherwise it runs unsplit, to the same bits as without the flag.
+ * Deterministic (the part count follows from the routing), though a split
+ * sum rounds differently from an unsplit one.  The permutation then runs as
+ * its own launch, and the SiLU*up reduction is one more.  Measured on
+ * MI355X (layer us, without / with): T=16 tokens over 16 Zipf-routed experts
+ * (H=4096, I=2048) 137.0 / 85.8, T=32 137.3 / 131.9; the tp_share slicing
+ * (E=64, top-4, I=512) at T=16 139.8 / 129.1; where nothing splits (T=128
+ * over 16 experts, 192 tasks) 140.2 / 141.2.  For decode-sized batches. */
 #define MOE_LAYER_SPLIT_K 0x200
 
 #define MOE_ROW_BLOCK 128 /* rows per task and per-expert alignment unit [P1 s.4] */

@@ -412,8 +412,11 @@ def layer(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: tor
     "scatter" folds the weighted sum into the down GEMM's epilogue.  The
     permutation runs inside the gate/up GEMM's prologue where the shape
     allows; separate_permute=True gives it its own launch (same results).
-    split_k=True: a GEMM with at most one wave of tasks splits its k range
-    (fp32 partial sums, reduced in a fixed order; MOE_LAYER_SPLIT_K)."""
+    split_k=True (MOE_LAYER_SPLIT_K, for decode-sized batches): a GEMM that
+    may have at most one wave of tasks takes its split-K form, which splits
+    each task's k range on the device where the routed tasks leave at least
+    a quarter of the compute units idle (fp32 partial sums, reduced in a
+    fixed order), and gives the unsplit bits otherwise."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w_gate, "w_gate", torch.bfloat16, 3)
     if w_up is not None:

@@ -27,10 +27,11 @@ hipError_t launch_grouped_gemm(int, int, int, const uint16_t *, const int32_t *,
                                const int32_t *, const float *, int, void *, int, bool,
                                hipStream_t, const int32_t *tile = nullptr, int ksplit = 1,
                                float *Dpart = nullptr, int part_R = 0);
-hipError_t launch_splitk_silu(const float *, int, int, int, const int32_t *, uint16_t *,
-                              hipStream_t);
-hipError_t launch_splitk_combine(const float *, int, int, int, int, const int32_t *,
-                                 const float *, uint16_t *, hipStream_t);
+hipError_t launch_splitk_silu(const float *, const int32_t *, int, int, int, int, int,
+                              const int32_t *, uint16_t *, hipStream_t);
+hipError_t launch_splitk_combine(const float *, const uint16_t *, const int32_t *, int, int, int,
+                                 int, int, int, const int32_t *, const float *, uint16_t *,
+                                 hipStream_t);
 bool gg_tile_usable(const int32_t *tile, int epilogue, int N, int K);
 hipError_t launch_gg_plan(const int32_t *, const int32_t *, int, int32_t *, hipStream_t);
 bool gg_fused_fits(int N, int K, int R, int E, int grid);
@@ -417,14 +418,16 @@ size_t layer_core_bytes(const size_t off[14], int combine) {
   return (combine & ~kLayerFlags) == MOE_COMBINE_SCATTER ? off[13] : off[12];
 }
 
-// k parts of a layer GEMM of N columns in BN-column blocks over a k range
-// of K, when the caller asks for split K: 1 (no split) unless even the most
-// row tasks any routing can give (an expert of c rows has ceil(c / 256) of
-// them, so at most floor((R + 255 * min(E, R)) / 256) in all) fit one wave
-// ("Comm-compute fusion (1)", section 5); then 4 parts (2 if K is too
-// short), each at least 16 slices of 32 -- shorter parts would not hide the
-// pipeline's fill behind their weight stream -- and only if the fp32
-// partials, parts x R x NB x N, fit in `room` bytes.
+// The most k parts a layer GEMM of N columns in BN-column blocks over a k
+// range of K may be split into (the GEMM picks the count on the device from
+// the routed task count, splitk_parts_for): 1 unless even the most row tasks
+// any routing can give (an expert of c rows has ceil(c / 256) of them, so at
+// most floor((R + 255 * min(E, R)) / 256) in all) fit one wave ("Comm-compute
+// fusion (1)", section 5) -- past that the fp32 partials of a share that did
+// not split would cost more than a split could win; else 4 (2 if K is too
+// short), parts of at least 16 slices of 32 -- shorter ones would not hide
+// the pipeline's fill behind their weight stream -- and only as many as
+// whose fp32 partials, parts x R x NB x N, fit in `room` bytes.
 int splitk_parts(long R, int E, int N, int BN, int NB, int K, int cus, size_t room) {
   const long rt = (R + 255L * (E < R ? E : R)) / 256;
   if (N % BN != 0 || rt * (N / BN) > cus) return 1;
@@ -442,17 +445,18 @@ int layer_run(const void *x, const void *w_router, const float *logits,
               const int32_t *topk_idx_in, const float *topk_w_in, const void *w_gate,
               const void *w_up, const void *w_down, int T, int H, int E, int k, int I, void *out,
               int combine, unsigned char *ws, const size_t off[14], int cus, hipStream_t s) {
-  // split K where a GEMM has less than one wave of tasks (its fp32 partials
-  // in y's region, free until the down GEMM: gate/up's are reduced into h
-  // before it, down's replace y); the down GEMM only with the gather combine
+  // with MOE_LAYER_SPLIT_K, the split-K form of a GEMM that may have less
+  // than one wave of tasks (its fp32 partials in y's region, free until the
+  // down GEMM: gate/up's are reduced into h before it, down's replace y);
+  // the down GEMM with the gather combine only (its reduction replaces the
+  // combine launch)
   const long R = (long)T * k;
   const size_t room = off[10] - off[9];
-  const bool may_split = (combine & MOE_LAYER_SPLIT_K) != 0;
-  const int ks_gu = may_split ? splitk_parts(R, E, I, 128, 2, H, cus, room) : 1;
-  const int ks_dn =
-      may_split && (combine & ~kLayerFlags) == MOE_COMBINE_GATHER
-          ? splitk_parts(R, E, H, 256, 1, I, cus, room)
-          : 1;
+  const bool split = (combine & MOE_LAYER_SPLIT_K) != 0;
+  const int ks_gu = split ? splitk_parts(R, E, I, 128, 2, H, cus, room) : 1;
+  const int ks_dn = split && (combine & ~kLayerFlags) == MOE_COMBINE_GATHER
+                        ? splitk_parts(R, E, H, 256, 1, I, cus, room)
+                        : 1;
   float *part = (float *)(ws + off[9]);
   // the reorder by route inside the gate/up GEMM's prologue (one launch
   // fewer) where the shape allows, unless the caller asks for the separate
@@ -527,7 +531,7 @@ int layer_run(const void *x, const void *w_router, const float *logits,
                                  nullptr, ks_gu, part, (int)R);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     if (ks_gu > 1) {
-      e = moe::launch_splitk_silu(part, ks_gu, (int)R, I, p2r, h, s);
+      e = moe::launch_splitk_silu(part, plan, I / 128, cus, ks_gu, (int)R, I, p2r, h, s);
       if (e != hipSuccess) return MOE_ERR_DEVICE;
     }
   }
@@ -546,7 +550,8 @@ int layer_run(const void *x, const void *w_router, const float *logits,
                                  stream_w, s, nullptr, ks_dn, part, (int)R);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     return launch_status(
-        moe::launch_splitk_combine(part, ks_dn, T, k, H, p2r, rw, (uint16_t *)out, s));
+        moe::launch_splitk_combine(part, y, plan, H / 256, cus, ks_dn, T, k, H, p2r, rw,
+                                   (uint16_t *)out, s));
   }
   // padding rows of y are never read: the down GEMM skips their stores
   e = moe::launch_grouped_gemm(MOE_BF16, H, I, h, nullptr, 1, (const uint16_t *)w_down, nullptr,

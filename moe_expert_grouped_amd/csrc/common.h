@@ -119,4 +119,31 @@ constexpr int kPlanHead = 2;
 constexpr int kPlanTwo = 1 << 30;
 inline size_t plan_ints(int cap) { return kPlanHead + 2 * (size_t)(cap / kRowBlock); }
 
+// Split K (the grouped GEMM's SK form and the reductions after it): the k
+// parts, at most `max_parts` (1, 2 or 4), of a GEMM of `tasks` (row task,
+// column block) tasks on `grid` persistent workgroups, decided from the
+// task count the routing gave (the plan), so the GEMM and its reduction agree
+// without the host.  1 unless the tasks leave at least a quarter of the
+// workgroups idle (with 3/4 of them busy the weight stream already draws
+// about all the HBM bandwidth it gets: measured); otherwise the part count
+// that gives the busiest workgroup the least work -- items of 1/p of the
+// k range, ceil(ceil(tasks p / XCDs) / workgroups per XCD) of them, as the
+// persistent schedule deals them out -- the fewer parts on a tie.
+__host__ __device__ inline int splitk_parts_for(int tasks, int grid, int max_parts) {
+  if (tasks <= 0 || 4L * tasks > 3L * grid - 1) return 1;
+  const int nx = grid % 8 == 0 ? 8 : 1, S = grid / nx;
+  int best = 1;
+  long best_items = ((long)tasks + nx - 1) / nx;
+  best_items = (best_items + S - 1) / S;
+  for (int p = 2; p <= max_parts; p *= 2) {
+    long items = ((long)tasks * p + nx - 1) / nx;
+    items = (items + S - 1) / S;
+    if (items * best < best_items * p) { // items / p < best_items / best
+      best = p;
+      best_items = items;
+    }
+  }
+  return best;
+}
+
 } // namespace moe

@@ -115,11 +115,13 @@ struct GGArgs {
   int32_t *o_counts = nullptr, *o_offsets = nullptr, *o_p2r = nullptr, *o_r2p = nullptr,
           *o_bexp = nullptr, *o_mpad = nullptr, *o_plan = nullptr;
   // Split K (store and SiLU*up epilogues, not the fused form): each task's k
-  // range in `ksplit` equal parts, each part a task of its own whose fp32
-  // accumulators go, for the rows with a pair p >= 0 in the task's table,
-  // to Dpart[(part * part_R + p) * NB * N + m * N + column] (m: the B
-  // matrix) instead of the epilogue; a reduction kernel adds the parts in
-  // order and applies the epilogue.
+  // range in S equal parts, S = splitk_parts_for(row tasks x column blocks,
+  // grid, ksplit), each part a task of its own whose fp32 accumulators go,
+  // for the rows with a pair p >= 0 in the task's table, to
+  // Dpart[(part * part_R + p) * NB * N + m * N + column] (m: the B matrix)
+  // instead of the epilogue; a reduction kernel adds the parts in order and
+  // applies the epilogue.  With S == 1 (the tasks fill the CUs) the epilogue
+  // runs as without the split, into D.
   int ksplit = 1;
   float *Dpart = nullptr;
   int part_R = 0;
@@ -460,9 +462,6 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
   const int wn = wave % WCOL;
   const int N = args.N, K = args.K;
   static_assert(!SK || (!LP && EPI != kEpiScatter), "split K: store and SiLU*up only");
-  // k parts per task (split K) and slices per item
-  const int KS = SK ? args.ksplit : 1;
-  const int KT = K / BK / KS;
   static_assert(!LP || (EPI == kEpiSiluMul && KN), "the fused form is the gate/up GEMM's");
   const bool has_a = LP || args.a_src_row != nullptr;
   // the pair table `tab` holds a_src_row if given, else epi_row_pair; the
@@ -579,6 +578,10 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
 
   // ---------------- schedule ----------------
   const int ncol = N / BN;
+  // k parts per task (split K: from the task count, at most args.ksplit)
+  // and slices per item
+  const int KS = SK ? splitk_parts_for(nrt * ncol, gridDim.x, args.ksplit) : 1;
+  const int KT = K / BK / KS;
   const int ntask = nrt * ncol * KS; // (row task, column block, k part)
   const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
   const int xcd = blockIdx.x % nx;
@@ -1072,7 +1075,7 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
       if constexpr (SCAT) {
         scatter_tile<4, NI>(acc, args.Dacc, N, pair_table(s), (const MOE_LDS float *)wtab[s],
                             args.topk, lane, wm * 128, n0 + wn * WC);
-      } else if constexpr (SK) {
+      } else if (SK && KS > 1) {
         // split K: this part's raw sums of the rows with a pair (the host
         // requires a table)
         partial_tile<NB, 4, NI>(acc, args.Dpart + (size_t)kpart(i) * args.part_R * NB * N, N,
@@ -1090,14 +1093,19 @@ __global__ __launch_bounds__(64 * WV, 1) void grouped_gemm_kernel(GGArgs args) {
                 ? (MOE_LDS unsigned char *)aring + ((c - 1) % NA) * A_BYTES + wave * SW
                 : (MOE_LDS unsigned char *)bring + ((c - 1) % NBR) * BS_BYTES +
                       (wave - WV / 2) * SW;
-        store_tile<NB, FP16, 4, NI>(acc, args.D + (size_t)b * kBM * N + n0, N,
+        // (the split form, with both epilogues in its loop, has no registers
+        // for the store offsets hoisted out of it: an opaque copy of N keeps
+        // them inside)
+        int Ns = N;
+        if constexpr (SK) asm volatile("" : "+s"(Ns));
+        store_tile<NB, FP16, 4, NI>(acc, args.D + (size_t)b * kBM * N + n0, Ns,
                                     has_tab ? pair_table(s) : nullptr, lane, wm * 128, wn * WC,
                                     stg);
       }
     }
     // every wavefront's staging is read back before any wavefront issues the
     // next slice's DMA into those stages (the other epilogues stage nothing)
-    if constexpr (!SCAT && !SK) block_barrier();
+    if (!SCAT && !(SK && KS > 1)) block_barrier();
     clear_acc();
   }
   // drain any DMA still in flight before the workgroup retires its LDS
