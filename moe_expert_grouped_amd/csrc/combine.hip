@@ -1,5 +1,5 @@
-// combine.hip -- the top-k weighted reduction back to token order (the
-// "epilogue + top-k weighted reduction" of the MoE layer1 row in
+// combine.hip -- the top-k weighted reduction back to token order (the step
+// after the down GEMM in the MoE layer1 row of the dataflow table in
 // "Comm-compute fusion (1)", section 4):
 //   out[t][n] = round_bf16( sum_{j<k} w[t][j] * y[pair_to_row[t*k+j]][n] ).
 //
