@@ -120,6 +120,55 @@ def test_layer_small_shapes():
         _check_layer(d, what="small T%d H%d E%d k%d I%d" % (T, H, E, k, I))
 
 
+def _degenerate_case(name):
+    """Edge shapes of the layer: one token (decode), every pair on the same
+    two experts, k = E, and a routing whose every id lies outside [0, E)."""
+    if name == "one_token":
+        return syn.make_moe(1, 256, 4, 1, 128, seed=21)
+    if name == "one_token_tp_slice":
+        return syn.make_moe(1, 4096, 64, 4, 512, seed=22, routing="uniform_idx")
+    if name == "two_experts":
+        d = syn.make_moe(64, 256, 8, 2, 128, seed=23, routing="uniform_idx")
+        d["topk_idx"][:, 0], d["topk_idx"][:, 1] = 3, 5
+        return d
+    if name == "k_equals_E":
+        return syn.make_moe(8, 128, 3, 3, 64, seed=24)
+    if name == "all_invalid":
+        d = syn.make_moe(16, 128, 4, 2, 128, seed=25, routing="uniform_idx")
+        d["topk_idx"][:] = -1
+        d["topk_idx"][::3, 1] = 4  # == E: also outside
+        return d
+    raise ValueError(name)
+
+
+@pytest.mark.parametrize("name", ["one_token", "one_token_tp_slice", "two_experts", "k_equals_E", "all_invalid"])
+def test_layer_degenerate_cases(name):
+    # every token against the oracle with both combines, the permutation as
+    # its own launch, and split K (a pair outside [0, E) adds nothing: it
+    # enters the oracle with weight 0)
+    d = _degenerate_case(name)
+    T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
+    idx, w = _routing(d)
+    bad = (idx < 0) | (idx >= E)
+    ref = oracle.moe_tokens(d["x"], np.where(bad, 0, idx).astype(np.int32), np.where(bad, 0, w).astype(np.float32),
+                            d["wg"], d["wu"], d["wd"], tokens=np.arange(T, dtype=np.int32))
+    D = _inputs_dev(d)
+    kw = dict(logits=torch.from_numpy(d["logits"]).cuda()) if "logits" in d else dict(
+        topk_idx=torch.from_numpy(d["topk_idx"]).cuda(), topk_w=torch.from_numpy(d["topk_w"]).cuda())
+    for combine, sep, split in (("gather", False, False), ("scatter", False, False), ("gather", True, False),
+                                ("gather", False, True)):
+        say("layer degenerate", name, combine, "separate" if sep else "", "split" if split else "")
+        ws = torch.full((moe.layer_workspace(T, H, E, k, I).numel(),), 0x7F, dtype=torch.uint8, device="cuda")
+        out = moe.layer(D["x"], D["wg"], D["wu"], D["wd"], k, workspace=ws, combine=combine, separate_permute=sep,
+                        split_k=split, **kw)
+        torch.cuda.synchronize()
+        if name == "all_invalid":
+            assert not torch.any(out.float() != 0), combine
+            assert int(moe.workspace_view(ws, T, H, E, k, I, "num_padded_rows")[0]) == 0
+        else:
+            assert_close(to_f64(out), ref, "%s %s" % (name, combine))
+
+
 def _sample(T, n, seed=0):
     s = np.random.default_rng(seed).choice(T, n, replace=False)
     return np.sort(np.concatenate([s, [0, T - 1]])).astype(np.int32)
