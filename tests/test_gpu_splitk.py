@@ -31,7 +31,10 @@ from _util import assert_close, dev16, say, to_f64
 
 pytestmark = pytest.mark.gpu
 
-GRID = 256  # workgroups of the layer's GEMMs: one per compute unit of MI355X
+
+def _grid():
+    """Workgroups of the layer's GEMMs: one per compute unit (256 on MI355X)."""
+    return torch.cuda.get_device_properties(0).multi_processor_count
 
 
 def _max_parts(T, H, E, k, I, N, bn, nb, K):
@@ -43,7 +46,7 @@ def _max_parts(T, H, E, k, I, N, bn, nb, K):
     room = lay["permute_scratch"] - lay["y"]
     R = T * k
     rt = (R + 255 * min(E, R)) // 256
-    if N % bn or rt * (N // bn) > GRID:
+    if N % bn or rt * (N // bn) > _grid():
         return 1
     for p in (4, 2):
         if K % (32 * p) == 0 and K // 32 // p >= 16 and p * R * nb * N * 4 <= room:
@@ -56,10 +59,12 @@ def _device_parts(tasks, max_parts):
     leave at least a quarter of the workgroups idle; else the count whose
     busiest workgroup (items dealt out per XCD) has the least work, fewer on
     a tie."""
-    if tasks <= 0 or 4 * tasks >= 3 * GRID:
+    grid = _grid()
+    if tasks <= 0 or 4 * tasks >= 3 * grid:
         return 1
-    S = GRID // 8
-    items = lambda p: -(-(-(-tasks * p // 8)) // S)
+    nx = 8 if grid % 8 == 0 else 1
+    S = grid // nx
+    items = lambda p: -(-(-(-tasks * p // nx)) // S)
     best = 1
     for p in (2, 4):
         if p <= max_parts and items(p) * best < items(best) * p:
