@@ -423,10 +423,11 @@ size_t layer_core_bytes(const size_t off[14], int combine) {
 // the routed task count, splitk_parts_for): 1 unless even the most row tasks
 // any routing can give (an expert of c rows has ceil(c / 256) of them, so at
 // most floor((R + 255 * min(E, R)) / 256) in all) fit one wave ("Comm-compute
-// fusion (1)", section 5) -- past that the fp32 partials of a share that did
-// not split would cost more than a split could win; else 4 (2 if K is too
-// short), parts of at least 16 slices of 32 -- shorter ones would not hide
-// the pipeline's fill behind their weight stream -- and only as many as
+// fusion (1)", section 5) -- a larger share keeps the plain form and its
+// launches (the split form of gate/up gives up the fused front end and adds
+// its reduction's launch, whether or not it then splits); else 4 (2 if K is
+// too short), parts of at least 16 slices of 32 -- shorter ones would not
+// hide the pipeline's fill behind their weight stream -- and only as many as
 // whose fp32 partials, parts x R x NB x N, fit in `room` bytes.
 int splitk_parts(long R, int E, int N, int BN, int NB, int K, int cus, size_t room) {
   const long rt = (R + 255L * (E < R ? E : R)) / 256;
