@@ -114,9 +114,10 @@ def _routing(name, T, E, k, seed):
 # (T, H, E, k, I, routing, seed, expected (gate/up, down) parts):
 # both GEMMs in 2 parts (4 would not fit the workspace or leave parts under
 # 16 slices), an expert of two blocks; gate/up in 2 and down in 4 parts;
-# both in 4 parts with two or three items per workgroup
+# both in 4 parts with two or three items per workgroup; gate/up in 2 parts
+# of an odd 17 slices (H = 1088, whose 64-column down tile has no split form)
 CASES = [(160, 2048, 8, 2, 1024, "heavy", 11, (2, 2)), (32, 2048, 16, 1, 2048, "few", 12, (2, 4)),
-         (72, 4096, 16, 1, 2048, "nine", 13, (4, 4))]
+         (72, 4096, 16, 1, 2048, "nine", 13, (4, 4)), (24, 1088, 8, 2, 1024, "few", 14, (2, 1))]
 IDS = ["T%d_H%d_E%d_k%d_I%d" % c[:5] for c in CASES]
 
 
@@ -218,7 +219,7 @@ def test_split_exact_sums_same_bits_as_unsplit(case):
     assert _parts(d) == parts
     ks_gu, ks_dn = parts
     say("split K exact", case[:5], "parts gate/up %d down %d" % parts)
-    nu, nd = (16, 32) if H > 2048 else (32, 32)
+    nu, nd = (16, 32) if H > 2048 else (32, 32)  # H % nu == 0 for every case
     D = _integer_inputs(T, H, E, k, I, seed, nu, nd)
     out_n, h_n, y_n, P = _unsplit(D, d)
     out_s, ws_s = _layer(D, d, split_k=True)
@@ -231,14 +232,18 @@ def test_split_exact_sums_same_bits_as_unsplit(case):
     assert torch.equal(view("pair_to_row").long(), p2r)
     # h of every pair's row (written by the reduction after the split gate/up)
     assert torch.equal(view("h")[rows].view(torch.int16), h_n[rows].view(torch.int16))
-    # the down GEMM's fp32 partials, [parts][pairs][H], in y's region: their
-    # sum (exact) rounds to the unsplit y of the pair's row, and no part is empty
-    lay = moe.layer_workspace_layout(T, H, E, k, I)
-    R = T * k
-    part = ws_s[lay["y"]:lay["y"] + ks_dn * R * H * 4].view(torch.float32).view(ks_dn, R, H)
-    y_s = part.sum(0)[ok].to(torch.bfloat16)
-    assert torch.equal(y_s.view(torch.int16), y_n[rows].view(torch.int16))
-    assert all(bool((part[s][ok] != 0).any()) for s in range(ks_dn))
+    if ks_dn > 1:
+        # the down GEMM's fp32 partials, [parts][pairs][H], in y's region: their
+        # sum (exact) rounds to the unsplit y of the pair's row, and no part is empty
+        lay = moe.layer_workspace_layout(T, H, E, k, I)
+        R = T * k
+        part = ws_s[lay["y"]:lay["y"] + ks_dn * R * H * 4].view(torch.float32).view(ks_dn, R, H)
+        y_s = part.sum(0)[ok].to(torch.bfloat16)
+        assert torch.equal(y_s.view(torch.int16), y_n[rows].view(torch.int16))
+        assert all(bool((part[s][ok] != 0).any()) for s in range(ks_dn))
+    else:
+        # not split: the down GEMM stored y itself
+        assert torch.equal(view("y")[rows].view(torch.int16), y_n[rows].view(torch.int16))
 
 
 def test_no_split_where_tasks_fill_the_cus():
